@@ -1,0 +1,173 @@
+"""CPU oracle for the DSA sparse-attention layer: lightning indexer, Top-K, sparse MLA.
+
+TEST INFRASTRUCTURE ONLY.  This module is the plain, slow, fp64 definition of
+what the GPU path computes.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import it; the library never does, and this
+module imports nothing from the library (it works on numpy arrays only).
+
+What it follows (pages: five articles on hybrid-attention LLM inference):
+  * "Day 0 Inference Adaptation and Performance Optimization for Hybrid
+    Attention LLMs", section "Index-Selected Sparse Attention": an indexer scores
+    all historical positions, the Top-K most relevant are kept, the sparse
+    attention reads only the latent KV at those positions.
+  * "Hybrid Attention LLM Inference Acceleration ...", section 2 (sparse
+    attention path): scoring, head-weight weighting and Top-K selection over the
+    paged K cache; attention only over the Top-K positions.
+  * "Optimizing Inference for Hybrid-Architecture LLMs ...", section 2.2 and
+    section 3.1 (indexer three-in-one fusion): scores are weighted by head
+    weights and compared for Top-K.
+The exact formula is S[p] = sum_h w_h * ReLU(q_h . k_p) over indexer heads h,
+MLA attention over the 576-wide latent rows (512 "nope" + 64 rope) with value =
+the first 512 dims and softmax scale 1/sqrt(576).
+
+Readings where the pages are silent (each also listed in the design notes):
+  * one index key per token, shared by all indexer heads; w is per query token;
+  * FP8 data is OCP e4m3fn codes times an fp32 scale (per token for keys, per
+    (token, head) for queries), dequantized before the dot product;
+  * Top-K keeps k_t = min(K, n_t) positions; ties go to the lower logical
+    position; outputs are physical pool slots, valid ones first, then -1;
+  * a query with no visible position attends over nothing and outputs zeros.
+
+Every function here is pinned by tests/test_oracle_pins.py against closed
+forms, hand-worked values, a library routine (torch's float8 decode and its
+float64 scaled_dot_product_attention), brute force on tiny inputs, or an
+invariant.  No function is left "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+PAGE = 64
+LATENT = 576
+VDIM = 512
+
+
+# --------------------------------------------------------------------------- decoding
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> exact float64 (bf16 is the top half of an fp32)."""
+    u32 = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):
+        return u32.view(np.float32).astype(np.float64)
+
+
+def fp8_e4m3fn_to_f64(codes: np.ndarray) -> np.ndarray:
+    """OCP e4m3fn code -> float64, decoded bit by bit: sign bit, 4-bit exponent
+    with bias 7, 3-bit mantissa; exponent 0 is subnormal (m/8 * 2^-6); no
+    infinities; S.1111.111 is NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    normal = (1.0 + m / 8.0) * np.exp2(e - 7.0)
+    subnormal = (m / 8.0) * 2.0 ** -6
+    v = sign * np.where(e == 0, subnormal, normal)
+    return np.where((e == 0xF) & (m == 0x7), np.nan, v)
+
+
+# --------------------------------------------------------------------------- paged cache access
+def logical_slots(block_row: np.ndarray, n: int) -> np.ndarray:
+    """Physical slot of logical positions 0..n-1 of one sequence: the page id
+    from the block table times 64, plus the offset inside the 64-token page."""
+    p = np.arange(n, dtype=np.int64)
+    return np.asarray(block_row, dtype=np.int64)[p // PAGE] * PAGE + p % PAGE
+
+
+def index_keys(k_idx_pool: np.ndarray, idx_dtype: str, D: int, slots: np.ndarray) -> np.ndarray:
+    """Dequantized index keys [len(slots), D] (float64) at the given pool slots."""
+    slots = np.asarray(slots, dtype=np.int64)
+    if idx_dtype == "bf16":
+        pool = np.asarray(k_idx_pool).reshape(-1, D)
+        return bf16_to_f64(pool[slots])
+    if idx_dtype == "fp8":
+        pages = np.asarray(k_idx_pool, dtype=np.uint8)
+        page, row = slots // PAGE, slots % PAGE
+        cols = row[:, None] * D + np.arange(D)[None, :]
+        codes = pages[page[:, None], cols]
+        sbytes = pages[page[:, None], PAGE * D + 4 * row[:, None] + np.arange(4)[None, :]]
+        scale = np.ascontiguousarray(sbytes).view("<f4").reshape(-1).astype(np.float64)
+        return fp8_e4m3fn_to_f64(codes) * scale[:, None]
+    raise ValueError(idx_dtype)
+
+
+def index_query(q_idx_t: np.ndarray, q_scale_t, idx_dtype: str) -> np.ndarray:
+    """Dequantized indexer query of one token, [H_idx, D] float64."""
+    if idx_dtype == "bf16":
+        return bf16_to_f64(q_idx_t)
+    return fp8_e4m3fn_to_f64(q_idx_t) * np.asarray(q_scale_t, dtype=np.float64)[:, None]
+
+
+# --------------------------------------------------------------------------- the three steps
+def indexer_scores(qv: np.ndarray, w: np.ndarray, keys: np.ndarray) -> np.ndarray:
+    """S[p] = sum_h w[h] * max(0, q[h] . k[p]) for every key row p (float64)."""
+    dots = keys @ qv.T                      # [n, H_idx]
+    return np.maximum(dots, 0.0) @ np.asarray(w, dtype=np.float64)
+
+
+def topk_positions(S: np.ndarray, K: int) -> np.ndarray:
+    """The min(K, n) positions with the largest S, ties to the lower position,
+    by a full stable sort on (-S, position)."""
+    n = S.shape[0]
+    order = np.lexsort((np.arange(n), -S))
+    return order[: min(K, n)]
+
+
+def sparse_mla(qh: np.ndarray, rows: np.ndarray, scale: float, return_probs: bool = False):
+    """Dense softmax attention of the H query heads over the gathered latent rows:
+    Z = scale * q . row (576-wide), P = softmax over rows, out = P @ rows[:, :512].
+    No rows -> zeros."""
+    H = qh.shape[0]
+    if rows.shape[0] == 0:
+        out = np.zeros((H, VDIM))
+        return (out, np.zeros((H, 0))) if return_probs else out
+    Z = scale * (qh @ rows.T)
+    Z = Z - Z.max(axis=1, keepdims=True)
+    E = np.exp(Z)
+    P = E / E.sum(axis=1, keepdims=True)
+    out = P @ rows[:, :VDIM]
+    return (out, P) if return_probs else out
+
+
+# --------------------------------------------------------------------------- per-query drivers
+def query_geometry(case: dict, t: int):
+    """(sequence b, visible count n_t, slots of positions 0..n_t-1)."""
+    b = int(case["q_seq"][t])
+    n = int(min(case["q_visible"][t], case["seq_lens"][b]))
+    n = max(n, 0)
+    return b, n, logical_slots(case["block_table"][b], n)
+
+
+def query_scores(case: dict, t: int):
+    """Indexer scores of query t over its visible positions, plus their slots."""
+    b, n, slots = query_geometry(case, t)
+    qv = index_query(case["q_idx"][t], None if case["q_idx_scale"] is None else case["q_idx_scale"][t],
+                     case["idx_dtype"])
+    keys = index_keys(case["k_idx_pool"], case["idx_dtype"], case["D_idx"], slots)
+    return indexer_scores(qv, case["w"][t], keys), slots
+
+
+def latent_rows(case: dict, slots: np.ndarray) -> np.ndarray:
+    return bf16_to_f64(np.asarray(case["kv_pool"]).reshape(-1, LATENT)[np.asarray(slots, dtype=np.int64)])
+
+
+def mla_query(case: dict, t: int, slots) -> np.ndarray:
+    """Sparse MLA output [H, 512] of query t over the given slots (-1 entries skipped)."""
+    slots = np.asarray(slots, dtype=np.int64)
+    slots = slots[slots >= 0]
+    qh = bf16_to_f64(np.asarray(case["q"][t]))
+    return sparse_mla(qh, latent_rows(case, slots), case["scale"])
+
+
+def layer_query(case: dict, t: int) -> dict:
+    """The whole layer for query t: scores, Top-K slots (padded to K with -1), output."""
+    S, slots = query_scores(case, t)
+    pos = topk_positions(S, case["K"])
+    sel = np.full(case["K"], -1, dtype=np.int64)
+    sel[: pos.shape[0]] = slots[pos]
+    return dict(scores=S, slots=slots, positions=pos, indices=sel, out=mla_query(case, t, sel))
+
+
+def layer_all(case: dict) -> dict:
+    """layer_query for every query of a (small) case."""
+    res = [layer_query(case, t) for t in range(case["T"])]
+    return dict(indices=np.stack([r["indices"] for r in res]), out=np.stack([r["out"] for r in res]),
+                per_query=res)

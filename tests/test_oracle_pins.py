@@ -1,0 +1,263 @@
+"""Pins for the CPU oracle: each oracle function is checked against something
+other than itself -- a library routine (torch's float8/bf16 decode, torch's
+float64 scaled_dot_product_attention), hand-worked values, closed forms, brute
+force with Python's own sorting, or an invariant.  The pages print no worked
+example, so no value here comes from them."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dsa_oracle as O
+
+
+def bf16_bits(x):
+    """float values (exactly representable in bf16) -> uint16 bit patterns."""
+    t = torch.tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16)
+    assert torch.equal(t.to(torch.float32), torch.tensor(np.asarray(x, dtype=np.float32))), "not exact in bf16"
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def make_case(idx_dtype, D, H_idx, k_rows, q_idx, w, seq_len, block_row, NB, q_scale=None, k_scales=None,
+              K=4, H=2, q=None, kv=None, q_visible=None):
+    """A one-query case dict in the oracle's array format."""
+    if idx_dtype == "bf16":
+        pool = np.zeros((NB * 64, D), dtype=np.uint16)
+        pool[O.logical_slots(block_row, len(k_rows))] = bf16_bits(k_rows)
+        pool = pool.reshape(NB, 64, D)
+    else:
+        pool = np.zeros((NB, 64 * D + 256), dtype=np.uint8)
+        slots = O.logical_slots(block_row, len(k_rows))
+        for p, s in enumerate(slots):
+            pg, r = divmod(int(s), 64)
+            pool[pg, r * D:(r + 1) * D] = np.asarray(k_rows[p], dtype=np.uint8)
+            pool[pg, 64 * D + 4 * r: 64 * D + 4 * r + 4] = np.frombuffer(np.float32(k_scales[p]).tobytes(), np.uint8)
+    if q is None:
+        q = np.zeros((1, H, 576), dtype=np.uint16)
+    if kv is None:
+        kv = np.zeros((NB * 64, 576), dtype=np.uint16)
+    return dict(
+        T=1, B=1, H_idx=H_idx, D_idx=D, idx_dtype=idx_dtype, K=K, H=H, scale=1 / math.sqrt(576), num_blocks=NB,
+        seq_lens=np.array([seq_len], np.int32), block_table=np.array([block_row], np.int32),
+        q_seq=np.array([0], np.int32), q_visible=np.array([seq_len if q_visible is None else q_visible], np.int32),
+        w=np.array([w], np.float32),
+        q_idx=(bf16_bits([q_idx]) if idx_dtype == "bf16" else np.array([q_idx], np.uint8)),
+        q_idx_scale=None if q_scale is None else np.array([q_scale], np.float32),
+        k_idx_pool=pool, q=q, kv_pool=kv)
+
+
+# ----------------------------------------------------------------------------- decoders
+def test_fp8_decode_all_256_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = O.fp8_e4m3fn_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(ours))
+    assert nan.sum() == 2  # 0x7f and 0xff only
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert O.fp8_e4m3fn_to_f64(np.uint8(0x7E)) == 448.0
+    assert O.fp8_e4m3fn_to_f64(np.uint8(0x01)) == 2.0 ** -9
+
+
+def test_bf16_decode_matches_torch():
+    rng = np.random.default_rng(0)
+    bits = rng.integers(0, 65536, 4096).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    ours = O.bf16_to_f64(bits)
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ours[ok], ref[ok])
+
+
+# ----------------------------------------------------------------------------- indexer scores
+def test_scores_hand_worked_bf16():
+    # q0=[1,2,0], q1=[0,-1,3], w=[0.5,-2]
+    # k0=[1,1,1]:    d=(3, 2)     -> 0.5*3 - 2*2      = -2.5
+    # k1=[2,0,-1]:   d=(2,-3)     -> 0.5*2 - 2*0      =  1.0
+    # k2=[0,-1,-1]:  d=(-2,-2)    -> 0                =  0.0
+    # k3=[-1,.5,2]:  d=(0, 5.5)   -> 0.5*0 - 2*5.5    = -11.0
+    keys = [[1, 1, 1], [2, 0, -1], [0, -1, -1], [-1, 0.5, 2]]
+    case = make_case("bf16", 3, 2, keys, [[1, 2, 0], [0, -1, 3]], [0.5, -2.0], 4, [0], 1)
+    S, slots = O.query_scores(case, 0)
+    assert S.tolist() == [-2.5, 1.0, 0.0, -11.0]
+    assert slots.tolist() == [0, 1, 2, 3]
+    assert O.topk_positions(S, 2).tolist() == [1, 2]
+
+
+def test_scores_hand_worked_fp8():
+    # e4m3fn codes: 0x38=1, 0x40=2, 0x44=3, 0xB8=-1
+    # q0 = [1,2]*0.5 = [0.5,1];  q1 = [3,-1]*2 = [6,-2];  w = [1,-0.25]
+    # k0 = [2,1]*4 = [8,4]:      d=(8, 40)     -> 8 - 10     = -2
+    # k1 = [1,3]*0.5 = [.5,1.5]: d=(1.75, 0)   -> 1.75
+    q_codes = [[0x38, 0x40], [0x44, 0xB8]]
+    k_codes = [[0x40, 0x38], [0x38, 0x44]]
+    case = make_case("fp8", 2, 2, k_codes, q_codes, [1.0, -0.25], 2, [3], 4, q_scale=[0.5, 2.0],
+                     k_scales=[4.0, 0.5])
+    S, slots = O.query_scores(case, 0)
+    assert S.tolist() == [-2.0, 1.75]
+    assert slots.tolist() == [192, 193]
+
+
+def test_scores_closed_form_ramp_through_permuted_pages():
+    # H=1, w=1, q=e0, k_p=(p+1)/256 e0 -> S_p=(p+1)/256; Top-K = last K positions
+    n, D = 256, 4
+    keys = np.zeros((n, D))
+    keys[:, 0] = (np.arange(n) + 1) / 256.0
+    block_row = [5, 2, 7, 0]
+    case = make_case("bf16", D, 1, keys, [[1, 0, 0, 0]], [1.0], n, block_row, 8, K=10)
+    S, slots = O.query_scores(case, 0)
+    assert np.array_equal(S, (np.arange(n) + 1) / 256.0)
+    res = O.layer_query(case, 0)
+    assert res["positions"].tolist() == list(range(255, 245, -1))
+    expect_slots = [block_row[p // 64] * 64 + p % 64 for p in range(255, 245, -1)]
+    assert res["indices"].tolist() == expect_slots
+
+
+def test_scores_positive_homogeneity():
+    rng = np.random.default_rng(1)
+    H, D, n = 4, 8, 64
+    qv = rng.standard_normal((H, D))
+    w = rng.standard_normal(H)
+    keys = rng.standard_normal((n, D))
+    S = O.indexer_scores(qv, w, keys)
+    for a in (0.25, 3.0):
+        np.testing.assert_allclose(O.indexer_scores(qv * a, w, keys), a * S, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(O.indexer_scores(qv, w * a, keys), a * S, rtol=1e-12, atol=1e-12)
+        assert set(O.topk_positions(O.indexer_scores(qv * a, w, keys), 9)) == set(O.topk_positions(S, 9))
+
+
+def test_scores_brute_force_loops_tiny():
+    # scalar Python loops over heads and dims: catches a transposed q or a dropped head
+    rng = np.random.default_rng(2)
+    H, D, n = 3, 5, 7
+    qv = rng.standard_normal((H, D))
+    w = rng.standard_normal(H)
+    keys = rng.standard_normal((n, D))
+    S = O.indexer_scores(qv, w, keys)
+    for p in range(n):
+        acc = 0.0
+        for h in range(H):
+            dot = math.fsum(qv[h, d] * keys[p, d] for d in range(D))
+            acc += w[h] * (dot if dot > 0 else 0.0)
+        assert abs(acc - S[p]) < 1e-12
+
+
+# ----------------------------------------------------------------------------- Top-K
+@pytest.mark.parametrize("n,K", [(1, 4), (5, 5), (37, 8), (300, 64), (64, 300)])
+def test_topk_matches_python_sorted_with_ties(n, K):
+    rng = np.random.default_rng(n * 7 + K)
+    S = rng.integers(-5, 6, n).astype(np.float64)  # many exact ties
+    S[rng.integers(0, n, max(1, n // 4))] = 0.0
+    ours = O.topk_positions(S, K)
+    ref = sorted(range(n), key=lambda p: (-S[p], p))[: min(K, n)]
+    assert ours.tolist() == ref
+
+
+def test_topk_selected_dominate_unselected():
+    rng = np.random.default_rng(3)
+    S = rng.standard_normal(5000)
+    pos = O.topk_positions(S, 123)
+    mask = np.zeros(5000, bool)
+    mask[pos] = True
+    assert S[mask].min() >= S[~mask].max()
+    assert len(set(pos.tolist())) == 123
+
+
+def test_causal_horizon_hides_later_positions():
+    # position 9 has the largest key but query sees only 0..7
+    n, D = 10, 2
+    keys = np.zeros((n, D))
+    keys[:, 0] = np.arange(n)
+    keys[9, 0] = 100
+    case = make_case("bf16", D, 1, keys, [[1, 0]], [1.0], n, [0], 1, K=3, q_visible=8)
+    res = O.layer_query(case, 0)
+    assert res["positions"].tolist() == [7, 6, 5]
+    assert res["indices"].tolist() == [7, 6, 5]
+
+
+def test_zero_visible_gives_padding_and_zero_output():
+    case = make_case("bf16", 2, 1, np.zeros((4, 2)), [[1, 0]], [1.0], 4, [0], 1, K=3, q_visible=0)
+    res = O.layer_query(case, 0)
+    assert res["indices"].tolist() == [-1, -1, -1]
+    assert not res["out"].any()
+
+
+# ----------------------------------------------------------------------------- sparse MLA
+def sdpa_f64(qh, rows, scale):
+    q = torch.from_numpy(qh)[:, None, :]                               # [H, 1, 576]
+    k = torch.from_numpy(rows)[None].expand(qh.shape[0], -1, -1)      # [H, k, 576]
+    v = torch.from_numpy(rows[:, :512])[None].expand(qh.shape[0], -1, -1).contiguous()
+    return torch.nn.functional.scaled_dot_product_attention(q, k.contiguous(), v, scale=scale)[:, 0].numpy()
+
+
+def test_mla_matches_torch_sdpa_float64():
+    rng = np.random.default_rng(4)
+    qh = rng.standard_normal((6, 576))
+    rows = rng.standard_normal((37, 576))
+    scale = 1 / math.sqrt(576)
+    np.testing.assert_allclose(O.sparse_mla(qh, rows, scale), sdpa_f64(qh, rows, scale), rtol=1e-12, atol=1e-13)
+
+
+def test_mla_identical_rows_return_the_row():
+    rng = np.random.default_rng(5)
+    c = rng.standard_normal(576)
+    rows = np.tile(c, (11, 1))
+    out = O.sparse_mla(rng.standard_normal((3, 576)), rows, 0.1)
+    np.testing.assert_allclose(out, np.tile(c[:512], (3, 1)), rtol=1e-14, atol=1e-14)
+
+
+def test_mla_zero_query_is_mean_of_values():
+    rng = np.random.default_rng(6)
+    rows = rng.standard_normal((9, 576))
+    out = O.sparse_mla(np.zeros((2, 576)), rows, 0.3)
+    np.testing.assert_allclose(out, np.tile(rows[:, :512].mean(0), (2, 1)), rtol=1e-13, atol=1e-14)
+
+
+def test_mla_single_row_and_empty():
+    rng = np.random.default_rng(7)
+    r = rng.standard_normal((1, 576))
+    np.testing.assert_array_equal(O.sparse_mla(rng.standard_normal((4, 576)), r, 1.0), np.tile(r[0, :512], (4, 1)))
+    assert not O.sparse_mla(rng.standard_normal((4, 576)), np.zeros((0, 576)), 1.0).any()
+
+
+def test_mla_softmax_weights_sum_to_one():
+    rng = np.random.default_rng(8)
+    _, P = O.sparse_mla(rng.standard_normal((5, 576)) * 3, rng.standard_normal((50, 576)), 1 / 24, True)
+    np.testing.assert_allclose(P.sum(1), 1.0, atol=1e-12)
+    assert (P >= 0).all()
+
+
+# ----------------------------------------------------------------------------- whole layer
+def random_layer_case(rng, n, NB, block_row, K, H=4, idx_dtype="bf16"):
+    D, H_idx = 8, 3
+    keys = rng.standard_normal((n, D)).astype(np.float32)
+    keys = torch.tensor(keys).to(torch.bfloat16).to(torch.float32).numpy()
+    q_idx = torch.tensor(rng.standard_normal((H_idx, D)).astype(np.float32)).to(torch.bfloat16).float().numpy()
+    q = bf16_bits(torch.tensor(rng.standard_normal((1, H, 576)).astype(np.float32)).to(torch.bfloat16).float().numpy())
+    kv = np.zeros((NB * 64, 576), np.uint16)
+    lat = torch.tensor(rng.standard_normal((n, 576)).astype(np.float32)).to(torch.bfloat16).float().numpy()
+    kv[O.logical_slots(block_row, n)] = bf16_bits(lat)
+    return make_case(idx_dtype, D, H_idx, keys, q_idx, rng.standard_normal(H_idx) * 0.5, n, block_row, NB,
+                     K=K, H=H, q=q, kv=kv), lat
+
+
+def test_layer_with_K_at_least_n_equals_dense_attention():
+    rng = np.random.default_rng(9)
+    n = 150
+    case, lat = random_layer_case(rng, n, 3, [2, 0, 1], K=256)
+    res = O.layer_query(case, 0)
+    assert sorted(res["positions"].tolist()) == list(range(n))
+    qh = O.bf16_to_f64(case["q"][0])
+    dense = sdpa_f64(qh, lat.astype(np.float64), case["scale"])
+    np.testing.assert_allclose(res["out"], dense, rtol=1e-11, atol=1e-12)
+
+
+def test_layer_invariant_under_page_permutation():
+    rng = np.random.default_rng(10)
+    n = 200
+    case_a, _ = random_layer_case(np.random.default_rng(11), n, 4, [0, 1, 2, 3], K=17)
+    case_b, _ = random_layer_case(np.random.default_rng(11), n, 4, [3, 1, 0, 2], K=17)
+    ra, rb = O.layer_query(case_a, 0), O.layer_query(case_b, 0)
+    assert ra["positions"].tolist() == rb["positions"].tolist()
+    np.testing.assert_array_equal(ra["out"], rb["out"])
+    assert ra["indices"].tolist() != rb["indices"].tolist()  # slots differ, positions do not
