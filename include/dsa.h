@@ -1,0 +1,181 @@
+/*
+ * dsa.h -- C ABI of the DSA sparse-attention layer for MI355X (gfx950).
+ *
+ * The layer (pages: "Day 0 Inference Adaptation and Performance Optimization
+ * for Hybrid Attention LLMs", section "Index-Selected Sparse Attention";
+ * "Inference Acceleration for a New Domestic LLM Architecture", section 3
+ * "DSA Integration", whose illustrative listing chains a fused lightning
+ * indexer, a Top-K selection and a sparse flash attention):
+ *
+ *   1. indexer:  S[t,p] = sum_h w[t,h] * ReLU(q_idx[t,h,:] . k_idx[p,:]) for
+ *                every cached position p visible to query token t, reading the
+ *                paged index-K cache directly;
+ *   2. Top-K:    the k_t = min(K, n_t) positions with the largest S (ties go to
+ *                the lower logical position);
+ *   3. sparse MLA: softmax(scale * q[t,h,:576] . C[j,:576]) over the selected
+ *                latent rows C, times C[j,:512] (value = first 512 dims).
+ *
+ * Conventions shared by every call
+ *   - All tensor pointers are DEVICE pointers unless stated otherwise; the
+ *     argument structs themselves live in host memory and are read during the
+ *     call only.
+ *   - Every buffer is owned by the caller.  The library never allocates device
+ *     memory; scratch comes from the caller's workspace (`ws`, `ws_bytes`),
+ *     sized by dsa_workspace_bytes().  The workspace needs no initialisation.
+ *   - Calls enqueue work on `stream` (a hipStream_t; NULL = the null stream),
+ *     never synchronise, and keep no mutable global state.  Two calls that share
+ *     a workspace must be ordered on one stream.
+ *   - Argument errors are detected on the host before anything is launched and
+ *     returned as a dsa_status; nothing is enqueued then.  A failed launch
+ *     returns DSA_ERR_HIP.  No exception crosses the ABI.
+ *   - Device-side contents (block_table, seq_lens, q_seq, q_visible, indices)
+ *     are the caller's responsibility: page ids outside [0, num_blocks) and
+ *     index slots outside [0, 64*num_blocks) are treated as absent (never read),
+ *     and visible counts are clamped to [0, seq_len] and to 64*max_blocks.
+ *
+ * Paged cache layout (64-token pages; one block table serves both caches)
+ *   - index-K pool, BF16:  [num_blocks][64][D_idx] bf16.
+ *   - index-K pool, FP8:   num_blocks pages of (64*D_idx + 256) bytes: 64 rows of
+ *                          D_idx OCP e4m3fn codes, then 64 fp32 dequantisation
+ *                          scales (one per token).  8448 B per page at D_idx=128.
+ *   - latent pool:         [num_blocks*64][576] bf16 (512 nope + 64 rope), row
+ *                          `slot` = page*64 + offset.
+ *   - block_table:         [B][max_blocks] int32, logical page -> physical page.
+ *   - seq_lens:            [B] int32 cached tokens per sequence.
+ *   Logical position p of sequence b lives at slot block_table[b][p/64]*64 + p%64.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+#define DSA_PAGE_TOKENS 64
+#define DSA_LATENT_DIM 576
+#define DSA_VALUE_DIM 512
+#define DSA_MAX_K 2048
+#define DSA_MAX_INDEX_HEADS 64
+
+typedef enum dsa_status {
+  DSA_OK = 0,
+  DSA_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  DSA_ERR_DTYPE = 2,       /* unknown index dtype enum                            */
+  DSA_ERR_SHAPE = 3,       /* a size is out of range (T, B, heads, dims, blocks)  */
+  DSA_ERR_K = 4,           /* K <= 0 or K > DSA_MAX_K                             */
+  DSA_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned                    */
+  DSA_ERR_WORKSPACE = 6,   /* ws_bytes < dsa_workspace_bytes(...) or ws NULL      */
+  DSA_ERR_UNSUPPORTED = 7, /* a valid but unimplemented combination               */
+  DSA_ERR_HIP = 8          /* a HIP launch failed                                 */
+} dsa_status;
+
+typedef enum dsa_idx_dtype {
+  DSA_IDX_BF16 = 0,       /* q_idx and the index-K pool are bf16                   */
+  DSA_IDX_FP8_E4M3FN = 1  /* OCP e4m3fn codes with fp32 scales (see layout above) */
+} dsa_idx_dtype;
+
+/*
+ * Indexer inputs ("Optimizing Inference for Hybrid-Architecture LLMs", section
+ * 3.1: scoring, head-weight weighting and Top-K selection fused, reading the
+ * paged K cache directly).
+ *   T            query tokens in this call (>= 1)
+ *   B            sequences (>= 1)
+ *   H_idx        indexer heads, 1..64
+ *   D_idx        indexer head dim: 64 or 128 (BF16), 128 (FP8)
+ *   idx_dtype    dsa_idx_dtype
+ *   q_idx        [T][H_idx][D_idx] bf16, or e4m3fn codes (uint8)
+ *   q_idx_scale  [T][H_idx] fp32 dequantisation scale per (token, head); FP8
+ *                only, must be NULL for BF16.  Scales must be > 0.
+ *   w            [T][H_idx] fp32 head weights (any sign)
+ *   k_idx_pool   paged index-K pool (layout above)
+ *   num_blocks   pages in both pools
+ *   block_table  [B][max_blocks] int32
+ *   max_blocks   row length of block_table (>= 1)
+ *   seq_lens     [B] int32
+ *   q_seq        [T] int32 sequence of each query, or NULL (then T == B and
+ *                query t belongs to sequence t).  Queries of one sequence that
+ *                are adjacent in t share one pass over its keys.
+ *   q_visible    [T] int32 causal horizon n_t (query t sees positions
+ *                0..n_t-1), or NULL (then n_t = seq_lens[q_seq[t]])
+ *   max_q_per_seq host-side upper bound on adjacent queries of one sequence
+ *                (1 for plain decode); it only selects the kernel variant.
+ */
+typedef struct dsa_indexer_args {
+  int32_t T, B, H_idx, D_idx;
+  int32_t idx_dtype;
+  const void* q_idx;
+  const float* q_idx_scale;
+  const float* w;
+  const void* k_idx_pool;
+  int64_t num_blocks;
+  const int32_t* block_table;
+  int32_t max_blocks;
+  const int32_t* seq_lens;
+  const int32_t* q_seq;
+  const int32_t* q_visible;
+  int32_t max_q_per_seq;
+} dsa_indexer_args;
+
+/*
+ * Sparse MLA inputs ("Hybrid Attention LLM Inference Acceleration", section 2:
+ * read the main attention KV at the selected indices and attend over the Top-K
+ * positions only).
+ *   T          query tokens (>= 1)
+ *   H          attention heads: 16, 32, 64 or 128
+ *   q          [T][H][576] bf16 (rope part already applied)
+ *   kv_pool    [num_blocks*64][576] bf16 latent rows
+ *   num_blocks pages in the pool
+ */
+typedef struct dsa_mla_args {
+  int32_t T, H;
+  const void* q;
+  const void* kv_pool;
+  int64_t num_blocks;
+} dsa_mla_args;
+
+/* Bytes of workspace the call needs.  Pass NULL for the struct a call does not
+ * use (dsa_indexer_topk: mla = NULL; dsa_sparse_mla_attn: idx = NULL).  Returns
+ * 0 when the arguments are invalid (the call itself reports why). */
+size_t dsa_workspace_bytes(const dsa_indexer_args* idx, const dsa_mla_args* mla, int K);
+
+/*
+ * Steps 1+2.  Writes indices_out[T][K] (int32 device): for each query the
+ * k_t = min(K, n_t) selected PHYSICAL pool slots in ascending logical-position
+ * order, then K - k_t entries of -1.  Scores never leave the chip except as
+ * bounded per-chunk candidate lists in the workspace.
+ */
+dsa_status dsa_indexer_topk(const dsa_indexer_args* a, int K, int32_t* indices_out,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Step 3.  indices [T][K] int32 device pool slots; entries < 0 (or outside the
+ * pool) are skipped.  out [T][H][512] bf16 device (fp32 accumulation).  A query
+ * with no valid entry gets zeros.  scale is the softmax scale (1/sqrt(576) for
+ * the pages' model).
+ */
+dsa_status dsa_sparse_mla_attn(const dsa_mla_args* a, const int32_t* indices, int K, float scale, void* out,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Steps 1-3 as one launch sequence on `stream`.  idx->T must equal mla->T and
+ * both must use the same num_blocks.  indices_out may be NULL (the indices then
+ * stay in the workspace); otherwise it receives what dsa_indexer_topk writes.
+ */
+dsa_status dsa_layer(const dsa_indexer_args* idx, const dsa_mla_args* mla, int K, float scale,
+                     int32_t* indices_out, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Static string for a status code ("unknown status" for anything else). */
+const char* dsa_status_str(dsa_status s);
+
+/* DSA_ABI_VERSION of the loaded library. */
+int dsa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

@@ -1,0 +1,260 @@
+// C ABI of the DSA layer: argument validation, workspace layout, launch order.
+// Every check runs on the host before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/dsa.h"
+#include "dsa_device.h"
+#include "dsa_params.h"
+
+namespace dsa {
+hipError_t launch_indexer(const IdxParams& p, int is_fp8, int D, int grid, hipStream_t st);
+hipError_t launch_mla(const MlaParams& p, hipStream_t st);
+
+namespace {
+
+constexpr int TARGET_ITEMS = 1024;  // key chunks aimed for per indexer call
+constexpr int CH_MIN = 4096;        // smallest chunk (keys)
+constexpr int MLA_TARGET_WGS = 256;
+constexpr int MLA_MIN_ROWS = 256;
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct IdxPlan {
+  int MQ = 1, CH = 0, nch_max = 1, U = 0, I = 0, grid = 0;
+  size_t off_hdr = 0, off_groups = 0, off_ctr = 0, off_lcnt = 0, off_lkeys = 0, off_lpos = 0, end = 0;
+};
+
+struct MlaPlan {
+  int S = 1, RPS = 0;
+  size_t off_o = 0, off_ml = 0, end = 0;
+};
+
+dsa_status check_indexer(const dsa_indexer_args* a, int K) {
+  if (!a) return DSA_ERR_NULL;
+  if (K <= 0 || K > DSA_MAX_K) return DSA_ERR_K;
+  if (a->idx_dtype != DSA_IDX_BF16 && a->idx_dtype != DSA_IDX_FP8_E4M3FN) return DSA_ERR_DTYPE;
+  if (!a->q_idx || !a->w || !a->k_idx_pool || !a->block_table || !a->seq_lens) return DSA_ERR_NULL;
+  if (a->idx_dtype == DSA_IDX_FP8_E4M3FN && !a->q_idx_scale) return DSA_ERR_NULL;
+  if (a->idx_dtype == DSA_IDX_BF16 && a->q_idx_scale) return DSA_ERR_DTYPE;
+  if (a->T < 1 || a->B < 1 || a->max_blocks < 1 || a->num_blocks < 1 || a->max_q_per_seq < 1) return DSA_ERR_SHAPE;
+  if (a->H_idx < 1 || a->H_idx > DSA_MAX_INDEX_HEADS) return DSA_ERR_SHAPE;
+  if (a->idx_dtype == DSA_IDX_BF16 && a->D_idx != 64 && a->D_idx != 128) return DSA_ERR_SHAPE;
+  if (a->idx_dtype == DSA_IDX_FP8_E4M3FN && a->D_idx != 128) return DSA_ERR_UNSUPPORTED;
+  if (!a->q_seq && a->T != a->B) return DSA_ERR_SHAPE;
+  if ((int64_t)a->max_blocks * DSA_PAGE_TOKENS > (int64_t)INT32_MAX / 2) return DSA_ERR_SHAPE;
+  if ((int64_t)a->num_blocks * DSA_PAGE_TOKENS > (int64_t)INT32_MAX) return DSA_ERR_SHAPE;
+  if (!aligned(a->q_idx, 16) || !aligned(a->k_idx_pool, 16) || !aligned(a->w, 4) || !aligned(a->block_table, 4) ||
+      !aligned(a->seq_lens, 4) || !aligned(a->q_idx_scale, 4) || !aligned(a->q_seq, 4) ||
+      !aligned(a->q_visible, 4))
+    return DSA_ERR_ALIGN;
+  return DSA_OK;
+}
+
+dsa_status check_mla(const dsa_mla_args* m, int K) {
+  if (!m) return DSA_ERR_NULL;
+  if (K <= 0 || K > DSA_MAX_K) return DSA_ERR_K;
+  if (!m->q || !m->kv_pool) return DSA_ERR_NULL;
+  if (m->T < 1 || m->num_blocks < 1) return DSA_ERR_SHAPE;
+  if (m->H != 16 && m->H != 32 && m->H != 64 && m->H != 128) return DSA_ERR_SHAPE;
+  if ((int64_t)m->num_blocks * DSA_PAGE_TOKENS > (int64_t)INT32_MAX) return DSA_ERR_SHAPE;
+  if (!aligned(m->q, 16) || !aligned(m->kv_pool, 16)) return DSA_ERR_ALIGN;
+  return DSA_OK;
+}
+
+IdxPlan plan_indexer(const dsa_indexer_args* a, int K, size_t base) {
+  IdxPlan pl;
+  pl.MQ = a->max_q_per_seq >= 3 ? 4 : a->max_q_per_seq;
+  const int64_t maxlen = (int64_t)a->max_blocks * DSA_PAGE_TOKENS;
+  const int64_t groups_est = a->q_seq ? std::min<int64_t>(a->T, a->B + (a->T + pl.MQ - 1) / pl.MQ) : a->T;
+  int64_t ch = (groups_est * maxlen + TARGET_ITEMS - 1) / TARGET_ITEMS;
+  ch = std::max<int64_t>(ch, CH_MIN);
+  ch = (ch + ROUND - 1) / ROUND * ROUND;
+  const int64_t ch_cap = (maxlen + ROUND - 1) / ROUND * ROUND;
+  ch = std::min(ch, ch_cap);
+  ch = std::min<int64_t>(ch, CH_MAX);
+  pl.CH = (int)ch;
+  pl.nch_max = (int)((maxlen + ch - 1) / ch);
+  pl.U = tree_lists(pl.nch_max);
+  pl.I = tree_counters(pl.nch_max);
+  const int64_t T = a->T;
+  size_t off = align_up(base, 256);
+  pl.off_hdr = off;
+  off = align_up(off + 64, 256);
+  pl.off_groups = off;
+  off = align_up(off + (size_t)T * G_FIELDS * 4, 256);
+  pl.off_ctr = off;
+  off = align_up(off + (size_t)T * pl.I * 4, 256);
+  pl.off_lcnt = off;
+  off = align_up(off + (size_t)T * pl.U * 4, 256);
+  pl.off_lkeys = off;
+  off = align_up(off + (size_t)T * pl.U * K * 4, 256);
+  pl.off_lpos = off;
+  off = align_up(off + (size_t)T * pl.U * K * 4, 256);
+  pl.end = off;
+  const int64_t items_max = T * pl.nch_max;
+  pl.grid = (int)std::min<int64_t>(items_max, 256);
+  return pl;
+}
+
+MlaPlan plan_mla(const dsa_mla_args* m, int K, size_t base) {
+  MlaPlan pl;
+  int S = (MLA_TARGET_WGS + m->T - 1) / m->T;
+  S = std::max(1, std::min(S, std::max(1, K / MLA_MIN_ROWS)));
+  int rps = (K + S - 1) / S;
+  rps = (rps + 31) / 32 * 32;
+  S = (K + rps - 1) / rps;
+  pl.S = S;
+  pl.RPS = rps;
+  size_t off = align_up(base, 256);
+  if (S > 1) {
+    pl.off_o = off;
+    off = align_up(off + (size_t)m->T * S * m->H * DSA_VALUE_DIM * 4, 256);
+    pl.off_ml = off;
+    off = align_up(off + (size_t)m->T * S * m->H * 2 * 4, 256);
+  }
+  pl.end = off;
+  return pl;
+}
+
+IdxParams make_idx_params(const dsa_indexer_args* a, int K, int32_t* indices, unsigned char* ws, const IdxPlan& pl) {
+  IdxParams p{};
+  p.q_idx = (const uint8_t*)a->q_idx;
+  p.q_scale = a->q_idx_scale;
+  p.w = a->w;
+  p.k_pool = (const uint8_t*)a->k_idx_pool;
+  p.num_blocks = a->num_blocks;
+  const int es = a->idx_dtype == DSA_IDX_BF16 ? 2 : 1;
+  p.page_bytes = (int64_t)DSA_PAGE_TOKENS * a->D_idx * es + (a->idx_dtype == DSA_IDX_BF16 ? 0 : DSA_PAGE_TOKENS * 4);
+  p.block_table = a->block_table;
+  p.seq_lens = a->seq_lens;
+  p.q_seq = a->q_seq;
+  p.q_visible = a->q_visible;
+  p.max_blocks = a->max_blocks;
+  p.T = a->T;
+  p.B = a->B;
+  p.H_idx = a->H_idx;
+  p.K = K;
+  p.CH = pl.CH;
+  p.MQ = pl.MQ;
+  p.indices = indices;
+  p.hdr = (int32_t*)(ws + pl.off_hdr);
+  p.groups = (int32_t*)(ws + pl.off_groups);
+  p.ctr = (uint32_t*)(ws + pl.off_ctr);
+  p.list_cnt = (int32_t*)(ws + pl.off_lcnt);
+  p.list_keys = (uint32_t*)(ws + pl.off_lkeys);
+  p.list_pos = (int32_t*)(ws + pl.off_lpos);
+  return p;
+}
+
+MlaParams make_mla_params(const dsa_mla_args* m, const int32_t* indices, int K, float scale, void* out,
+                          unsigned char* ws, const MlaPlan& pl) {
+  MlaParams p{};
+  p.q = (const uint16_t*)m->q;
+  p.kv = (const uint16_t*)m->kv_pool;
+  p.num_slots = m->num_blocks * DSA_PAGE_TOKENS;
+  p.indices = indices;
+  p.T = m->T;
+  p.H = m->H;
+  p.K = K;
+  p.S = pl.S;
+  p.rows_per_split = pl.RPS;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.out = (uint16_t*)out;
+  p.part_o = pl.S > 1 ? (float*)(ws + pl.off_o) : nullptr;
+  p.part_ml = pl.S > 1 ? (float*)(ws + pl.off_ml) : nullptr;
+  return p;
+}
+
+dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
+
+}  // namespace
+}  // namespace dsa
+
+using namespace dsa;
+
+extern "C" {
+
+int dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+const char* dsa_status_str(dsa_status s) {
+  switch (s) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_NULL: return "a required pointer is NULL";
+    case DSA_ERR_DTYPE: return "bad index dtype (or scale pointer inconsistent with it)";
+    case DSA_ERR_SHAPE: return "a size is out of range";
+    case DSA_ERR_K: return "K must be in 1..2048";
+    case DSA_ERR_ALIGN: return "a pointer is misaligned";
+    case DSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case DSA_ERR_UNSUPPORTED: return "unsupported combination";
+    case DSA_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+size_t dsa_workspace_bytes(const dsa_indexer_args* idx, const dsa_mla_args* mla, int K) {
+  size_t end = 0;
+  if (idx) {
+    if (check_indexer(idx, K) != DSA_OK) return 0;
+    end = plan_indexer(idx, K, 0).end;
+  }
+  if (mla) {
+    if (check_mla(mla, K) != DSA_OK) return 0;
+    if (idx) end = align_up(end + (size_t)idx->T * K * 4, 256);  // indices kept for the layer
+    end = plan_mla(mla, K, end).end;
+  }
+  return end;
+}
+
+dsa_status dsa_indexer_topk(const dsa_indexer_args* a, int K, int32_t* indices_out, void* ws, size_t ws_bytes,
+                            void* stream) {
+  dsa_status st = check_indexer(a, K);
+  if (st != DSA_OK) return st;
+  if (!indices_out) return DSA_ERR_NULL;
+  if (!aligned(indices_out, 4)) return DSA_ERR_ALIGN;
+  const IdxPlan pl = plan_indexer(a, K, 0);
+  if (!ws || ws_bytes < pl.end || !aligned(ws, 256)) return DSA_ERR_WORKSPACE;
+  IdxParams p = make_idx_params(a, K, indices_out, (unsigned char*)ws, pl);
+  return hip_status(launch_indexer(p, a->idx_dtype == DSA_IDX_FP8_E4M3FN, a->D_idx, pl.grid, (hipStream_t)stream));
+}
+
+dsa_status dsa_sparse_mla_attn(const dsa_mla_args* m, const int32_t* indices, int K, float scale, void* out, void* ws,
+                               size_t ws_bytes, void* stream) {
+  dsa_status st = check_mla(m, K);
+  if (st != DSA_OK) return st;
+  if (!indices || !out) return DSA_ERR_NULL;
+  if (!aligned(indices, 4) || !aligned(out, 8)) return DSA_ERR_ALIGN;
+  const MlaPlan pl = plan_mla(m, K, 0);
+  if (pl.end > 0 && (!ws || ws_bytes < pl.end || !aligned(ws, 256))) return DSA_ERR_WORKSPACE;
+  MlaParams p = make_mla_params(m, indices, K, scale, out, (unsigned char*)ws, pl);
+  return hip_status(launch_mla(p, (hipStream_t)stream));
+}
+
+dsa_status dsa_layer(const dsa_indexer_args* idx, const dsa_mla_args* mla, int K, float scale, int32_t* indices_out,
+                     void* out, void* ws, size_t ws_bytes, void* stream) {
+  dsa_status st = check_indexer(idx, K);
+  if (st != DSA_OK) return st;
+  st = check_mla(mla, K);
+  if (st != DSA_OK) return st;
+  if (idx->T != mla->T || idx->num_blocks != mla->num_blocks) return DSA_ERR_SHAPE;
+  if (!out) return DSA_ERR_NULL;
+  if (!aligned(out, 8) || !aligned(indices_out, 4)) return DSA_ERR_ALIGN;
+  const IdxPlan ip = plan_indexer(idx, K, 0);
+  const size_t off_idx = align_up(ip.end, 256);
+  const size_t idx_end = align_up(off_idx + (size_t)idx->T * K * 4, 256);
+  const MlaPlan mp = plan_mla(mla, K, idx_end);
+  if (!ws || ws_bytes < mp.end || !aligned(ws, 256)) return DSA_ERR_WORKSPACE;
+  unsigned char* w = (unsigned char*)ws;
+  int32_t* indices = indices_out ? indices_out : (int32_t*)(w + off_idx);
+  hipStream_t s = (hipStream_t)stream;
+  IdxParams p = make_idx_params(idx, K, indices, w, ip);
+  st = hip_status(launch_indexer(p, idx->idx_dtype == DSA_IDX_FP8_E4M3FN, idx->D_idx, ip.grid, s));
+  if (st != DSA_OK) return st;
+  MlaParams q = make_mla_params(mla, indices, K, scale, out, w, mp);
+  return hip_status(launch_mla(q, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,115 @@
+// Device-side helpers shared by the DSA kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+constexpr int PAGE = 64;
+constexpr int LATENT = 576;
+constexpr int VDIM = 512;
+constexpr int KMAX = 2048;
+constexpr int ROUND = 1024;  // keys scored per streaming round of the indexer
+constexpr int FANIN = 8;     // fan-in of the candidate-merge tree
+constexpr int CH_MAX = 65536;  // largest key chunk one indexer workgroup scans
+
+// Order-preserving map fp32 -> uint32 (a < b  <=>  key(a) < key(b)); -0 maps
+// like +0.  Key 0 is below every finite value and marks "no candidate".
+__device__ __forceinline__ uint32_t order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Sum over the four lanes l, l^16, l^32, l^48 (the four k-groups of a 16x16
+// MFMA tile); every one of the four lanes receives the same value.
+__device__ __forceinline__ float sum_lane_groups(float v) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  float s = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+__device__ __forceinline__ float max_lane_groups(float v) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  float s = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also drains every
+// outstanding global load (vmcnt(0)), which would empty the prefetch queues.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Barrier for code that also has direct-to-LDS loads in flight: waits for this
+// wave's LDS instructions only (an LDS-scoped fence would also wait for every
+// outstanding direct-to-LDS load).  Callers wait for the loads they need with
+// an explicit vmcnt before calling it.
+__device__ __forceinline__ void lds_barrier_keep_dma() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// 16-byte global -> LDS copy per lane: lane i writes LDS[lds_base + 16 i].
+// Issued as asm so the compiler does not add its own (drain-everything) wait
+// before later LDS reads; callers wait with an explicit vmcnt.  The asm has no
+// output register, only the address input, and the m0 write is declared.
+__device__ __forceinline__ void dma16_to_lds(const void* gaddr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(lds_base) : "memory", "m0");
+}
+
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
+template <typename T>
+__device__ __forceinline__ T uniform(T v) {
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    uint32_t o = __shfl_up(v, d, 64);
+    if (l >= d) v += o;
+  }
+  return v;
+}
+
+// Tree of candidate lists for one query group: level 0 has n leaves (one per
+// key chunk); level l+1 has ceil(N_l / FANIN) nodes; the single top node is
+// the root.  "Lists" are stored for every non-root node; "counters" exist for
+// every node above level 0.
+__host__ __device__ inline int tree_lists(int n) {
+  int total = 0;
+  while (n > 1) {
+    total += n;
+    n = (n + FANIN - 1) / FANIN;
+  }
+  return total;
+}
+__host__ __device__ inline int tree_counters(int n) {
+  int total = 0;
+  while (n > 1) {
+    n = (n + FANIN - 1) / FANIN;
+    total += n;
+  }
+  return total;
+}
+
+}  // namespace dsa

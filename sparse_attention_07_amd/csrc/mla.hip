@@ -1,0 +1,316 @@
+// Sparse MLA over the selected latent rows, for gfx950.
+//
+// What is computed ("Hybrid Attention LLM Inference Acceleration", section 2,
+// sparse attention computation; "Day-0 Inference Adaptation for LLMs",
+// operator section 2: the filter results go straight to the compute kernel):
+// for query token t and head h over the selected rows C_j (576-wide latent,
+// 512 nope + 64 rope),
+//     out[t,h,:] = sum_j softmax_j(scale * q[t,h,:] . C_j) * C_j[:512].
+//
+// Design for CDNA4:
+//  * grid = (split, query); a workgroup owns a contiguous slice of the query's
+//    index list and all H heads, so every gathered row leaves HBM once;
+//  * rows are gathered 32 at a time with direct-to-LDS 16-byte loads
+//    (global_load_lds_dwordx4) into a 3-stage ring; rows sit at a padded
+//    stride of 73 sixteen-byte units (1168 B = 292 dwords, so consecutive rows
+//    start 36 banks apart) and operand addresses stay base + immediate;
+//  * H/16 waves.  Logits: wave w owns heads 16w..16w+15, keeps their q in
+//    registers as the MFMA B operand and computes S^T = C q^T (bf16 16x16x32;
+//    rows on M in an order that makes the probabilities come out as 8
+//    consecutive rows per lane), runs the online softmax (exp2 domain) and
+//    writes P^T (bf16) and the per-head rescale factor to LDS.
+//    PV: wave w owns value dims [512w/NW, 512(w+1)/NW) for all heads and
+//    accumulates O^T += C^T P^T, reading C^T with the gfx950 LDS transpose
+//    read (ds_read_b64_tr_b16) and P^T with plain 16-byte reads;
+//  * the O rescale is skipped for a wave when no head's running max moved;
+//  * with several splits, partial (O, m, l) go to the workspace and a small
+//    kernel merges them with log-sum-exp weights.
+#include "dsa_device.h"
+#include "dsa_params.h"
+
+namespace dsa {
+
+constexpr int TILE_ROWS = 32;
+constexpr int ROW_UNITS = LATENT * 2 / 16;                         // 72 sixteen-byte units per row
+constexpr int ROW_STRIDE = ROW_UNITS + 1;                          // padded row stride (units)
+constexpr int TILE_LOADS = (TILE_ROWS * ROW_STRIDE + 63) / 64;     // 37 wave-loads of 64 units
+constexpr int STAGES = 3;
+constexpr int STAGE_BYTES = TILE_LOADS * 64 * 16;
+
+// byte offset, inside a stage, of bf16 element (row r, column col)
+__device__ __forceinline__ int stage_off(int r, int col) { return 16 * (r * ROW_STRIDE + (col >> 3)) + 2 * (col & 7); }
+
+template <int NW>
+struct MlaSmem {
+  unsigned char stage[STAGES][STAGE_BYTES];
+  uint16_t pt[16 * NW][TILE_ROWS];  // P^T as [head][row] bf16
+  float alpha[16 * NW];
+  float mfin[16 * NW];
+  float lfin[16 * NW];
+  // followed by the slice's slots (int32)
+};
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) {
+  constexpr int NT = NW * 64;
+  constexpr int H = 16 * NW;
+  constexpr int VT = 32 / NW;  // 16-wide value tiles per wave in PV
+  constexpr int LMIN = TILE_LOADS / NW;                // DMA loads of every wave per tile
+  constexpr int LEXTRA = TILE_LOADS - LMIN * NW;       // waves [0, LEXTRA) issue one more
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  MlaSmem<NW>& sm = *reinterpret_cast<MlaSmem<NW>*>(smem_raw);
+  int32_t* sidx = reinterpret_cast<int32_t*>(smem_raw + sizeof(MlaSmem<NW>));
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int g4 = lane >> 4;
+  const int n16 = lane & 15;
+  const int t = blockIdx.y;
+  const int s = blockIdx.x;
+  const int r_begin = s * p.rows_per_split;
+  const int r_end = min(p.K, r_begin + p.rows_per_split);
+  const int nrows = max(0, r_end - r_begin);
+  const int ntiles = (nrows + TILE_ROWS - 1) / TILE_ROWS;
+
+  // ---- the slice's pool slots (invalid -> -1)
+  for (int i = tid; i < ntiles * TILE_ROWS; i += NT) {
+    int v = -1;
+    if (i < nrows) {
+      v = p.indices[(int64_t)t * p.K + r_begin + i];
+      if (v < 0 || (int64_t)v >= p.num_slots) v = -1;
+    }
+    sidx[i] = v;
+  }
+
+  // ---- q of this wave's 16 heads as the logits B operand (k = latent dim)
+  const int hq = wave * 16 + n16;
+  v4i qb[18];
+  {
+    const uint16_t* qrow = p.q + ((int64_t)t * H + hq) * LATENT;
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) qb[ks] = *reinterpret_cast<const v4i*>(qrow + 32 * ks + 8 * g4);
+  }
+  // retire every plain global load here, so no compiler-inserted wait inside the
+  // tile loop can count (and drain) the row DMA queue
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+  lds_barrier();
+
+  auto issue_tile = [&](int ti) {
+    unsigned char* st = sm.stage[ti % STAGES];
+    const int nl = LMIN + (wave < LEXTRA ? 1 : 0);
+    const int first = wave * LMIN + min(wave, LEXTRA);
+    for (int k = 0; k < nl; ++k) {
+      const int u0 = (first + k) * 64;
+      const int u = u0 + lane;
+      int r = u / ROW_STRIDE;
+      int c = u - r * ROW_STRIDE;
+      if (r >= TILE_ROWS || c >= ROW_UNITS) {  // padding slot: fetch a harmless valid unit
+        r = min(r, TILE_ROWS - 1);
+        c = 0;
+      }
+      int slot = sidx[ti * TILE_ROWS + r];
+      slot = slot < 0 ? 0 : slot;
+      const uint16_t* g = p.kv + (int64_t)slot * LATENT + 8 * c;
+      const uint32_t lds_addr =
+          (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)(st + 16 * u0);
+      dma16_to_lds(g, uniform(lds_addr));
+    }
+  };
+
+  v4f o[VT][NW];  // O^T[v tile][head tile]
+#pragma unroll
+  for (int vt = 0; vt < VT; ++vt)
+#pragma unroll
+    for (int nt = 0; nt < NW; ++nt) o[vt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;  // for head hq (logits role)
+
+  if (ntiles > 0) issue_tile(0);
+  if (ntiles > 1) issue_tile(1);
+
+  for (int ti = 0; ti < ntiles; ++ti) {
+    // this wave's loads of tile ti are done when at most one newer tile is in flight
+    if (ti + 1 < ntiles)
+      __builtin_amdgcn_s_waitcnt((LMIN & 15) | ((LMIN >> 4) << 14) | (7 << 4) | (15 << 8));
+    else
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    lds_barrier_keep_dma();
+    if (ti + 2 < ntiles) issue_tile(ti + 2);
+    const unsigned char* st = sm.stage[ti % STAGES];
+
+    // ---- logits S^T[row, head] for heads 16w..16w+15
+    const uint32_t vmask = (uint32_t)ballot(lane < 32 && sidx[ti * TILE_ROWS + (lane & 31)] >= 0);
+    v4f acc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+    // M-tile row n16 holds tile row 8*(n16/4) + 4*mt + n16%4; k-step ks adds 64 bytes
+    const unsigned char* la0 = st + 16 * ((8 * (n16 >> 2) + (n16 & 3)) * ROW_STRIDE + g4);
+    const unsigned char* la1 = la0 + 16 * 4 * ROW_STRIDE;
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) {
+      const v4i a0 = *reinterpret_cast<const v4i*>(la0 + 64 * ks);
+      const v4i a1 = *reinterpret_cast<const v4i*>(la1 + 64 * ks);
+      acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a0), __builtin_bit_cast(v8bf, qb[ks]),
+                                                       acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a1), __builtin_bit_cast(v8bf, qb[ks]),
+                                                       acc[1], 0, 0, 0);
+    }
+    // ---- online softmax: this lane holds head hq, rows 8*g4 + 4*mt + i
+    {
+      float x[8];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 8 * g4 + 4 * mt + i;
+          const bool ok = (vmask >> row) & 1u;
+          x[4 * mt + i] = ok ? acc[mt][i] * p.scale_log2 : -INFINITY;
+          tmax = fmaxf(tmax, x[4 * mt + i]);
+        }
+      tmax = max_lane_groups(tmax);
+      const float m_new = fmaxf(m_run, tmax);
+      const float a_ = (m_new > m_run) ? exp2f(m_run - m_new) : 1.f;
+      float lsum = 0.f;
+      __bf16 pv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float pr = (m_new == -INFINITY) ? 0.f : exp2f(x[j] - m_new);
+        lsum += pr;
+        pv[j] = (__bf16)pr;
+      }
+      l_run = l_run * a_ + lsum;
+      m_run = m_new;
+      *reinterpret_cast<v4i*>(&sm.pt[hq][8 * g4]) = __builtin_bit_cast(v4i, pv);
+      if (g4 == 0) sm.alpha[hq] = a_;
+    }
+    lds_barrier_keep_dma();
+
+    // ---- PV: O^T[v, head] = alpha * O^T + C^T[v, row] P^T[row, head], v in this wave's slice
+    {
+      float al[NW];
+      bool any = false;
+#pragma unroll
+      for (int nt = 0; nt < NW; ++nt) {
+        al[nt] = sm.alpha[16 * nt + n16];
+        any |= (al[nt] != 1.f);
+      }
+      if (__builtin_amdgcn_ballot_w64(any)) {
+#pragma unroll
+        for (int vt = 0; vt < VT; ++vt)
+#pragma unroll
+          for (int nt = 0; nt < NW; ++nt) o[vt][nt] *= al[nt];
+      }
+      // transpose-read base: row 8*g4 + n16/4, column 16*(wave*VT) + 4*(n16%4); v tile vt adds 32 bytes
+      const unsigned char* tb = st + stage_off(8 * g4 + (n16 >> 2), wave * VT * 16 + 4 * (n16 & 3));
+      v8bf av[VT];
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt) {
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(tb + 32 * vt));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(tb + 16 * 4 * ROW_STRIDE + 32 * vt));
+        av[vt] = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int nt = 0; nt < NW; ++nt) {
+        const v4i pb = *reinterpret_cast<const v4i*>(&sm.pt[16 * nt + n16][8 * g4]);
+#pragma unroll
+        for (int vt = 0; vt < VT; ++vt)
+          o[vt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[vt], __builtin_bit_cast(v8bf, pb), o[vt][nt], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- epilogue: per-head (m, l) from the logits role, then normalise/store
+  {
+    const float l_tot = sum_lane_groups(l_run);
+    if (g4 == 0) {
+      sm.mfin[hq] = m_run;
+      sm.lfin[hq] = l_tot;
+    }
+  }
+  lds_barrier();
+#pragma unroll
+  for (int nt = 0; nt < NW; ++nt) {
+    const int h = 16 * nt + n16;
+    if (p.S == 1) {
+      const float l_tot = sm.lfin[h];
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      uint16_t* orow = p.out + ((int64_t)t * H + h) * VDIM;
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt) {
+        __bf16 b4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b4[i] = (__bf16)(o[vt][nt][i] * inv);
+        *reinterpret_cast<uint2*>(orow + (wave * VT + vt) * 16 + 4 * g4) = __builtin_bit_cast(uint2, b4);
+      }
+    } else {
+      const int64_t rowi = ((int64_t)t * p.S + s) * H + h;
+      float* prow = p.part_o + rowi * VDIM;
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt) *reinterpret_cast<v4f*>(prow + (wave * VT + vt) * 16 + 4 * g4) = o[vt][nt];
+    }
+  }
+  if (p.S > 1 && tid < H) {
+    const int64_t rowi = ((int64_t)t * p.S + s) * H + tid;
+    p.part_ml[rowi * 2 + 0] = sm.mfin[tid];
+    p.part_ml[rowi * 2 + 1] = sm.lfin[tid];
+  }
+}
+
+// Merge S partial results per (query, head): out = sum_s e^(m_s-M) O_s / sum_s e^(m_s-M) l_s
+__global__ __launch_bounds__(128) void dsa_mla_combine_kernel(MlaParams p) {
+  const int th = blockIdx.x;  // t * H + h
+  const int t = th / p.H, h = th % p.H;
+  const int v = threadIdx.x * 4;
+  float M = -INFINITY;
+  for (int s = 0; s < p.S; ++s) M = fmaxf(M, p.part_ml[(((int64_t)t * p.S + s) * p.H + h) * 2]);
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < p.S; ++s) {
+      const int64_t rowi = ((int64_t)t * p.S + s) * p.H + h;
+      const float ms = p.part_ml[rowi * 2], ls = p.part_ml[rowi * 2 + 1];
+      if (ms == -INFINITY) continue;
+      const float wgt = exp2f(ms - M);
+      L += wgt * ls;
+      const v4f ov = *reinterpret_cast<const v4f*>(p.part_o + rowi * VDIM + v);
+      acc += wgt * ov;
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  __bf16 b4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b4[i] = (__bf16)(acc[i] * inv);
+  *reinterpret_cast<uint2*>(p.out + (int64_t)th * VDIM + v) = __builtin_bit_cast(uint2, b4);
+}
+
+template <int NW>
+static size_t mla_smem_t(int rows_per_split) {
+  const int tiles = (rows_per_split + TILE_ROWS - 1) / TILE_ROWS;
+  return sizeof(MlaSmem<NW>) + (size_t)tiles * TILE_ROWS * 4;
+}
+
+size_t mla_smem_bytes(int rows_per_split) { return mla_smem_t<8>(rows_per_split); }
+
+template <int NW>
+static hipError_t launch_mla_t(const MlaParams& p, hipStream_t st) {
+  auto kfn = dsa_mla_split_kernel<NW>;
+  const size_t smem = mla_smem_t<NW>(p.rows_per_split);
+  hipError_t e = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kfn, dim3(p.S, p.T), dim3(NW * 64), smem, st, p);
+  e = hipGetLastError();
+  if (e != hipSuccess || p.S == 1) return e;
+  hipLaunchKernelGGL(dsa_mla_combine_kernel, dim3(p.T * p.H), dim3(128), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_mla(const MlaParams& p, hipStream_t st) {
+  switch (p.H) {
+    case 16: return launch_mla_t<1>(p, st);
+    case 32: return launch_mla_t<2>(p, st);
+    case 64: return launch_mla_t<4>(p, st);
+    default: return launch_mla_t<8>(p, st);
+  }
+}
+
+}  // namespace dsa

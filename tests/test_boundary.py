@@ -1,0 +1,183 @@
+"""CPU tests of the C ABI: the library loads, exports every function that
+include/dsa.h declares, the ctypes structs match the C layout, and every
+argument error is reported before anything is launched (no GPU needed: each
+case below stops at a host-side check)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+dsa = pytest.importorskip("sparse_attention_07_amd.dsa", reason="libdsa.so not built")
+
+OK, E_NULL, E_DTYPE, E_SHAPE, E_K, E_ALIGN, E_WS, E_UNSUP, E_HIP = range(9)
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(dsa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert set(names) == set(dsa.EXPORTS), names
+    out = subprocess.run(["nm", "-D", "--defined-only", dsa.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(dsa.LIB, n)
+
+
+def test_abi_version_and_status_strings():
+    assert dsa.LIB.dsa_abi_version() == 1
+    m = re.search(r"#define DSA_ABI_VERSION (\d+)", open(HEADER).read())
+    assert int(m.group(1)) == 1
+    assert dsa.status_str(0) == "ok"
+    for s in range(1, 9):
+        assert dsa.status_str(s) and dsa.status_str(s) != "unknown status"
+    assert dsa.status_str(99) == "unknown status"
+
+
+def test_ctypes_structs_match_c_layout(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include <stddef.h>
+#include "dsa.h"
+#define F(s, f) printf(#s "." #f " %zu\n", offsetof(s, f))
+int main(void) {
+  printf("dsa_indexer_args %zu\n", sizeof(dsa_indexer_args));
+  printf("dsa_mla_args %zu\n", sizeof(dsa_mla_args));
+  F(dsa_indexer_args, T); F(dsa_indexer_args, idx_dtype); F(dsa_indexer_args, q_idx);
+  F(dsa_indexer_args, q_idx_scale); F(dsa_indexer_args, w); F(dsa_indexer_args, k_idx_pool);
+  F(dsa_indexer_args, num_blocks); F(dsa_indexer_args, block_table); F(dsa_indexer_args, max_blocks);
+  F(dsa_indexer_args, seq_lens); F(dsa_indexer_args, q_seq); F(dsa_indexer_args, q_visible);
+  F(dsa_indexer_args, max_q_per_seq);
+  F(dsa_mla_args, T); F(dsa_mla_args, H); F(dsa_mla_args, q); F(dsa_mla_args, kv_pool); F(dsa_mla_args, num_blocks);
+  return 0;
+}
+''')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = dict(l.rsplit(" ", 1) for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                         check=True).stdout.splitlines())
+    assert int(got["dsa_indexer_args"]) == ctypes.sizeof(dsa.IndexerArgs)
+    assert int(got["dsa_mla_args"]) == ctypes.sizeof(dsa.MlaArgs)
+    for k, v in got.items():
+        if "." in k:
+            s, f = k.split(".")
+            cls = dsa.IndexerArgs if s == "dsa_indexer_args" else dsa.MlaArgs
+            assert getattr(cls, f).offset == int(v), k
+
+
+# ---------------------------------------------------------------- validation (host-only paths)
+_buf = ctypes.create_string_buffer(1 << 12)
+_base = (ctypes.addressof(_buf) + 255) // 256 * 256  # aligned fake address, never dereferenced
+
+
+def good_idx(**kw):
+    a = dsa.IndexerArgs()
+    a.T, a.B, a.H_idx, a.D_idx, a.idx_dtype = 4, 4, 64, 128, dsa.IDX_FP8_E4M3FN
+    a.q_idx = a.q_idx_scale = a.w = a.k_idx_pool = a.block_table = a.seq_lens = _base
+    a.num_blocks, a.max_blocks, a.max_q_per_seq = 100, 10, 1
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def good_mla(**kw):
+    m = dsa.MlaArgs()
+    m.T, m.H, m.q, m.kv_pool, m.num_blocks = 4, 128, _base, _base, 100
+    for k, v in kw.items():
+        setattr(m, k, v)
+    return m
+
+
+def call_idx(a, K=2048, out=_base, ws=None, ws_bytes=0):
+    return dsa.LIB.dsa_indexer_topk(None if a is None else ctypes.byref(a), K, out, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,K,expect", [
+    ({}, 0, E_K), ({}, 2049, E_K), ({}, -5, E_K),
+    (dict(idx_dtype=7), 2048, E_DTYPE),
+    (dict(q_idx=None), 2048, E_NULL), (dict(w=None), 2048, E_NULL), (dict(k_idx_pool=None), 2048, E_NULL),
+    (dict(block_table=None), 2048, E_NULL), (dict(seq_lens=None), 2048, E_NULL),
+    (dict(q_idx_scale=None), 2048, E_NULL),
+    (dict(idx_dtype=dsa.IDX_BF16), 2048, E_DTYPE),  # bf16 with a scale pointer
+    (dict(T=0), 2048, E_SHAPE), (dict(B=0), 2048, E_SHAPE), (dict(H_idx=0), 2048, E_SHAPE),
+    (dict(H_idx=65), 2048, E_SHAPE), (dict(max_blocks=0), 2048, E_SHAPE), (dict(num_blocks=0), 2048, E_SHAPE),
+    (dict(max_q_per_seq=0), 2048, E_SHAPE), (dict(T=5), 2048, E_SHAPE),  # no q_seq and T != B
+    (dict(D_idx=64), 2048, E_UNSUP),  # FP8 with 64-wide heads
+    (dict(idx_dtype=dsa.IDX_BF16, q_idx_scale=None, D_idx=96), 2048, E_SHAPE),
+    (dict(q_idx=_base + 8), 2048, E_ALIGN), (dict(k_idx_pool=_base + 4), 2048, E_ALIGN),
+    (dict(w=_base + 2), 2048, E_ALIGN), (dict(q_seq=_base + 1), 2048, E_ALIGN),
+    (dict(num_blocks=1 << 26), 2048, E_SHAPE),
+])
+def test_indexer_argument_errors(kw, K, expect):
+    assert call_idx(good_idx(**kw), K) == expect
+
+
+def test_indexer_null_struct_output_and_workspace():
+    assert call_idx(None) == E_NULL
+    assert call_idx(good_idx(), out=None) == E_NULL
+    assert call_idx(good_idx(), out=_base + 2) == E_ALIGN
+    assert call_idx(good_idx(), ws=None) == E_WS
+    need = dsa.workspace_bytes(good_idx(), None, 2048)
+    assert need > 0
+    assert call_idx(good_idx(), ws=_base, ws_bytes=need - 1) == E_WS
+    assert call_idx(good_idx(), ws=_base + 16, ws_bytes=need) == E_WS  # workspace must be 256-B aligned
+
+
+def call_mla(m, K=2048, idx=_base, out=_base, ws=None, ws_bytes=0):
+    return dsa.LIB.dsa_sparse_mla_attn(None if m is None else ctypes.byref(m), idx, K, 0.04, out, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(H=48), E_SHAPE), (dict(H=256), E_SHAPE), (dict(T=0), E_SHAPE), (dict(num_blocks=0), E_SHAPE),
+    (dict(q=None), E_NULL), (dict(kv_pool=None), E_NULL), (dict(q=_base + 8), E_ALIGN),
+    (dict(kv_pool=_base + 2), E_ALIGN),
+])
+def test_mla_argument_errors(kw, expect):
+    assert call_mla(good_mla(**kw)) == expect
+
+
+def test_mla_null_and_workspace():
+    assert call_mla(None) == E_NULL
+    assert call_mla(good_mla(), idx=None) == E_NULL
+    assert call_mla(good_mla(), out=None) == E_NULL
+    assert call_mla(good_mla(), out=_base + 4) == E_ALIGN
+    assert call_mla(good_mla(), K=0) == E_K
+    # 4 queries -> the rows are split and partial results need workspace
+    assert dsa.workspace_bytes(None, good_mla(), 2048) > 0
+    assert call_mla(good_mla()) == E_WS
+
+
+def test_layer_argument_errors():
+    def call(a, m, out=_base, ws=None, ws_bytes=0, idx_out=None):
+        return dsa.LIB.dsa_layer(ctypes.byref(a), ctypes.byref(m), 2048, 0.04, idx_out, out, ws, ws_bytes, None)
+    assert call(good_idx(), good_mla(T=3)) == E_SHAPE
+    assert call(good_idx(), good_mla(num_blocks=99)) == E_SHAPE
+    assert call(good_idx(), good_mla(), out=None) == E_NULL
+    assert call(good_idx(), good_mla(), idx_out=_base + 1) == E_ALIGN
+    assert call(good_idx(H_idx=0), good_mla()) == E_SHAPE
+    assert call(good_idx(), good_mla(H=3)) == E_SHAPE
+    need = dsa.workspace_bytes(good_idx(), good_mla(), 2048)
+    assert need > dsa.workspace_bytes(good_idx(), None, 2048)
+    assert call(good_idx(), good_mla(), ws=_base, ws_bytes=need - 256) == E_WS
+
+
+def test_workspace_bytes_invalid_and_scaling():
+    assert dsa.workspace_bytes(good_idx(T=0), None, 2048) == 0
+    assert dsa.workspace_bytes(None, good_mla(H=7), 2048) == 0
+    # 64 sequences of up to 128K tokens: bounded candidate storage (well under 1 GB)
+    a = good_idx(T=64, B=64, max_blocks=2048, num_blocks=100000)
+    n = dsa.workspace_bytes(a, good_mla(T=64, num_blocks=100000), 2048)
+    assert 0 < n < (1 << 30)
+    # a single short-context decode needs no candidate lists (one chunk per query)
+    small = dsa.workspace_bytes(good_idx(T=1, B=1, max_blocks=64), None, 256)
+    assert 0 < small < 4096

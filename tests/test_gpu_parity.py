@@ -1,0 +1,95 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Small cases are checked on every query; they span several key chunks, merge
+tree levels, 1024-key rounds and 32-row attention tiles, with ragged tails.
+The five named workloads run at full size in the launch configuration the
+benchmark times, with sampled queries checked one by one."""
+import pytest
+import torch
+
+from gpu_cases import check_queries, say
+from sparse_attention_07_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from sparse_attention_07_amd import dsa
+DEV = "cuda"
+
+
+def run_case(spec, queries=None, prefill_chunk=None, unit=True, check=True):
+    say(f"[case] {spec.name} chunk={prefill_chunk}")
+    case = synth.build_case(spec, device=DEV, prefill_chunk=prefill_chunk)
+    layer = dsa.layer_from_case(case)
+    layer()
+    torch.cuda.synchronize()
+    say(f"  layer ran: T={case.T} B={case.B} K={spec.K} H={spec.H}")
+    if not check:
+        return case, layer
+    qs = range(case.T) if queries is None else queries
+    mla_unit = (lambda idx: dsa.sparse_mla_attn(case.q, case.kv_pool, idx, spec.scale)) if unit else None
+    check_queries(case, layer.indices, layer.out, qs, mla_unit=mla_unit)
+    return case, layer
+
+
+def spec(name, **kw):
+    base = dict(H_idx=64, D_idx=128, idx_dtype="fp8", K=2048, H=128)
+    base.update(kw)
+    return synth.CaseSpec(name, **base)
+
+
+# --------------------------------------------------------------------------- small, every query
+def test_tiny_decode_preset():
+    run_case(synth.PRESETS["tiny_decode"])
+
+
+def test_bf16_decode_ragged_multichunk():
+    run_case(spec("bf16_ragged", idx_dtype="bf16", lens=[5000, 64, 12345, 2047], seed=3))
+
+
+def test_fp8_decode_two_level_merge_tree():
+    # 40000 keys at 4096-key chunks: 10 chunk lists, two merge levels
+    run_case(spec("fp8_tree", lens=[40000, 1000, 3], seed=5))
+
+
+def test_speculative_multi_query_groups():
+    run_case(spec("spec_mix", lens=[3000, 9000, 20000, 130], queries_per_seq=[1, 4, 2, 3], seed=7))
+
+
+@pytest.mark.parametrize("chunk", [0, 1, 2])
+def test_prefill_chunks_causal(chunk):
+    run_case(spec("prefill_small", prefill=(6000, 2048), K=512, H=64, seed=11), prefill_chunk=chunk,
+             queries=[0, 1, 511, 512, 513, 1000, 2047] if chunk < 2 else None)
+
+
+def test_edge_lengths_and_small_k():
+    run_case(spec("edges_bf16", idx_dtype="bf16", H_idx=4, D_idx=64, K=4, H=16, lens=[0, 1, 63, 65, 4], seed=13))
+    run_case(spec("edges_k1", H_idx=16, K=1, H=32, lens=[1, 2, 700], seed=17))
+
+
+def test_deterministic_bitwise():
+    case = synth.build_case(spec("det", lens=[20000, 7000, 33333], seed=19), device=DEV)
+    layer = dsa.layer_from_case(case)
+    layer()
+    i1, o1 = layer.indices.clone(), layer.out.clone()
+    layer()
+    torch.cuda.synchronize()
+    assert torch.equal(i1, layer.indices)
+    assert torch.equal(o1.view(torch.int16), layer.out.view(torch.int16))
+
+
+# --------------------------------------------------------------------------- full-size workloads, sampled
+def test_full_decode_b32_32k():
+    run_case(synth.PRESETS["decode_b32_32k"], queries=[0, 17, 31])
+
+
+def test_full_decode_b64_128k_fp8():
+    run_case(synth.PRESETS["decode_b64_128k_fp8"], queries=[0, 40, 63])
+
+
+def test_full_prefill_16k_last_chunk():
+    run_case(synth.PRESETS["prefill_16k"], prefill_chunk=3, queries=[0, 1, 2047, 4095])
+
+
+def test_full_mixed_1m():
+    run_case(synth.PRESETS["mixed_1m"], queries=[0, 3, 7, 10])
