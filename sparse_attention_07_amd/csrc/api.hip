@@ -10,13 +10,11 @@
 #include "dsa_params.h"
 
 namespace dsa {
-hipError_t launch_indexer(const IdxParams& p, int is_fp8, int D, int grid, hipStream_t st);
+hipError_t launch_indexer(const IdxParams& p, int is_fp8, int D, int grid, bool need_merge, hipStream_t st);
 hipError_t launch_mla(const MlaParams& p, hipStream_t st);
 
 namespace {
 
-constexpr int TARGET_ITEMS = 1024;  // key chunks aimed for per indexer call
-constexpr int CH_MIN = 4096;        // smallest chunk (keys)
 constexpr int MLA_TARGET_WGS = 256;
 constexpr int MLA_MIN_ROWS = 256;
 
@@ -24,8 +22,11 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 struct IdxPlan {
-  int MQ = 1, CH = 0, nch_max = 1, U = 0, I = 0, grid = 0;
-  size_t off_hdr = 0, off_groups = 0, off_ctr = 0, off_lcnt = 0, off_lkeys = 0, off_lpos = 0, end = 0;
+  int MQ = 1, nwg = 256;
+  bool need_merge = false;
+  int64_t lists = 0;  // candidate lists the workspace holds
+  size_t off_hdr = 0, off_groups = 0, off_qgroup = 0, off_lcnt = 0, off_lmin = 0, off_lkeys = 0, off_lpos = 0,
+         end = 0;
 };
 
 struct MlaPlan {
@@ -65,38 +66,43 @@ dsa_status check_mla(const dsa_mla_args* m, int K) {
   return DSA_OK;
 }
 
-IdxPlan plan_indexer(const dsa_indexer_args* a, int K, size_t base) {
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  return n;
+}
+
+// nwg: indexer workgroups (one per CU); the workspace depends on it, so the
+// same value must be used for sizing and for the call.
+IdxPlan plan_indexer(const dsa_indexer_args* a, int K, size_t base, int nwg) {
   IdxPlan pl;
   pl.MQ = a->max_q_per_seq >= 3 ? 4 : a->max_q_per_seq;
+  pl.nwg = nwg;
   const int64_t maxlen = (int64_t)a->max_blocks * DSA_PAGE_TOKENS;
-  const int64_t groups_est = a->q_seq ? std::min<int64_t>(a->T, a->B + (a->T + pl.MQ - 1) / pl.MQ) : a->T;
-  int64_t ch = (groups_est * maxlen + TARGET_ITEMS - 1) / TARGET_ITEMS;
-  ch = std::max<int64_t>(ch, CH_MIN);
-  ch = (ch + ROUND - 1) / ROUND * ROUND;
-  const int64_t ch_cap = (maxlen + ROUND - 1) / ROUND * ROUND;
-  ch = std::min(ch, ch_cap);
-  ch = std::min<int64_t>(ch, CH_MAX);
-  pl.CH = (int)ch;
-  pl.nch_max = (int)((maxlen + ch - 1) / ch);
-  pl.U = tree_lists(pl.nch_max);
-  pl.I = tree_counters(pl.nch_max);
   const int64_t T = a->T;
+  // a query group is split over workgroups (and then needs candidate lists and
+  // the merge) only if the whole key space exceeds one minimum slice
+  const int64_t max_total = T * std::max<int64_t>(16, (maxlen + 15) & ~15);
+  pl.need_merge = max_total > MIN_SLICE;
+  pl.lists = pl.need_merge ? (int64_t)2 * pl.MQ * nwg : 0;
   size_t off = align_up(base, 256);
   pl.off_hdr = off;
   off = align_up(off + 64, 256);
   pl.off_groups = off;
   off = align_up(off + (size_t)T * G_FIELDS * 4, 256);
-  pl.off_ctr = off;
-  off = align_up(off + (size_t)T * pl.I * 4, 256);
+  pl.off_qgroup = off;
+  off = align_up(off + (size_t)T * 4, 256);
   pl.off_lcnt = off;
-  off = align_up(off + (size_t)T * pl.U * 4, 256);
+  off = align_up(off + (size_t)pl.lists * 4, 256);
+  pl.off_lmin = off;
+  off = align_up(off + (size_t)pl.lists * 4, 256);
   pl.off_lkeys = off;
-  off = align_up(off + (size_t)T * pl.U * K * 4, 256);
+  off = align_up(off + (size_t)pl.lists * K * 4, 256);
   pl.off_lpos = off;
-  off = align_up(off + (size_t)T * pl.U * K * 4, 256);
+  off = align_up(off + (size_t)pl.lists * K * 4, 256);
   pl.end = off;
-  const int64_t items_max = T * pl.nch_max;
-  pl.grid = (int)std::min<int64_t>(items_max, 256);
   return pl;
 }
 
@@ -138,13 +144,14 @@ IdxParams make_idx_params(const dsa_indexer_args* a, int K, int32_t* indices, un
   p.B = a->B;
   p.H_idx = a->H_idx;
   p.K = K;
-  p.CH = pl.CH;
+  p.nwg = pl.nwg;
   p.MQ = pl.MQ;
   p.indices = indices;
   p.hdr = (int32_t*)(ws + pl.off_hdr);
   p.groups = (int32_t*)(ws + pl.off_groups);
-  p.ctr = (uint32_t*)(ws + pl.off_ctr);
+  p.qgroup = (int32_t*)(ws + pl.off_qgroup);
   p.list_cnt = (int32_t*)(ws + pl.off_lcnt);
+  p.list_min = (uint32_t*)(ws + pl.off_lmin);
   p.list_keys = (uint32_t*)(ws + pl.off_lkeys);
   p.list_pos = (int32_t*)(ws + pl.off_lpos);
   return p;
@@ -199,7 +206,7 @@ size_t dsa_workspace_bytes(const dsa_indexer_args* idx, const dsa_mla_args* mla,
   size_t end = 0;
   if (idx) {
     if (check_indexer(idx, K) != DSA_OK) return 0;
-    end = plan_indexer(idx, K, 0).end;
+    end = plan_indexer(idx, K, 0, device_cus()).end;
   }
   if (mla) {
     if (check_mla(mla, K) != DSA_OK) return 0;
@@ -215,10 +222,11 @@ dsa_status dsa_indexer_topk(const dsa_indexer_args* a, int K, int32_t* indices_o
   if (st != DSA_OK) return st;
   if (!indices_out) return DSA_ERR_NULL;
   if (!aligned(indices_out, 4)) return DSA_ERR_ALIGN;
-  const IdxPlan pl = plan_indexer(a, K, 0);
+  const IdxPlan pl = plan_indexer(a, K, 0, device_cus());
   if (!ws || ws_bytes < pl.end || !aligned(ws, 256)) return DSA_ERR_WORKSPACE;
   IdxParams p = make_idx_params(a, K, indices_out, (unsigned char*)ws, pl);
-  return hip_status(launch_indexer(p, a->idx_dtype == DSA_IDX_FP8_E4M3FN, a->D_idx, pl.grid, (hipStream_t)stream));
+  return hip_status(launch_indexer(p, a->idx_dtype == DSA_IDX_FP8_E4M3FN, a->D_idx, pl.nwg, pl.need_merge,
+                                   (hipStream_t)stream));
 }
 
 dsa_status dsa_sparse_mla_attn(const dsa_mla_args* m, const int32_t* indices, int K, float scale, void* out, void* ws,
@@ -242,7 +250,7 @@ dsa_status dsa_layer(const dsa_indexer_args* idx, const dsa_mla_args* mla, int K
   if (idx->T != mla->T || idx->num_blocks != mla->num_blocks) return DSA_ERR_SHAPE;
   if (!out) return DSA_ERR_NULL;
   if (!aligned(out, 8) || !aligned(indices_out, 4)) return DSA_ERR_ALIGN;
-  const IdxPlan ip = plan_indexer(idx, K, 0);
+  const IdxPlan ip = plan_indexer(idx, K, 0, device_cus());
   const size_t off_idx = align_up(ip.end, 256);
   const size_t idx_end = align_up(off_idx + (size_t)idx->T * K * 4, 256);
   const MlaPlan mp = plan_mla(mla, K, idx_end);
@@ -251,7 +259,7 @@ dsa_status dsa_layer(const dsa_indexer_args* idx, const dsa_mla_args* mla, int K
   int32_t* indices = indices_out ? indices_out : (int32_t*)(w + off_idx);
   hipStream_t s = (hipStream_t)stream;
   IdxParams p = make_idx_params(idx, K, indices, w, ip);
-  st = hip_status(launch_indexer(p, idx->idx_dtype == DSA_IDX_FP8_E4M3FN, idx->D_idx, ip.grid, s));
+  st = hip_status(launch_indexer(p, idx->idx_dtype == DSA_IDX_FP8_E4M3FN, idx->D_idx, ip.nwg, ip.need_merge, s));
   if (st != DSA_OK) return st;
   MlaParams q = make_mla_params(mla, indices, K, scale, out, w, mp);
   return hip_status(launch_mla(q, s));

@@ -17,8 +17,9 @@ constexpr int LATENT = 576;
 constexpr int VDIM = 512;
 constexpr int KMAX = 2048;
 constexpr int ROUND = 1024;  // keys scored per streaming round of the indexer
-constexpr int FANIN = 8;     // fan-in of the candidate-merge tree
-constexpr int CH_MAX = 65536;  // largest key chunk one indexer workgroup scans
+constexpr int MIN_SLICE = 4096;       // smallest key slice an indexer workgroup is given
+constexpr int SUB = 16384;            // keys whose page ids the indexer stages in LDS at once
+constexpr int MRG_MAX_LISTS = 1024;   // most candidate lists of one query the merge accepts
 
 // Order-preserving map fp32 -> uint32 (a < b  <=>  key(a) < key(b)); -0 maps
 // like +0.  Key 0 is below every finite value and marks "no candidate".
@@ -89,27 +90,6 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
     if (l >= d) v += o;
   }
   return v;
-}
-
-// Tree of candidate lists for one query group: level 0 has n leaves (one per
-// key chunk); level l+1 has ceil(N_l / FANIN) nodes; the single top node is
-// the root.  "Lists" are stored for every non-root node; "counters" exist for
-// every node above level 0.
-__host__ __device__ inline int tree_lists(int n) {
-  int total = 0;
-  while (n > 1) {
-    total += n;
-    n = (n + FANIN - 1) / FANIN;
-  }
-  return total;
-}
-__host__ __device__ inline int tree_counters(int n) {
-  int total = 0;
-  while (n > 1) {
-    n = (n + FANIN - 1) / FANIN;
-    total += n;
-  }
-  return total;
 }
 
 }  // namespace dsa

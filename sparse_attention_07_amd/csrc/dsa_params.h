@@ -5,8 +5,11 @@
 
 namespace dsa {
 
-// Per-group record written by the planning kernel (int32 fields).
-enum GroupField { G_T0 = 0, G_NQ, G_SEQ, G_RANGE, G_NCH, G_ITEM, G_LIST, G_CTR, G_FIELDS };
+// Per-group record written by the planning kernel (int32 fields): first query,
+// query count, sequence, visible key range, offset of the group in the
+// concatenated (16-key padded) key space, number of indexer workgroups whose
+// slice overlaps the group, first candidate-list slot, first workgroup.
+enum GroupField { G_T0 = 0, G_NQ, G_SEQ, G_RANGE, G_OFF, G_NL, G_LIST, G_W0, G_FIELDS };
 
 struct IdxParams {
   const uint8_t* q_idx;   // [T][H_idx][D_idx] bf16 or e4m3fn codes
@@ -21,16 +24,17 @@ struct IdxParams {
   const int32_t* q_visible;  // may be null
   int32_t max_blocks;
   int32_t T, B, H_idx, K;
-  int32_t CH;  // keys per chunk, multiple of ROUND
-  int32_t MQ;  // max queries per group
+  int32_t nwg;  // indexer workgroups (each scans one equal slice of the key space)
+  int32_t MQ;   // max queries per group
   int32_t* indices;  // [T][K] output
   // workspace
-  int32_t* hdr;      // [0] groups, [1] items
-  int32_t* groups;   // [T][G_FIELDS]
-  uint32_t* ctr;     // merge-tree arrival counters
-  int32_t* list_cnt;
-  uint32_t* list_keys;
-  int32_t* list_pos;
+  int32_t* hdr;        // [0] groups, [1] padded keys in total, [2] keys per workgroup slice
+  int32_t* groups;     // [T][G_FIELDS]
+  int32_t* qgroup;     // [T] group of each query
+  int32_t* list_cnt;   // per (query, chunk) candidate list: entry count
+  uint32_t* list_min;  //   smallest key of the list
+  uint32_t* list_keys; //   [.][K] order keys, ascending position
+  int32_t* list_pos;   //   [.][K] logical positions
 };
 
 struct MlaParams {

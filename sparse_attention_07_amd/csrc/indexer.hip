@@ -8,26 +8,31 @@
 // then the min(K, n_t) largest S are kept (ties to the lower position).  The
 // paged index-K cache is read directly, the per-head dot products never leave
 // registers, and scores only live in LDS; what reaches memory are bounded
-// per-chunk candidate lists (<= K entries) that a merge tree reduces.
+// per-chunk candidate lists (<= K entries each).
 //
 // Design for CDNA4 (not the pages' accelerator):
 //  * a planning kernel turns (seq_lens, q_seq, q_visible) into query groups
 //    (adjacent queries of one sequence, up to MQ) and equal-size key chunks;
 //  * one persistent workgroup per CU walks chunks.  Each wave streams 16-key
 //    slices of 64-token pages straight into MFMA operand registers (per lane
-//    64 contiguous bytes per key per load pair), with a 4-deep register
-//    prefetch ring;
+//    64 contiguous bytes per key per load pair) with a 4-deep register prefetch
+//    ring; page ids come from an LDS copy of the chunk's block-table slice, so
+//    no load in the prefetch chain depends on another;
 //  * MFMA M = 16 indexer heads per tile, N = 16 keys, K = head dim
 //    (FP8: one 16x16x128 e4m3 MFMA per head tile; BF16: 16x16x32 steps);
-//    ReLU and the head-weighted reduction run on the accumulators, then a
-//    2-step permlane butterfly sums the four head groups;
-//  * selection streams: each 1024-key round's scores are filtered against the
-//    current K-th score into an LDS candidate buffer; when the buffer fills, a
-//    block-wide 8-bit radix select (ties broken by position through a 64-bit
-//    composite key) cuts it back to K.  Candidates stay in position order;
-//  * a chunk's K survivors go to the workspace; the last chunk of each group of
-//    8 to finish merges its siblings (arrival counter, no spinning), up to the
-//    root, which writes the final pool slots.
+//    ReLU (an integer max on the bit pattern) and the head-weighted reduction
+//    run on the accumulators, then a 2-step permlane butterfly sums the four
+//    head groups of the tile;
+//  * selection streams: each 1024-key round's scores are filtered against a
+//    lower bound of the current K-th score into an LDS candidate buffer; when
+//    the buffer fills, a block-wide 8-bit radix select (ties broken by position
+//    through a 64-bit composite key) cuts it back to K.  Candidates stay in
+//    position order throughout;
+//  * a query whose keys span several chunks gets one list per chunk; a merge
+//    kernel (after a kernel boundary, so no cross-workgroup fences) starts from
+//    the largest minimum key of any full list -- that list alone already holds
+//    K entries at or above it -- filters the lists' entries against it, and
+//    selects the final K.
 #include "dsa_device.h"
 #include "dsa_params.h"
 
@@ -100,119 +105,141 @@ __global__ __launch_bounds__(PLAN_NT) void dsa_plan_kernel(IdxParams p) {
     __syncthreads();
   }
   const int n_groups = carry_gid;
-  __threadfence_block();
-  __syncthreads();
-  // ---- pass 2 + 3: per-group sizes and exclusive prefix sums
-  int c_item = 0, c_list = 0, c_ctr = 0;
+  // ---- pass 2: per-group key ranges and their offsets in the concatenated
+  // key space (each group padded to whole 16-key groups, at least one)
+  int c_off = 0;
   for (int base = 0; base < n_groups; base += PLAN_NT) {
     const int g = base + tid;
-    int items = 0, lists = 0, ctrs = 0;
+    int wgt = 0;
     int* gr = p.groups + (int64_t)g * G_FIELDS;
     if (g < n_groups) {
       const int t0 = gr[G_T0];
       const int t1 = (g + 1 < n_groups) ? p.groups[(int64_t)(g + 1) * G_FIELDS + G_T0] : p.T;
-      const int nq = t1 - t0;
       int range = 0;
-      for (int t = t0; t < t1; ++t) range = max(range, plan_vis(p, t));
-      const int nch = max(1, (range + p.CH - 1) / p.CH);
-      gr[G_NQ] = nq;
+      for (int t = t0; t < t1; ++t) {
+        range = max(range, plan_vis(p, t));
+        p.qgroup[t] = g;
+      }
+      gr[G_NQ] = t1 - t0;
       gr[G_RANGE] = range;
-      gr[G_NCH] = nch;
-      items = nch;
-      lists = nq * tree_lists(nch);
-      ctrs = tree_counters(nch);
+      wgt = max(16, (range + 15) & ~15);
     }
-    const int si = block_scan_incl(items, s_w, false);
-    const int sl = block_scan_incl(lists, s_w, false);
-    const int sc = block_scan_incl(ctrs, s_w, false);
-    if (g < n_groups) {
-      gr[G_ITEM] = c_item + si - items;
-      gr[G_LIST] = c_list + sl - lists;
-      gr[G_CTR] = c_ctr + sc - ctrs;
-    }
-    if (tid == PLAN_NT - 1) {
-      s_carry[0] = c_item + si;
-      s_carry[1] = c_list + sl;
-      s_carry[2] = c_ctr + sc;
-    }
+    const int so = block_scan_incl(wgt, s_w, false);
+    if (g < n_groups) gr[G_OFF] = c_off + so - wgt;
+    if (tid == PLAN_NT - 1) s_carry[0] = c_off + so;
     __syncthreads();
-    c_item = s_carry[0];
-    c_list = s_carry[1];
-    c_ctr = s_carry[2];
+    c_off = s_carry[0];
     __syncthreads();
   }
-  for (int i = tid; i < c_ctr; i += PLAN_NT) p.ctr[i] = 0u;
+  const int total = c_off;
+  const int slice = max(MIN_SLICE, (((total + p.nwg - 1) / p.nwg) + 15) & ~15);
+  // ---- pass 3: workgroups overlapping each group; list slots of split groups
+  int c_list = 0;
+  for (int base = 0; base < n_groups; base += PLAN_NT) {
+    const int g = base + tid;
+    int lists = 0;
+    int* gr = p.groups + (int64_t)g * G_FIELDS;
+    if (g < n_groups) {
+      const int off = gr[G_OFF];
+      const int wgt = max(16, (gr[G_RANGE] + 15) & ~15);
+      const int w0 = off / slice, w1 = (off + wgt - 1) / slice;
+      gr[G_W0] = w0;
+      gr[G_NL] = w1 - w0 + 1;
+      lists = w1 > w0 ? gr[G_NQ] * (w1 - w0 + 1) : 0;
+    }
+    const int sl = block_scan_incl(lists, s_w, false);
+    if (g < n_groups) gr[G_LIST] = c_list + sl - lists;
+    if (tid == PLAN_NT - 1) s_carry[0] = c_list + sl;
+    __syncthreads();
+    c_list = s_carry[0];
+    __syncthreads();
+  }
   if (tid == 0) {
     p.hdr[0] = n_groups;
-    p.hdr[1] = c_item;
+    p.hdr[1] = total;
+    p.hdr[2] = slice;
   }
 }
 
 // =============================================================================
-// Main indexer kernel.
+// Block-wide selection primitives (shared by the indexer and the merge).
 // =============================================================================
-template <int MQ>
-struct CapOf {
-  static constexpr int value = MQ == 1 ? 8192 : (MQ == 2 ? 4096 : 3072);
-};
 
-template <int NW, int MQ>
-struct IdxSmem {
-  static constexpr int CAP = CapOf<MQ>::value;
-  static constexpr int NT = NW * 64;
-  static constexpr int SL = ROUND / NT;
-  uint32_t cand_key[MQ][CAP];
-  int32_t cand_pos[MQ][CAP];
-  uint32_t rb[2][MQ][ROUND];
-  uint32_t hist[256];
-  uint32_t wcnt[MQ][SL][NW];
-  int32_t cnt[MQ];
-  uint32_t thr[MQ];
-  int32_t sel[4];
-  int32_t flag;
-  int32_t grp[G_FIELDS];
-  int32_t pages[CH_MAX / PAGE];  // the chunk's block-table slice (-1 = invalid page)
-};
-
-// Block-wide Top-K of keys/pos[0..n) (n > K) by 8-bit radix select over the
-// 64-bit composite (key, ~pos); exactly K entries remain, in their original
-// (position) order, at [0..K).  Returns a lower bound of the smallest kept key
-// (a later, higher position with key <= bound can never enter the Top-K).
+// Top-K of keys/pos[0..n) (n > K) by radix select over the 64-bit composite
+// (key, ~pos); exactly K entries remain, in their original (position) order,
+// at [0..K).  The leading bits shared by every key (block min/max) are skipped,
+// so the first 8-bit digit already spreads clustered keys over the bins; each
+// wave counts into its own histogram (hist: NW*256 words).  Returns a lower
+// bound of the smallest kept key: an entry at a later position whose key is
+// <= the bound can never enter.
 template <int NW>
 __device__ uint32_t block_select(uint32_t* keys, int32_t* pos, int n, int K, uint32_t* hist, int32_t* sel,
                                  uint32_t* wtmp) {
   constexpr int NT = NW * 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t kpref = 0, ppref = 0;
+  // ---- common prefix of all keys
+  uint32_t mn = 0xffffffffu, mx = 0u;
+  for (int i = tid; i < n; i += NT) {
+    const uint32_t k = keys[i];
+    mn = min(mn, k);
+    mx = max(mx, k);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, d, 64));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, d, 64));
+  }
+  if (lane == 0) {
+    wtmp[wave] = mn;
+    wtmp[NW + wave] = mx;
+  }
+  lds_barrier();
+  mn = 0xffffffffu;
+  mx = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    mn = min(mn, wtmp[w]);
+    mx = max(mx, wtmp[NW + w]);
+  }
+  lds_barrier();
+  int kb = (mn == mx) ? 32 : __builtin_clz(mn ^ mx);  // key bits resolved
+  uint32_t kpref = kb >= 32 ? mn : (kb == 0 ? 0u : (mn & ~(0xffffffffu >> kb)));
+  int pb = 0;  // position bits resolved (of ~pos)
+  uint32_t ppref = 0;
   int need = K;
-  int d = 0;
-  for (; d < 8; ++d) {
-    for (int i = tid; i < 256; i += NT) hist[i] = 0u;
+  bool done = false;
+  while (!done && pb < 32) {
+    const bool onpos = kb >= 32;
+    const int rb = onpos ? pb : kb;
+    const int wd = min(8, 32 - rb);
+    const int shift = 32 - rb - wd;
+    for (int i = tid; i < NW * 256; i += NT) hist[i] = 0u;
     lds_barrier();
-    const bool onpos = d >= 4;
-    const int dd = onpos ? d - 4 : d;
-    const int shift = 24 - 8 * dd;
+    uint32_t* wh = hist + wave * 256;
     for (int i = tid; i < n; i += NT) {
       const uint32_t k = keys[i];
       const uint32_t pp = ~(uint32_t)pos[i];
       bool m;
       if (!onpos)
-        m = (dd == 0) || ((k >> (32 - 8 * dd)) == (kpref >> (32 - 8 * dd)));
+        m = (kb == 0) || ((k >> (32 - kb)) == (kpref >> (32 - kb)));
       else
-        m = (k == kpref) && ((dd == 0) || ((pp >> (32 - 8 * dd)) == (ppref >> (32 - 8 * dd))));
-      if (m) atomicAdd(&hist[((onpos ? pp : k) >> shift) & 255u], 1u);
+        m = (k == kpref) && ((pb == 0) || ((pp >> (32 - pb)) == (ppref >> (32 - pb))));
+      if (m) atomicAdd(&wh[((onpos ? pp : k) >> shift) & ((1u << wd) - 1u)], 1u);
     }
     lds_barrier();
     if (tid < 64) {
-      // lane L owns bins 255-4L .. 252-4L (descending)
-      uint32_t c[4], s = 0;
+      // lane L owns bins 255-4L .. 252-4L (descending), summed over the waves
+      uint32_t c[4], sum = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        c[j] = hist[255 - 4 * lane - j];
-        s += c[j];
+        uint32_t v = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) v += hist[w * 256 + 255 - 4 * lane - j];
+        c[j] = v;
+        sum += v;
       }
-      const uint32_t incl = wave_incl_scan(s);
-      const uint32_t excl = incl - s;
+      const uint32_t incl = wave_incl_scan(sum);
+      const uint32_t excl = incl - sum;
       if (excl < (uint32_t)need && (uint32_t)need <= incl) {
         uint32_t acc = excl;
 #pragma unroll
@@ -230,17 +257,17 @@ __device__ uint32_t block_select(uint32_t* keys, int32_t* pos, int n, int K, uin
     const int bin = sel[0], above = sel[1], cb = sel[2];
     lds_barrier();
     need -= above;
-    if (!onpos)
+    if (!onpos) {
       kpref |= (uint32_t)bin << shift;
-    else
+      kb += wd;
+    } else {
       ppref |= (uint32_t)bin << shift;
-    if (cb == need) break;
+      pb += wd;
+    }
+    done = (cb == need);
   }
-  if (d > 7) d = 7;
-  // ---- order-preserving compaction of the selected entries
-  const bool onpos = d >= 4;
-  const int kshift = onpos ? 0 : 24 - 8 * d;
-  const int pshift = onpos ? 24 - 8 * (d - 4) : 0;
+  // ---- order-preserving compaction of the selected entries: the resolved
+  // prefix of (key, ~pos) must be >= the threshold prefix
   int running = 0;
   for (int base = 0; base < n; base += NT) {
     const int i = base + tid;
@@ -250,10 +277,10 @@ __device__ uint32_t block_select(uint32_t* keys, int32_t* pos, int n, int K, uin
     if (i < n) {
       k = keys[i];
       ps = pos[i];
-      if (!onpos)
-        s = (k >> kshift) >= (kpref >> kshift);
+      if (kb < 32)
+        s = kb == 0 || (k >> (32 - kb)) >= (kpref >> (32 - kb));
       else
-        s = (k > kpref) || (k == kpref && ((~(uint32_t)ps) >> pshift) >= (ppref >> pshift));
+        s = (k > kpref) || (k == kpref && (pb == 0 || ((~(uint32_t)ps) >> (32 - pb)) >= (ppref >> (32 - pb))));
     }
     const uint64_t m = ballot(s);
     if (lane == 0) wtmp[wave] = (uint32_t)__builtin_popcountll(m);
@@ -273,8 +300,85 @@ __device__ uint32_t block_select(uint32_t* keys, int32_t* pos, int n, int K, uin
     running += tot;
     lds_barrier();
   }
-  return kpref;
+  return kb >= 32 ? kpref : (kb == 0 ? 0u : (kpref & ~(0xffffffffu >> kb)));
 }
+
+// Order-preserving append of the entries (kk[s], pp[s]) held by this thread
+// for slots s (entry index s*NT + tid) whose key exceeds thr, at keys/pos[base..].
+// Returns the new count (the same in every thread).  wcnt: SL*NW words of LDS.
+template <int NW, int SL>
+__device__ int block_append(uint32_t* keys, int32_t* pos, int base, uint32_t thr, const uint32_t (&kk)[SL],
+                            const int32_t (&pp)[SL], uint32_t* wcnt) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint64_t mk[SL];
+#pragma unroll
+  for (int s = 0; s < SL; ++s) {
+    mk[s] = ballot(kk[s] > thr);
+    if (lane == 0) wcnt[s * NW + wave] = (uint32_t)__builtin_popcountll(mk[s]);
+  }
+  lds_barrier();
+  int running = base;
+#pragma unroll
+  for (int s = 0; s < SL; ++s) {
+    int pre = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int c = (int)wcnt[s * NW + w];
+      pre += (w < wave) ? c : 0;
+      tot += c;
+    }
+    if (kk[s] > thr) {
+      const int o = running + pre + lanes_below(mk[s]);
+      keys[o] = kk[s];
+      pos[o] = pp[s];
+    }
+    running += tot;
+  }
+  lds_barrier();
+  return running;
+}
+
+// Smallest key of keys[0..n) (block-wide; n >= 1).
+template <int NW>
+__device__ uint32_t block_min(const uint32_t* keys, int n, uint32_t* red) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t m = 0xffffffffu;
+  for (int i = tid; i < n; i += NW * 64) m = min(m, keys[i]);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) m = min(m, (uint32_t)__shfl_xor((int)m, d, 64));
+  if (lane == 0) red[wave] = m;
+  lds_barrier();
+  uint32_t r = 0xffffffffu;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) r = min(r, red[w]);
+  lds_barrier();
+  return r;
+}
+
+// =============================================================================
+// Main indexer kernel.
+// =============================================================================
+template <int MQ>
+struct CapOf {
+  static constexpr int value = MQ == 1 ? 8192 : (MQ == 2 ? 4096 : 3072);
+};
+
+template <int NW, int MQ>
+struct IdxSmem {
+  static constexpr int CAP = CapOf<MQ>::value;
+  static constexpr int NT = NW * 64;
+  static constexpr int SL = ROUND / NT;
+  uint32_t cand_key[MQ][CAP];
+  int32_t cand_pos[MQ][CAP];
+  uint32_t rb[2][MQ][ROUND];
+  uint32_t hist[NW * 256];
+  uint32_t wcnt[SL * NW];
+  uint32_t red[2 * NW];
+  int32_t cnt[MQ];
+  uint32_t thr[MQ];
+  int32_t sel[4];
+  int32_t pages[SUB / PAGE + 1];  // the sub-chunk's block-table slice (-1 = invalid page); +1 when unaligned
+};
 
 template <int DT, int D>
 struct Frag {
@@ -297,7 +401,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
   constexpr int CAP = Sm::CAP;
   constexpr int SL = Sm::SL;
   constexpr int GPW = ROUND / 16 / NW;  // 16-key groups per wave per round
-  constexpr int PF = 4;                 // register prefetch depth (groups)
+  constexpr int PF = MQ == 1 ? 8 : 4;    // register prefetch depth (groups)
   constexpr int ES = DT == 0 ? 2 : 1;   // bytes per element
   constexpr int ROWB = D * ES;          // bytes per key row
   static_assert(GPW % PF == 0, "prefetch ring must divide the round");
@@ -312,47 +416,54 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
   const int g4 = lane >> 4;
   const int n16 = lane & 15;
 
-  const int n_items = p.hdr[1];
   const int n_groups = p.hdr[0];
+  const int total = p.hdr[1];
+  const int slice = p.hdr[2];
+  const int a0 = blockIdx.x * slice;
+  const int a1 = min(a0 + slice, total);
+  if (a0 >= a1) return;
 
-  for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
-    const int item = n_items - 1 - it;  // heaviest (last) groups first
-    // ---- locate the group of this item (binary search on item starts)
+  // first group overlapping [a0, a1): the last one whose offset is <= a0
+  int g = 0;
+  {
     int lo = 0, hi = n_groups - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (p.groups[(int64_t)mid * G_FIELDS + G_ITEM] <= item)
+      if (p.groups[(int64_t)mid * G_FIELDS + G_OFF] <= a0)
         lo = mid;
       else
         hi = mid - 1;
     }
-    const int* gr = p.groups + (int64_t)lo * G_FIELDS;
+    g = lo;
+  }
+
+  for (; g < n_groups; ++g) {
+    const int* gr = p.groups + (int64_t)g * G_FIELDS;
+    const int off = uniform(gr[G_OFF]);
+    if (off >= a1) break;
     const int t0 = uniform(gr[G_T0]);
     const int nq = uniform(gr[G_NQ]);
     const int seq = uniform(gr[G_SEQ]);
     const int range = uniform(gr[G_RANGE]);
-    const int nch = uniform(gr[G_NCH]);
-    const int chunk = item - uniform(gr[G_ITEM]);
+    const int nl = uniform(gr[G_NL]);
     const int list_base = uniform(gr[G_LIST]);
-    const int ctr_base = uniform(gr[G_CTR]);
-    const int kb = chunk * p.CH;
-    const int ke = min(kb + p.CH, range);
+    const int w0 = uniform(gr[G_W0]);
+    const int wgt = max(16, (range + 15) & ~15);
+    // this workgroup's keys of the group: [seg_lo, seg_hi), multiples of 16
+    const int seg_lo = max(a0, off) - off;
+    const int seg_hi = min(min(a1, off + wgt) - off, range);
     const int32_t* bt = p.block_table + (int64_t)max(seq, 0) * p.max_blocks;
 
-    int lim[MQ];
+    int vis[MQ];
 #pragma unroll
     for (int q = 0; q < MQ; ++q) {
       int v = 0;
-      if (q < nq) {
-        const int t = t0 + q;
-        const int b = seq;
-        if (b >= 0) {
-          const int L = min(max(p.seq_lens[b], 0), p.max_blocks * PAGE);
-          v = p.q_visible ? p.q_visible[t] : L;
-          v = min(max(v, 0), L);
-        }
+      if (q < nq && seq >= 0) {
+        const int L = min(max(p.seq_lens[seq], 0), p.max_blocks * PAGE);
+        v = p.q_visible ? p.q_visible[t0 + q] : L;
+        v = min(max(v, 0), L);
       }
-      lim[q] = uniform(min(v, ke));
+      vis[q] = uniform(v);
     }
 
     // ---- query operands and weights (identical in every wave)
@@ -367,8 +478,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
         const uint8_t* row = p.q_idx + ((int64_t)(t0 + q) * p.H_idx + h) * ROWB;
 #pragma unroll
         for (int j = 0; j < Frag<DT, D>::NP; ++j) {
-          const int off = DT == 0 ? 2 * (32 * j + 8 * g4) : (64 * j + 16 * g4);
-          a[q][mt].d[j] = okh ? *reinterpret_cast<const v4i*>(row + off) : v4i{0, 0, 0, 0};
+          const int off_b = DT == 0 ? 2 * (32 * j + 8 * g4) : (64 * j + 16 * g4);
+          a[q][mt].d[j] = okh ? *reinterpret_cast<const v4i*>(row + off_b) : v4i{0, 0, 0, 0};
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -388,132 +499,87 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
       sm.cnt[tid] = 0;
       sm.thr[tid] = 0u;
     }
-    for (int i = tid; i < (ke - kb + PAGE - 1) / PAGE; i += NT) {
-      const int pg = bt[(kb >> 6) + i];
-      sm.pages[i] = (pg >= 0 && (int64_t)pg < p.num_blocks) ? pg : -1;
-    }
-    lds_barrier();
 
-    // ---- streaming rounds
-    const int nkeys = max(ke - kb, 0);
-    const int nrounds = (nkeys + ROUND - 1) / ROUND;
-    const int total_j = nrounds * GPW;
-    auto group_p0 = [&](int j) { return kb + (j / GPW) * ROUND + (wave * GPW + (j % GPW)) * 16; };
-
-    auto load_b = [&](BFrag<DT, D>& bf, int p0) {
-      int page = sm.pages[(p0 - kb) >> 6];
-      const bool ok = page >= 0;
-      page = ok ? page : 0;
-      const int r = (p0 & 63) + n16;
-      const uint8_t* pg = p.k_pool + (int64_t)page * p.page_bytes;
-      const uint8_t* rowp = pg + r * ROWB;
-#pragma unroll
-      for (int j = 0; j < Frag<DT, D>::NP; ++j) {
-        const int off = DT == 0 ? 2 * (32 * j + 8 * g4) : (64 * j + 16 * g4);
-        bf.f.d[j] = *reinterpret_cast<const v4i*>(rowp + off);
+    // ---- stream the segment in sub-chunks (page ids of a sub-chunk staged in LDS)
+    for (int kb = seg_lo; kb < seg_hi; kb += SUB) {
+      const int ke = min(kb + SUB, seg_hi);
+      const int pg0 = kb >> 6;
+      for (int i = tid; i <= ((ke - 1) >> 6) - pg0; i += NT) {
+        const int pg = bt[pg0 + i];
+        sm.pages[i] = (pg >= 0 && (int64_t)pg < p.num_blocks) ? pg : -1;
       }
-      bf.sc = DT == 1 ? *reinterpret_cast<const float*>(pg + PAGE * ROWB + 4 * r) : 1.f;
-      bf.ok = ok;
-    };
+      lds_barrier();
+      int lim[MQ];
+#pragma unroll
+      for (int q = 0; q < MQ; ++q) lim[q] = min(vis[q], ke);
 
-    auto score_group = [&](const BFrag<DT, D>& bf, int p0, int rs, int rbuf) {
+      const int nkeys = ke - kb;
+      const int nrounds = (nkeys + ROUND - 1) / ROUND;
+      auto group_p0 = [&](int j) { return kb + (j / GPW) * ROUND + (wave * GPW + (j % GPW)) * 16; };
+
+      auto load_b = [&](BFrag<DT, D>& bf, int p0) {
+        int page = sm.pages[(p0 >> 6) - pg0];
+        const bool ok = page >= 0;
+        page = ok ? page : 0;
+        const int r = (p0 & 63) + n16;
+        const uint8_t* pgp = p.k_pool + (int64_t)page * p.page_bytes;
+        const uint8_t* rowp = pgp + r * ROWB;
 #pragma unroll
-      for (int q = 0; q < MQ; ++q) {
-        if (q < nq) {
-          // all head tiles' MFMAs first (independent accumulators), then the VALU
-          v4f acc[HT];
+        for (int j = 0; j < Frag<DT, D>::NP; ++j) {
+          const int off_b = DT == 0 ? 2 * (32 * j + 8 * g4) : (64 * j + 16 * g4);
+          bf.f.d[j] = *reinterpret_cast<const v4i*>(rowp + off_b);
+        }
+        bf.sc = DT == 1 ? *reinterpret_cast<const float*>(pgp + PAGE * ROWB + 4 * r) : 1.f;
+        bf.ok = ok;
+      };
+
+      auto score_group = [&](const BFrag<DT, D>& bf, int p0, int rs, int rbuf) {
 #pragma unroll
-          for (int mt = 0; mt < HT; ++mt) {
-            acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
-            if constexpr (DT == 1) {
-              const v8i av = __builtin_shufflevector(a[q][mt].d[0], a[q][mt].d[1], 0, 1, 2, 3, 4, 5, 6, 7);
-              const v8i bv = __builtin_shufflevector(bf.f.d[0], bf.f.d[1], 0, 1, 2, 3, 4, 5, 6, 7);
-              acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[mt], 0, 0, 0, 0, 0, 0);
-            } else {
+        for (int q = 0; q < MQ; ++q) {
+          if (q < nq) {
+            // all head tiles' MFMAs first (independent accumulators), then the VALU
+            v4f acc[HT];
 #pragma unroll
-              for (int j = 0; j < Frag<DT, D>::NP; ++j)
-                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[q][mt].d[j]),
-                                                                  __builtin_bit_cast(v8bf, bf.f.d[j]), acc[mt], 0, 0, 0);
+            for (int mt = 0; mt < HT; ++mt) {
+              acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+              if constexpr (DT == 1) {
+                const v8i av = __builtin_shufflevector(a[q][mt].d[0], a[q][mt].d[1], 0, 1, 2, 3, 4, 5, 6, 7);
+                const v8i bv = __builtin_shufflevector(bf.f.d[0], bf.f.d[1], 0, 1, 2, 3, 4, 5, 6, 7);
+                acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[mt], 0, 0, 0, 0, 0, 0);
+              } else {
+#pragma unroll
+                for (int j = 0; j < Frag<DT, D>::NP; ++j)
+                  acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[q][mt].d[j]),
+                                                                    __builtin_bit_cast(v8bf, bf.f.d[j]), acc[mt], 0,
+                                                                    0, 0);
+              }
             }
+            float part = 0.f;
+#pragma unroll
+            for (int mt = 0; mt < HT; ++mt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                // ReLU as an integer max on the bit pattern: negative floats
+                // (sign bit set) become +0, everything else is unchanged
+                const float d = __int_as_float(max(__float_as_int(acc[mt][i]), 0));
+                part = fmaf(wv[q][mt][i], d, part);
+              }
+            float sc = sum_lane_groups(part);
+            if (DT == 1) sc *= bf.sc;
+            const int pp = p0 + n16;
+            const bool valid = bf.ok && pp < lim[q];
+            if (lane < 16) sm.rb[rbuf][q][pp - rs] = valid ? order_key(sc) : 0u;
           }
-          float part = 0.f;
-#pragma unroll
-          for (int mt = 0; mt < HT; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              // ReLU as an integer max on the bit pattern: negative floats
-              // (sign bit set) become +0, everything else is unchanged
-              const float d = __int_as_float(max(__float_as_int(acc[mt][i]), 0));
-              part = fmaf(wv[q][mt][i], d, part);
-            }
-          float s = sum_lane_groups(part);
-          if (DT == 1) s *= bf.sc;
-          const int pp = p0 + n16;
-          const bool valid = bf.ok && pp < lim[q];
-          if (lane < 16) sm.rb[rbuf][q][pp - rs] = valid ? order_key(s) : 0u;
         }
-      }
-    };
+      };
 
-    // streaming filter of one batch of up to ROUND (key, pos) pairs into the
-    // candidate buffers, keeping position order
-    auto filter_append = [&](int q, int n, auto get) {
-      const uint32_t thr = sm.thr[q];
-      const int base = sm.cnt[q];
-      uint32_t kk[SL];
-      int32_t pp[SL];
-      uint64_t mk[SL];
-#pragma unroll
-      for (int s = 0; s < SL; ++s) {
-        const int i = s * NT + tid;
-        kk[s] = 0u;
-        pp[s] = 0;
-        if (i < n) get(i, kk[s], pp[s]);
-        mk[s] = ballot(kk[s] > thr);
-        if (lane == 0) sm.wcnt[q][s][wave] = (uint32_t)__builtin_popcountll(mk[s]);
-      }
-      lds_barrier();
-      int running = base;
-#pragma unroll
-      for (int s = 0; s < SL; ++s) {
-        int pre = 0, tot = 0;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-          const int c = (int)sm.wcnt[q][s][w];
-          pre += (w < wave) ? c : 0;
-          tot += c;
-        }
-        if (kk[s] > thr) {
-          const int o = running + pre + lanes_below(mk[s]);
-          sm.cand_key[q][o] = kk[s];
-          sm.cand_pos[q][o] = pp[s];
-        }
-        running += tot;
-      }
-      lds_barrier();
-      if (tid == 0) sm.cnt[q] = running;
-      lds_barrier();
-      if (running > CAP - ROUND) {
-        const uint32_t t = block_select<NW>(sm.cand_key[q], sm.cand_pos[q], running, p.K, sm.hist, sm.sel,
-                                            &sm.wcnt[0][0][0]);
-        if (tid == 0) {
-          sm.cnt[q] = p.K;
-          sm.thr[q] = t;
-        }
-        lds_barrier();
-      }
-    };
-
-    {
       // Loads are unconditional so the prefetch queue depth stays static: slots
-      // past the chunk end re-read the chunk's last 16-key group (a cache hit).
-      const int last_p0 = kb + ((max(nkeys, 1) - 1) & ~15);
+      // past the sub-chunk end re-read its last 16-key group (a cache hit).
+      const int last_p0 = kb + ((nkeys - 1) & ~15);
       auto load_p0 = [&](int j) { return min(group_p0(j), last_p0); };
       BFrag<DT, D> buf[PF];
-      if (nkeys > 0) {
 #pragma unroll
-        for (int s = 0; s < PF; ++s) load_b(buf[s], load_p0(s));
-      }
+      for (int s = 0; s < PF; ++s) load_b(buf[s], load_p0(s));
       for (int r = 0; r < nrounds; ++r) {
         const int rs = kb + r * ROUND;
         const int rbuf = r & 1;
@@ -527,34 +593,43 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
         lds_barrier();
         const int nr = min(ROUND, ke - rs);
 #pragma unroll
-        for (int q = 0; q < MQ; ++q)
-          if (q < nq)
-            filter_append(q, nr, [&](int i, uint32_t& k, int32_t& ps) {
-              k = sm.rb[rbuf][q][i];
-              ps = rs + i;
-            });
-      }
-    }
-
-    auto finish_select = [&]() {
+        for (int q = 0; q < MQ; ++q) {
+          if (q < nq) {
+            uint32_t kk[SL];
+            int32_t pp[SL];
 #pragma unroll
-      for (int q = 0; q < MQ; ++q) {
-        if (q < nq) {
-          const int c = sm.cnt[q];
-          if (c > p.K) {
-            block_select<NW>(sm.cand_key[q], sm.cand_pos[q], c, p.K, sm.hist, sm.sel, &sm.wcnt[0][0][0]);
-            lds_barrier();
-            if (tid == 0) sm.cnt[q] = p.K;
+            for (int s = 0; s < SL; ++s) {
+              const int i = s * NT + tid;
+              kk[s] = i < nr ? sm.rb[rbuf][q][i] : 0u;
+              pp[s] = rs + i;
+            }
+            const int c = block_append<NW, SL>(sm.cand_key[q], sm.cand_pos[q], sm.cnt[q], sm.thr[q], kk, pp,
+                                               sm.wcnt);
+            if (c > CAP - ROUND) {
+              const uint32_t t = block_select<NW>(sm.cand_key[q], sm.cand_pos[q], c, p.K, sm.hist, sm.sel, sm.red);
+              if (tid == 0) {
+                sm.cnt[q] = p.K;
+                sm.thr[q] = t;
+              }
+            } else if (tid == 0) {
+              sm.cnt[q] = c;
+            }
             lds_barrier();
           }
         }
       }
-    };
-    auto write_final = [&]() {
+    }
+
+    // ---- final selection and output
 #pragma unroll
-      for (int q = 0; q < MQ; ++q) {
-        if (q < nq) {
-          const int c = sm.cnt[q];
+    for (int q = 0; q < MQ; ++q) {
+      if (q < nq) {
+        int c = sm.cnt[q];
+        if (c > p.K) {
+          block_select<NW>(sm.cand_key[q], sm.cand_pos[q], c, p.K, sm.hist, sm.sel, sm.red);
+          c = p.K;
+        }
+        if (nl == 1) {
           int32_t* out = p.indices + (int64_t)(t0 + q) * p.K;
           for (int i = tid; i < p.K; i += NT) {
             int v = -1;
@@ -564,81 +639,125 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
             }
             out[i] = v;
           }
-        }
-      }
-    };
-
-    finish_select();
-    if (nch == 1) {
-      write_final();
-      lds_barrier();
-      continue;
-    }
-
-    // ---- merge tree over the group's chunks (last arrival merges)
-    const int U = tree_lists(nch);
-    int idx = chunk, n_level = nch, off_list = 0, off_ctr = 0;
-    while (true) {
-      // store this node's lists
-#pragma unroll
-      for (int q = 0; q < MQ; ++q) {
-        if (q < nq) {
-          const int64_t unit = (int64_t)list_base + (int64_t)q * U + off_list + idx;
-          const int c = sm.cnt[q];
+        } else {
+          const int64_t unit = (int64_t)list_base + (int64_t)q * nl + (blockIdx.x - w0);
           for (int i = tid; i < c; i += NT) {
             p.list_keys[unit * p.K + i] = sm.cand_key[q][i];
             p.list_pos[unit * p.K + i] = sm.cand_pos[q][i];
           }
-          if (tid == 0) p.list_cnt[unit] = c;
-        }
-      }
-      __threadfence();
-      __syncthreads();
-      const int parent = idx / FANIN;
-      const int n_parent = (n_level + FANIN - 1) / FANIN;
-      const int nchild = min(FANIN, n_level - parent * FANIN);
-      if (tid == 0) {
-        const uint32_t old = atomicAdd(&p.ctr[ctr_base + off_ctr + parent], 1u);
-        sm.flag = (old == (uint32_t)(nchild - 1)) ? 1 : 0;
-      }
-      __syncthreads();
-      if (!sm.flag) break;
-      __threadfence();
-      // merge the children of `parent`
-      if (tid < MQ) {
-        sm.cnt[tid] = 0;
-        sm.thr[tid] = 0u;
-      }
-      __syncthreads();
-      for (int ch = 0; ch < nchild; ++ch) {
-        const int cidx = parent * FANIN + ch;
-#pragma unroll
-        for (int q = 0; q < MQ; ++q) {
-          if (q < nq) {
-            const int64_t unit = (int64_t)list_base + (int64_t)q * U + off_list + cidx;
-            const int n_c = __hip_atomic_load(&p.list_cnt[unit], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const uint32_t* lk = p.list_keys + unit * p.K;
-            const int32_t* lp = p.list_pos + unit * p.K;
-            for (int s0 = 0; s0 < n_c; s0 += ROUND) {
-              filter_append(q, min(ROUND, n_c - s0), [&](int i, uint32_t& k, int32_t& ps) {
-                k = lk[s0 + i];
-                ps = lp[s0 + i];
-              });
-            }
+          const uint32_t mn = c > 0 ? block_min<NW>(sm.cand_key[q], c, sm.red) : 0u;
+          if (tid == 0) {
+            p.list_cnt[unit] = c;
+            p.list_min[unit] = mn;
           }
         }
-      }
-      finish_select();
-      off_list += n_level;
-      off_ctr += n_parent;
-      idx = parent;
-      n_level = n_parent;
-      if (n_level == 1) {
-        write_final();
-        break;
+        lds_barrier();
       }
     }
-    __syncthreads();
+  }
+}
+
+// =============================================================================
+// Merge kernel: one workgroup per query whose keys span several chunks.
+// =============================================================================
+constexpr int MRG_NW = 8;
+constexpr int MRG_NT = MRG_NW * 64;
+constexpr int MRG_SL = 8;                       // entries per thread per batch
+constexpr int MRG_BATCH = MRG_SL * MRG_NT;      // 4096
+constexpr int MRG_CAP = 16384;
+
+struct MergeSmem {
+  uint32_t cand_key[MRG_CAP];
+  int32_t cand_pos[MRG_CAP];
+  uint32_t hist[MRG_NW * 256];
+  uint32_t wcnt[MRG_SL * MRG_NW];
+  uint32_t red[2 * MRG_NW];
+  int32_t sel[4];
+  int32_t lcnt[MRG_MAX_LISTS];
+};
+
+__global__ __launch_bounds__(MRG_NT, 1) void dsa_merge_kernel(IdxParams p) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  MergeSmem& sm = *reinterpret_cast<MergeSmem*>(smem_raw);
+  const int tid = threadIdx.x;
+  const int t = blockIdx.x;
+  if (t >= p.T) return;
+  const int g = p.qgroup[t];
+  const int* gr = p.groups + (int64_t)g * G_FIELDS;
+  const int nch = gr[G_NL];  // lists of this query (one per overlapping indexer workgroup)
+  if (nch <= 1) return;
+  const int q = t - gr[G_T0];
+  const int seq = gr[G_SEQ];
+  const int64_t unit0 = (int64_t)gr[G_LIST] + (int64_t)q * nch;
+  const int K = p.K;
+
+  // list sizes to LDS; lower bound of the final K-th key: the largest minimum
+  // over full lists
+  uint32_t lb = 0;
+  for (int c = tid; c < nch; c += MRG_NT) {
+    const int n_c = p.list_cnt[unit0 + c];
+    sm.lcnt[c] = n_c;
+    if (n_c == K) lb = max(lb, p.list_min[unit0 + c]);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) lb = max(lb, (uint32_t)__shfl_xor((int)lb, d, 64));
+  if ((tid & 63) == 0) sm.red[tid >> 6] = lb;
+  lds_barrier();
+  lb = 0;
+#pragma unroll
+  for (int w = 0; w < MRG_NW; ++w) lb = max(lb, sm.red[w]);
+  lds_barrier();
+  // keep keys >= lb (an equal key can still win on position); key 0 = no entry
+  uint32_t thr = lb > 0 ? lb - 1 : 0;
+
+  // entries in list order (= position order), batch by batch with one batch prefetched
+  const int total = nch * K;  // <= 1024 chunks x 2048
+  auto load = [&](int b0, uint32_t (&kk)[MRG_SL], int32_t (&pp)[MRG_SL]) {
+#pragma unroll
+    for (int s = 0; s < MRG_SL; ++s) {
+      const int e = b0 + s * MRG_NT + tid;
+      kk[s] = 0u;
+      pp[s] = 0;
+      if (e < total) {
+        const int c = e / K, i = e - c * K;
+        if (i < sm.lcnt[c]) {
+          kk[s] = p.list_keys[(unit0 + c) * K + i];
+          pp[s] = p.list_pos[(unit0 + c) * K + i];
+        }
+      }
+    }
+  };
+  uint32_t ka[MRG_SL], kb2[MRG_SL];
+  int32_t pa[MRG_SL], pb2[MRG_SL];
+  load(0, ka, pa);
+  int cnt = 0;
+  for (int b0 = 0; b0 < total; b0 += 2 * MRG_BATCH) {
+    load(b0 + MRG_BATCH, kb2, pb2);
+    cnt = block_append<MRG_NW, MRG_SL>(sm.cand_key, sm.cand_pos, cnt, thr, ka, pa, sm.wcnt);
+    if (cnt > MRG_CAP - MRG_BATCH) {
+      thr = max(thr, block_select<MRG_NW>(sm.cand_key, sm.cand_pos, cnt, K, sm.hist, sm.sel, sm.red));
+      cnt = K;
+    }
+    load(b0 + 2 * MRG_BATCH, ka, pa);
+    cnt = block_append<MRG_NW, MRG_SL>(sm.cand_key, sm.cand_pos, cnt, thr, kb2, pb2, sm.wcnt);
+    if (cnt > MRG_CAP - MRG_BATCH) {
+      thr = max(thr, block_select<MRG_NW>(sm.cand_key, sm.cand_pos, cnt, K, sm.hist, sm.sel, sm.red));
+      cnt = K;
+    }
+  }
+  if (cnt > K) {
+    block_select<MRG_NW>(sm.cand_key, sm.cand_pos, cnt, K, sm.hist, sm.sel, sm.red);
+    cnt = K;
+  }
+  const int32_t* bt = p.block_table + (int64_t)max(seq, 0) * p.max_blocks;
+  int32_t* out = p.indices + (int64_t)t * K;
+  for (int i = tid; i < K; i += MRG_NT) {
+    int v = -1;
+    if (i < cnt) {
+      const int ps = sm.cand_pos[i];
+      v = bt[ps >> 6] * PAGE + (ps & 63);
+    }
+    out[i] = v;
   }
 }
 
@@ -664,22 +783,23 @@ static hipError_t launch_indexer_mq(const IdxParams& p, int grid, hipStream_t st
   }
 }
 
-hipError_t launch_indexer(const IdxParams& p, int is_fp8, int D, int grid, hipStream_t st) {
+hipError_t launch_indexer(const IdxParams& p, int is_fp8, int D, int grid, bool need_merge, hipStream_t st) {
   hipLaunchKernelGGL(dsa_plan_kernel, dim3(1), dim3(PLAN_NT), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const bool small_heads = p.H_idx <= 16;
-  if (is_fp8) return small_heads ? launch_indexer_mq<1, 128, 1>(p, grid, st) : launch_indexer_mq<1, 128, 4>(p, grid, st);
-  if (D == 64) return small_heads ? launch_indexer_mq<0, 64, 1>(p, grid, st) : launch_indexer_mq<0, 64, 4>(p, grid, st);
-  return small_heads ? launch_indexer_mq<0, 128, 1>(p, grid, st) : launch_indexer_mq<0, 128, 4>(p, grid, st);
-}
-
-size_t indexer_smem_bytes(int MQ) {
-  switch (MQ) {
-    case 1: return sizeof(IdxSmem<8, 1>);
-    case 2: return sizeof(IdxSmem<8, 2>);
-    default: return sizeof(IdxSmem<4, 4>);
-  }
+  if (is_fp8)
+    e = small_heads ? launch_indexer_mq<1, 128, 1>(p, grid, st) : launch_indexer_mq<1, 128, 4>(p, grid, st);
+  else if (D == 64)
+    e = small_heads ? launch_indexer_mq<0, 64, 1>(p, grid, st) : launch_indexer_mq<0, 64, 4>(p, grid, st);
+  else
+    e = small_heads ? launch_indexer_mq<0, 128, 1>(p, grid, st) : launch_indexer_mq<0, 128, 4>(p, grid, st);
+  if (e != hipSuccess || !need_merge) return e;
+  const size_t smem = sizeof(MergeSmem);
+  e = hipFuncSetAttribute((const void*)dsa_merge_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(dsa_merge_kernel, dim3(p.T), dim3(MRG_NT), smem, st, p);
+  return hipGetLastError();
 }
 
 }  // namespace dsa

@@ -93,3 +93,23 @@ def test_full_prefill_16k_last_chunk():
 
 def test_full_mixed_1m():
     run_case(synth.PRESETS["mixed_1m"], queries=[0, 3, 7, 10])
+
+
+def test_all_scores_tied_picks_lowest_positions():
+    # zero indexer queries: every score is exactly 0, so Top-K is decided by
+    # position alone (lowest positions win), across chunks and the merge
+    sp = spec("all_tied", lens=[30000, 2500, 40], seed=23)
+    case = synth.build_case(sp, device=DEV)
+    case.q_idx.zero_()
+    layer = dsa.layer_from_case(case)
+    layer()
+    torch.cuda.synchronize()
+    check_queries(case, layer.indices, layer.out, range(case.T))
+    bt = case.block_table.cpu()
+    idx = layer.indices.cpu()
+    for t, L in enumerate(case.seq_lens.tolist()):
+        k = min(sp.K, L)
+        pos = torch.arange(k)
+        expect = (bt[t, pos // 64] * 64 + pos % 64).to(torch.int32)
+        assert torch.equal(idx[t, :k], expect)
+        assert (idx[t, k:] == -1).all()
