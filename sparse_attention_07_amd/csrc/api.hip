@@ -97,7 +97,7 @@ IdxPlan plan_indexer(const dsa_indexer_args* a, int K, size_t base, int nwg) {
   pl.off_lcnt = off;
   off = align_up(off + (size_t)pl.lists * 4, 256);
   pl.off_lmin = off;
-  off = align_up(off + (size_t)pl.lists * 4, 256);
+  off = align_up(off + (size_t)pl.lists * 8, 256);
   pl.off_lkeys = off;
   off = align_up(off + (size_t)pl.lists * K * 4, 256);
   pl.off_lpos = off;
@@ -151,7 +151,7 @@ IdxParams make_idx_params(const dsa_indexer_args* a, int K, int32_t* indices, un
   p.groups = (int32_t*)(ws + pl.off_groups);
   p.qgroup = (int32_t*)(ws + pl.off_qgroup);
   p.list_cnt = (int32_t*)(ws + pl.off_lcnt);
-  p.list_min = (uint32_t*)(ws + pl.off_lmin);
+  p.list_mm = (uint32_t*)(ws + pl.off_lmin);
   p.list_keys = (uint32_t*)(ws + pl.off_lkeys);
   p.list_pos = (int32_t*)(ws + pl.off_lpos);
   return p;

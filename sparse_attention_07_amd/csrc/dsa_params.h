@@ -32,7 +32,7 @@ struct IdxParams {
   int32_t* groups;     // [T][G_FIELDS]
   int32_t* qgroup;     // [T] group of each query
   int32_t* list_cnt;   // per (query, chunk) candidate list: entry count
-  uint32_t* list_min;  //   smallest key of the list
+  uint32_t* list_mm;   //   [.][2] smallest and largest key of the list
   uint32_t* list_keys; //   [.][K] order keys, ascending position
   int32_t* list_pos;   //   [.][K] logical positions
 };

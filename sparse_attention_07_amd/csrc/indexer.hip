@@ -305,10 +305,12 @@ __device__ uint32_t block_select(uint32_t* keys, int32_t* pos, int n, int K, uin
 
 // Order-preserving append of the entries (kk[s], pp[s]) held by this thread
 // for slots s (entry index s*NT + tid) whose key exceeds thr, at keys/pos[base..].
-// Returns the new count (the same in every thread).  wcnt: SL*NW words of LDS.
+// Returns the new count (the same in every thread).  wcnt: 2*SL*NW + 1 words of
+// LDS (counts per (slot, wave), then their exclusive scan and the total).
 template <int NW, int SL>
 __device__ int block_append(uint32_t* keys, int32_t* pos, int base, uint32_t thr, const uint32_t (&kk)[SL],
                             const int32_t (&pp)[SL], uint32_t* wcnt) {
+  static_assert(SL * NW <= 64, "one wave scans the (slot, wave) counts");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint64_t mk[SL];
 #pragma unroll
@@ -317,42 +319,55 @@ __device__ int block_append(uint32_t* keys, int32_t* pos, int base, uint32_t thr
     if (lane == 0) wcnt[s * NW + wave] = (uint32_t)__builtin_popcountll(mk[s]);
   }
   lds_barrier();
-  int running = base;
+  if (wave == 0) {
+    const uint32_t c = lane < SL * NW ? wcnt[lane] : 0u;
+    const uint32_t incl = wave_incl_scan(c);
+    if (lane < SL * NW) wcnt[SL * NW + lane] = incl - c;
+    if (lane == 63) wcnt[2 * SL * NW] = incl;
+  }
+  lds_barrier();
 #pragma unroll
   for (int s = 0; s < SL; ++s) {
-    int pre = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const int c = (int)wcnt[s * NW + w];
-      pre += (w < wave) ? c : 0;
-      tot += c;
-    }
     if (kk[s] > thr) {
-      const int o = running + pre + lanes_below(mk[s]);
+      const int o = base + (int)wcnt[SL * NW + s * NW + wave] + lanes_below(mk[s]);
       keys[o] = kk[s];
       pos[o] = pp[s];
     }
-    running += tot;
   }
+  const int total = base + (int)wcnt[2 * SL * NW];
   lds_barrier();
-  return running;
+  return total;
 }
 
-// Smallest key of keys[0..n) (block-wide; n >= 1).
+// Smallest and largest key of keys[0..n) (block-wide; n >= 1).
 template <int NW>
-__device__ uint32_t block_min(const uint32_t* keys, int n, uint32_t* red) {
+__device__ void block_minmax(const uint32_t* keys, int n, uint32_t* red, uint32_t& mn_out, uint32_t& mx_out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t m = 0xffffffffu;
-  for (int i = tid; i < n; i += NW * 64) m = min(m, keys[i]);
+  uint32_t mn = 0xffffffffu, mx = 0u;
+  for (int i = tid; i < n; i += NW * 64) {
+    mn = min(mn, keys[i]);
+    mx = max(mx, keys[i]);
+  }
 #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) m = min(m, (uint32_t)__shfl_xor((int)m, d, 64));
-  if (lane == 0) red[wave] = m;
+  for (int d = 32; d >= 1; d >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, d, 64));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, d, 64));
+  }
+  if (lane == 0) {
+    red[wave] = mn;
+    red[NW + wave] = mx;
+  }
   lds_barrier();
-  uint32_t r = 0xffffffffu;
+  mn = 0xffffffffu;
+  mx = 0u;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) r = min(r, red[w]);
+  for (int w = 0; w < NW; ++w) {
+    mn = min(mn, red[w]);
+    mx = max(mx, red[NW + w]);
+  }
   lds_barrier();
-  return r;
+  mn_out = mn;
+  mx_out = mx;
 }
 
 // =============================================================================
@@ -372,7 +387,7 @@ struct IdxSmem {
   int32_t cand_pos[MQ][CAP];
   uint32_t rb[2][MQ][ROUND];
   uint32_t hist[NW * 256];
-  uint32_t wcnt[SL * NW];
+  uint32_t wcnt[2 * SL * NW + 1];
   uint32_t red[2 * NW];
   int32_t cnt[MQ];
   uint32_t thr[MQ];
@@ -645,10 +660,12 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
             p.list_keys[unit * p.K + i] = sm.cand_key[q][i];
             p.list_pos[unit * p.K + i] = sm.cand_pos[q][i];
           }
-          const uint32_t mn = c > 0 ? block_min<NW>(sm.cand_key[q], c, sm.red) : 0u;
+          uint32_t mn = 0u, mx = 0u;
+          if (c > 0) block_minmax<NW>(sm.cand_key[q], c, sm.red, mn, mx);
           if (tid == 0) {
             p.list_cnt[unit] = c;
-            p.list_min[unit] = mn;
+            p.list_mm[2 * unit] = mn;
+            p.list_mm[2 * unit + 1] = mx;
           }
         }
         lds_barrier();
@@ -658,91 +675,294 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
 }
 
 // =============================================================================
-// Merge kernel: one workgroup per query whose keys span several chunks.
+// Merge kernel: one workgroup per query whose keys span several slices.
+//
+// Every full list (K entries) is itself the Top-K of its slice, so the largest
+// list minimum lb bounds the final K-th key from below, and keys below lb are
+// out.  Pass A histograms the 11 bits that follow the common prefix of
+// [lb, max key] over all list entries in global memory and finds the bin that
+// holds the K-th key; pass B appends (in position order) only the entries at
+// or above that bin; a small LDS select then finishes.  If that bin is too
+// heavy for LDS (e.g. exact ties), the lists are streamed through the
+// filter-and-select loop instead.
 // =============================================================================
 constexpr int MRG_NW = 8;
 constexpr int MRG_NT = MRG_NW * 64;
 constexpr int MRG_SL = 8;                       // entries per thread per batch
+constexpr int MRG_RS = 32;                      // entries per thread when a query's lists fit in registers
 constexpr int MRG_BATCH = MRG_SL * MRG_NT;      // 4096
 constexpr int MRG_CAP = 16384;
+constexpr int MRG_BITS = 11;
 
 struct MergeSmem {
   uint32_t cand_key[MRG_CAP];
   int32_t cand_pos[MRG_CAP];
-  uint32_t hist[MRG_NW * 256];
-  uint32_t wcnt[MRG_SL * MRG_NW];
+  uint32_t hist[MRG_NW * 256];  // also the 2^MRG_BITS-bin histogram of pass A
+  uint32_t wcnt[2 * MRG_SL * MRG_NW + 1];
   uint32_t red[2 * MRG_NW];
   int32_t sel[4];
   int32_t lcnt[MRG_MAX_LISTS];
 };
+static_assert(MRG_NW * 256 >= (1 << MRG_BITS), "pass-A histogram fits the radix histogram space");
 
 __global__ __launch_bounds__(MRG_NT, 1) void dsa_merge_kernel(IdxParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   MergeSmem& sm = *reinterpret_cast<MergeSmem*>(smem_raw);
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = blockIdx.x;
   if (t >= p.T) return;
   const int g = p.qgroup[t];
   const int* gr = p.groups + (int64_t)g * G_FIELDS;
-  const int nch = gr[G_NL];  // lists of this query (one per overlapping indexer workgroup)
-  if (nch <= 1) return;
+  const int nl = gr[G_NL];  // lists of this query (one per overlapping indexer workgroup)
+  if (nl <= 1) return;
   const int q = t - gr[G_T0];
   const int seq = gr[G_SEQ];
-  const int64_t unit0 = (int64_t)gr[G_LIST] + (int64_t)q * nch;
+  const int64_t unit0 = (int64_t)gr[G_LIST] + (int64_t)q * nl;
   const int K = p.K;
+  const int total = nl * K;
+  // e / K as a multiply-high by ceil(2^32 / K): exact while e * K < 2^32
+  // (here e < nl * K <= 256 * 2048)
+  const uint64_t inv_k = (0x100000000ull + K - 1) / K;
 
-  // list sizes to LDS; lower bound of the final K-th key: the largest minimum
-  // over full lists
-  uint32_t lb = 0;
-  for (int c = tid; c < nch; c += MRG_NT) {
+  // ---- small merges keep every list slot in registers: issue all loads now
+  // (slots past a list's count are ignored once the counts are known)
+  const bool in_regs = total <= MRG_RS * MRG_NT;
+  uint32_t rk[MRG_RS];
+  int32_t rp[MRG_RS];
+  if (in_regs) {
+#pragma unroll
+    for (int s = 0; s < MRG_RS; ++s) {
+      const int e = s * MRG_NT + tid;
+      rk[s] = 0u;
+      rp[s] = 0;
+      if (e < total) {
+        const int c = (int)(((uint64_t)e * inv_k) >> 32), i = e - c * K;
+        rk[s] = p.list_keys[(unit0 + c) * K + i];
+        rp[s] = p.list_pos[(unit0 + c) * K + i];
+      }
+    }
+  }
+
+  // ---- list sizes to LDS; lb = largest minimum over full lists; largest key
+  uint32_t lb = 1u, mx = 0u;
+  for (int c = tid; c < nl; c += MRG_NT) {
     const int n_c = p.list_cnt[unit0 + c];
     sm.lcnt[c] = n_c;
-    if (n_c == K) lb = max(lb, p.list_min[unit0 + c]);
+    if (n_c > 0) mx = max(mx, p.list_mm[2 * (unit0 + c) + 1]);
+    if (n_c == K) lb = max(lb, p.list_mm[2 * (unit0 + c)]);
   }
 #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) lb = max(lb, (uint32_t)__shfl_xor((int)lb, d, 64));
-  if ((tid & 63) == 0) sm.red[tid >> 6] = lb;
+  for (int d = 32; d >= 1; d >>= 1) {
+    lb = max(lb, (uint32_t)__shfl_xor((int)lb, d, 64));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, d, 64));
+  }
+  if (lane == 0) {
+    sm.red[wave] = lb;
+    sm.red[MRG_NW + wave] = mx;
+  }
   lds_barrier();
-  lb = 0;
+  lb = 1u;
+  mx = 0u;
 #pragma unroll
-  for (int w = 0; w < MRG_NW; ++w) lb = max(lb, sm.red[w]);
+  for (int w = 0; w < MRG_NW; ++w) {
+    lb = max(lb, sm.red[w]);
+    mx = max(mx, sm.red[MRG_NW + w]);
+  }
   lds_barrier();
-  // keep keys >= lb (an equal key can still win on position); key 0 = no entry
-  uint32_t thr = lb > 0 ? lb - 1 : 0;
 
-  // entries in list order (= position order), batch by batch with one batch prefetched
-  const int total = nch * K;  // <= 1024 chunks x 2048
-  auto load = [&](int b0, uint32_t (&kk)[MRG_SL], int32_t (&pp)[MRG_SL]) {
+  // entry e (list e / K, slot e % K), in list order = position order
+  auto load = [&](int b0, uint32_t (&kk)[MRG_SL], int32_t (&pp)[MRG_SL], bool with_pos) {
 #pragma unroll
     for (int s = 0; s < MRG_SL; ++s) {
       const int e = b0 + s * MRG_NT + tid;
       kk[s] = 0u;
       pp[s] = 0;
       if (e < total) {
-        const int c = e / K, i = e - c * K;
+        const int c = (int)(((uint64_t)e * inv_k) >> 32), i = e - c * K;
         if (i < sm.lcnt[c]) {
           kk[s] = p.list_keys[(unit0 + c) * K + i];
-          pp[s] = p.list_pos[(unit0 + c) * K + i];
+          if (with_pos) pp[s] = p.list_pos[(unit0 + c) * K + i];
         }
       }
     }
   };
+
   uint32_t ka[MRG_SL], kb2[MRG_SL];
   int32_t pa[MRG_SL], pb2[MRG_SL];
-  load(0, ka, pa);
   int cnt = 0;
-  for (int b0 = 0; b0 < total; b0 += 2 * MRG_BATCH) {
-    load(b0 + MRG_BATCH, kb2, pb2);
-    cnt = block_append<MRG_NW, MRG_SL>(sm.cand_key, sm.cand_pos, cnt, thr, ka, pa, sm.wcnt);
-    if (cnt > MRG_CAP - MRG_BATCH) {
-      thr = max(thr, block_select<MRG_NW>(sm.cand_key, sm.cand_pos, cnt, K, sm.hist, sm.sel, sm.red));
-      cnt = K;
+  bool streamed = true;
+  if (in_regs && mx >= lb && lb != mx) {
+    // ---- register path: drop slots past the counts and keys below lb
+#pragma unroll
+    for (int s = 0; s < MRG_RS; ++s) {
+      const int e = s * MRG_NT + tid;
+      const int c = min((int)(((uint64_t)e * inv_k) >> 32), nl - 1), i = e - c * K;
+      if (e >= total || i >= sm.lcnt[c] || rk[s] < lb) rk[s] = 0u;
     }
-    load(b0 + 2 * MRG_BATCH, ka, pa);
-    cnt = block_append<MRG_NW, MRG_SL>(sm.cand_key, sm.cand_pos, cnt, thr, kb2, pb2, sm.wcnt);
-    if (cnt > MRG_CAP - MRG_BATCH) {
-      thr = max(thr, block_select<MRG_NW>(sm.cand_key, sm.cand_pos, cnt, K, sm.hist, sm.sel, sm.red));
-      cnt = K;
+    const int cp = __builtin_clz(lb ^ mx);
+    const int wb = min(MRG_BITS, 32 - cp);
+    const int shift = 32 - cp - wb;
+    const uint32_t pref = cp == 0 ? 0u : (lb & ~(0xffffffffu >> cp));
+    for (int i = tid; i < (1 << MRG_BITS); i += MRG_NT) sm.hist[i] = 0u;
+    lds_barrier();
+#pragma unroll
+    for (int s = 0; s < MRG_RS; ++s)
+      if (rk[s] != 0u) atomicAdd(&sm.hist[(rk[s] >> shift) & ((1u << wb) - 1u)], 1u);
+    lds_barrier();
+    const int nb = 1 << wb;
+    uint32_t c4[4], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int bin = nb - 1 - (4 * tid + j);
+      c4[j] = bin >= 0 ? sm.hist[bin] : 0u;
+      sum += c4[j];
+    }
+    const uint32_t winc = wave_incl_scan(sum);
+    if (lane == 63) sm.red[wave] = winc;
+    lds_barrier();
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < MRG_NW; ++w) {
+      before += (w < wave) ? sm.red[w] : 0u;
+      all += sm.red[w];
+    }
+    const uint32_t excl = before + winc - sum;
+    if (tid == 0) sm.sel[0] = -1;
+    lds_barrier();
+    if (all > (uint32_t)K && excl < (uint32_t)K && (uint32_t)K <= excl + sum) {
+      uint32_t acc = excl;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (acc < (uint32_t)K && acc + c4[j] >= (uint32_t)K) {
+          sm.sel[0] = nb - 1 - (4 * tid + j);
+          sm.sel[2] = (int)(acc + c4[j]);
+        }
+        acc += c4[j];
+      }
+    }
+    lds_barrier();
+    const int bsel = sm.sel[0];
+    const int n_keep = bsel >= 0 ? sm.sel[2] : (int)all;
+    const uint32_t thr = (bsel >= 0 ? max(lb, pref | ((uint32_t)bsel << shift)) : lb) - 1u;
+    lds_barrier();
+    if (n_keep <= MRG_CAP) {
+      streamed = false;
+#pragma unroll
+      for (int s0 = 0; s0 < MRG_RS; s0 += MRG_SL) {
+        uint32_t kk[MRG_SL];
+        int32_t pp[MRG_SL];
+#pragma unroll
+        for (int s = 0; s < MRG_SL; ++s) {
+          kk[s] = rk[s0 + s];
+          pp[s] = rp[s0 + s];
+        }
+        // slot s of this call is entry (s0 + s) * NT + tid: the order is kept
+        cnt = block_append<MRG_NW, MRG_SL>(sm.cand_key, sm.cand_pos, cnt, thr, kk, pp, sm.wcnt);
+      }
+    }
+  } else if (!in_regs && mx >= lb) {
+    // ---- pass A: histogram of the digit below the common prefix of [lb, mx]
+    const int cp = (lb == mx) ? 32 : __builtin_clz(lb ^ mx);
+    const int wb = min(MRG_BITS, 32 - cp);
+    const int shift = 32 - cp - wb;
+    const uint32_t pref = cp == 0 ? 0u : (lb & ~(0xffffffffu >> cp));
+    for (int i = tid; i < (1 << MRG_BITS); i += MRG_NT) sm.hist[i] = 0u;
+    lds_barrier();
+    if (wb > 0) {
+      load(0, ka, pa, false);
+      for (int b0 = 0; b0 < total; b0 += MRG_BATCH) {
+        uint32_t cur[MRG_SL];
+#pragma unroll
+        for (int s = 0; s < MRG_SL; ++s) cur[s] = ka[s];
+        load(b0 + MRG_BATCH, ka, pa, false);
+#pragma unroll
+        for (int s = 0; s < MRG_SL; ++s)
+          if (cur[s] >= lb) atomicAdd(&sm.hist[(cur[s] >> shift) & ((1u << wb) - 1u)], 1u);
+      }
+    }
+    lds_barrier();
+    // bin B holding the K-th largest: count(> B) < K <= count(>= B); each
+    // thread owns 4 consecutive bins, descending from the top
+    uint32_t thr_key = lb;  // keep keys >= thr_key
+    int n_keep = 0;
+    if (wb > 0) {
+      const int nb = 1 << wb;
+      uint32_t c4[4], sum = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int bin = nb - 1 - (4 * tid + j);
+        c4[j] = bin >= 0 ? sm.hist[bin] : 0u;
+        sum += c4[j];
+      }
+      const uint32_t winc = wave_incl_scan(sum);
+      if (lane == 63) sm.red[wave] = winc;
+      lds_barrier();
+      uint32_t before = 0, all = 0;
+#pragma unroll
+      for (int w = 0; w < MRG_NW; ++w) {
+        before += (w < wave) ? sm.red[w] : 0u;
+        all += sm.red[w];
+      }
+      const uint32_t excl = before + winc - sum;
+      if (tid == 0) {
+        sm.sel[0] = -1;
+        sm.sel[1] = (int)all;
+      }
+      lds_barrier();
+      if (all > (uint32_t)K && excl < (uint32_t)K && (uint32_t)K <= excl + sum) {
+        uint32_t acc = excl;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (acc < (uint32_t)K && acc + c4[j] >= (uint32_t)K) {
+            sm.sel[0] = nb - 1 - (4 * tid + j);
+            sm.sel[2] = (int)(acc + c4[j]);  // entries at or above the bin
+          }
+          acc += c4[j];
+        }
+      }
+      lds_barrier();
+      const int bsel = sm.sel[0];
+      if (bsel >= 0) {
+        thr_key = max(lb, pref | ((uint32_t)bsel << shift));
+        n_keep = sm.sel[2];
+      } else {
+        n_keep = sm.sel[1];  // at most K entries reach lb: keep them all
+      }
+      lds_barrier();
+    } else {
+      n_keep = MRG_CAP + 1;  // one key value only: decided by position, stream
+    }
+    // ---- pass B: append the kept entries in order (fits LDS by construction)
+    if (n_keep <= MRG_CAP - MRG_BATCH) {
+      streamed = false;
+      const uint32_t thr = thr_key - 1u;
+      load(0, ka, pa, true);
+      for (int b0 = 0; b0 < total; b0 += 2 * MRG_BATCH) {
+        load(b0 + MRG_BATCH, kb2, pb2, true);
+        cnt = block_append<MRG_NW, MRG_SL>(sm.cand_key, sm.cand_pos, cnt, thr, ka, pa, sm.wcnt);
+        load(b0 + 2 * MRG_BATCH, ka, pa, true);
+        cnt = block_append<MRG_NW, MRG_SL>(sm.cand_key, sm.cand_pos, cnt, thr, kb2, pb2, sm.wcnt);
+      }
+    }
+  }
+  if (streamed) {
+    // ---- fallback: stream every entry >= lb through filter-and-select
+    uint32_t thr = lb - 1u;
+    cnt = 0;
+    load(0, ka, pa, true);
+    for (int b0 = 0; b0 < total; b0 += 2 * MRG_BATCH) {
+      load(b0 + MRG_BATCH, kb2, pb2, true);
+      cnt = block_append<MRG_NW, MRG_SL>(sm.cand_key, sm.cand_pos, cnt, thr, ka, pa, sm.wcnt);
+      if (cnt > MRG_CAP - MRG_BATCH) {
+        thr = max(thr, block_select<MRG_NW>(sm.cand_key, sm.cand_pos, cnt, K, sm.hist, sm.sel, sm.red));
+        cnt = K;
+      }
+      load(b0 + 2 * MRG_BATCH, ka, pa, true);
+      cnt = block_append<MRG_NW, MRG_SL>(sm.cand_key, sm.cand_pos, cnt, thr, kb2, pb2, sm.wcnt);
+      if (cnt > MRG_CAP - MRG_BATCH) {
+        thr = max(thr, block_select<MRG_NW>(sm.cand_key, sm.cand_pos, cnt, K, sm.hist, sm.sel, sm.red));
+        cnt = K;
+      }
     }
   }
   if (cnt > K) {
