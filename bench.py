@@ -33,11 +33,42 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_b64_128k_fp8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=4, help="queries the CPU oracle is timed on")
+    ap.add_argument("--cpu-sample", type=int, default=48, help="queries the CPU oracle is timed on")
     ap.add_argument("--copies", type=int, default=2,
                     help="input copies the steps rotate through, so no step re-reads the previous step's "
                          "data from the 256 MB last-level cache")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the benchmark, run a plain 1 GiB device copy three times (the reference kernel "
+                         "that scales the FETCH_SIZE / WRITE_SIZE counters to bytes)")
     return ap.parse_args()
+
+
+def source_digest():
+    """sha256 over the kernel and ABI sources: a stored traffic measurement is
+    reported only while the code it was taken on is unchanged."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "sparse_attention_07_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "dsa.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload):
+    """HBM bytes per indexer call from the counter runs recorded under
+    profiles/, or None when absent or taken on other sources."""
+    path = os.path.join(ROOT, "profiles", f"indexer_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("sources_sha256") != source_digest():
+        return None
+    return rec.get("traffic_bytes_per_call")
 
 
 def algorithmic_bytes(case, indices):
@@ -184,8 +215,8 @@ def main():
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-            "kernel": "dsa_indexer_kernel (+ its 1-workgroup planning kernel)",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": stored_traffic(spec.name),
+            "kernel": "dsa_indexer_topk: planning + dsa_indexer_kernel + dsa_merge_kernel",
             "launch_ms": round(idx_ms, 5), "algorithmic_bytes": idx_bytes,
         },
         "layer": {
@@ -196,6 +227,13 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_sample)
     print(json.dumps(line), flush=True)
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 1 << 30, "launches": 3}), flush=True)
 
 
 if __name__ == "__main__":
