@@ -25,7 +25,7 @@ struct IdxPlan {
   int MQ = 1, nwg = 256;
   bool need_merge = false;
   int64_t lists = 0;  // candidate lists the workspace holds
-  size_t off_hdr = 0, off_groups = 0, off_qgroup = 0, off_lcnt = 0, off_lmin = 0, off_lkeys = 0, off_lpos = 0,
+  size_t off_hdr = 0, off_groups = 0, off_qgroup = 0, off_wgfirst = 0, off_lcnt = 0, off_lmin = 0, off_lkeys = 0, off_lpos = 0,
          end = 0;
 };
 
@@ -94,6 +94,8 @@ IdxPlan plan_indexer(const dsa_indexer_args* a, int K, size_t base, int nwg) {
   off = align_up(off + (size_t)T * G_FIELDS * 4, 256);
   pl.off_qgroup = off;
   off = align_up(off + (size_t)T * 4, 256);
+  pl.off_wgfirst = off;
+  off = align_up(off + (size_t)nwg * 4, 256);
   pl.off_lcnt = off;
   off = align_up(off + (size_t)pl.lists * 4, 256);
   pl.off_lmin = off;
@@ -150,6 +152,7 @@ IdxParams make_idx_params(const dsa_indexer_args* a, int K, int32_t* indices, un
   p.hdr = (int32_t*)(ws + pl.off_hdr);
   p.groups = (int32_t*)(ws + pl.off_groups);
   p.qgroup = (int32_t*)(ws + pl.off_qgroup);
+  p.wg_first = (int32_t*)(ws + pl.off_wgfirst);
   p.list_cnt = (int32_t*)(ws + pl.off_lcnt);
   p.list_mm = (uint32_t*)(ws + pl.off_lmin);
   p.list_keys = (uint32_t*)(ws + pl.off_lkeys);

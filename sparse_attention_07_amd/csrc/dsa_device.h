@@ -18,7 +18,7 @@ constexpr int VDIM = 512;
 constexpr int KMAX = 2048;
 constexpr int ROUND = 1024;  // keys scored per streaming round of the indexer
 constexpr int MIN_SLICE = 4096;       // smallest key slice an indexer workgroup is given
-constexpr int SUB = 16384;            // keys whose page ids the indexer stages in LDS at once
+constexpr int SUB = 65536;            // keys whose page ids the indexer stages in LDS at once
 constexpr int MRG_MAX_LISTS = 1024;   // most candidate lists of one query the merge accepts
 
 // Order-preserving map fp32 -> uint32 (a < b  <=>  key(a) < key(b)); -0 maps
@@ -81,15 +81,57 @@ __device__ __forceinline__ T uniform(T v) {
   return __builtin_amdgcn_readfirstlane(v);
 }
 
+// Cross-lane steps through DPP (a VALU operand modifier): unlike __shfl_*,
+// which go through LDS (ds_bpermute plus a wait each), these cost a few cycles.
+// Controls: row_shr:n = 0x110 + n within 16-lane rows; row_bcast:15 / :31
+// feed lane 15 / 31 of a row into the next row(s) selected by row_mask.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t identity, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    uint32_t o = __shfl_up(v, d, 64);
-    if (l >= d) v += o;
-  }
+  v += dpp_u32<0x111, 0xf>(0u, v);
+  v += dpp_u32<0x112, 0xf>(0u, v);
+  v += dpp_u32<0x114, 0xf>(0u, v);
+  v += dpp_u32<0x118, 0xf>(0u, v);
+  v += dpp_u32<0x142, 0xa>(0u, v);
+  v += dpp_u32<0x143, 0xc>(0u, v);
   return v;
+}
+
+// Inclusive prefix maximum (signed) over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_max(int v) {
+  const uint32_t id = 0x80000000u;
+  v = max(v, (int)dpp_u32<0x111, 0xf>(id, (uint32_t)v));
+  v = max(v, (int)dpp_u32<0x112, 0xf>(id, (uint32_t)v));
+  v = max(v, (int)dpp_u32<0x114, 0xf>(id, (uint32_t)v));
+  v = max(v, (int)dpp_u32<0x118, 0xf>(id, (uint32_t)v));
+  v = max(v, (int)dpp_u32<0x142, 0xa>(id, (uint32_t)v));
+  v = max(v, (int)dpp_u32<0x143, 0xc>(id, (uint32_t)v));
+  return v;
+}
+
+// Wave-wide minimum / maximum (unsigned), returned to every lane (uniform).
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u32<0x111, 0xf>(0xffffffffu, v));
+  v = min(v, dpp_u32<0x112, 0xf>(0xffffffffu, v));
+  v = min(v, dpp_u32<0x114, 0xf>(0xffffffffu, v));
+  v = min(v, dpp_u32<0x118, 0xf>(0xffffffffu, v));
+  v = min(v, dpp_u32<0x142, 0xa>(0xffffffffu, v));
+  v = min(v, dpp_u32<0x143, 0xc>(0xffffffffu, v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0x111, 0xf>(0u, v));
+  v = max(v, dpp_u32<0x112, 0xf>(0u, v));
+  v = max(v, dpp_u32<0x114, 0xf>(0u, v));
+  v = max(v, dpp_u32<0x118, 0xf>(0u, v));
+  v = max(v, dpp_u32<0x142, 0xa>(0u, v));
+  v = max(v, dpp_u32<0x143, 0xc>(0u, v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 }  // namespace dsa

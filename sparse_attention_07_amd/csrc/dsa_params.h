@@ -31,6 +31,7 @@ struct IdxParams {
   int32_t* hdr;        // [0] groups, [1] padded keys in total, [2] keys per workgroup slice
   int32_t* groups;     // [T][G_FIELDS]
   int32_t* qgroup;     // [T] group of each query
+  int32_t* wg_first;   // [nwg] first group of each indexer workgroup
   int32_t* list_cnt;   // per (query, chunk) candidate list: entry count
   uint32_t* list_mm;   //   [.][2] smallest and largest key of the list
   uint32_t* list_keys; //   [.][K] order keys, ascending position

@@ -46,11 +46,7 @@ constexpr int PLAN_NT = 1024;
 __device__ __forceinline__ int block_scan_incl(int v, int* s_w, bool is_max) {
   // inclusive scan (sum or max) over PLAN_NT threads; s_w: >= 16 ints of LDS
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    int o = __shfl_up(v, d, 64);
-    if (lane >= d) v = is_max ? max(v, o) : v + o;
-  }
+  v = is_max ? wave_incl_max(v) : (int)wave_incl_scan((uint32_t)v);
   if (lane == 63) s_w[wave] = v;
   __syncthreads();
   int add = is_max ? -1 : 0;
@@ -145,6 +141,8 @@ __global__ __launch_bounds__(PLAN_NT) void dsa_plan_kernel(IdxParams p) {
       const int w0 = off / slice, w1 = (off + wgt - 1) / slice;
       gr[G_W0] = w0;
       gr[G_NL] = w1 - w0 + 1;
+      // workgroups whose slice starts inside this group begin with it
+      for (int w = (off + slice - 1) / slice; w <= w1 && w < p.nwg; ++w) p.wg_first[w] = g;
       lists = w1 > w0 ? gr[G_NQ] * (w1 - w0 + 1) : 0;
     }
     const int sl = block_scan_incl(lists, s_w, false);
@@ -165,67 +163,109 @@ __global__ __launch_bounds__(PLAN_NT) void dsa_plan_kernel(IdxParams p) {
 // Block-wide selection primitives (shared by the indexer and the merge).
 // =============================================================================
 
-// Top-K of keys/pos[0..n) (n > K) by radix select over the 64-bit composite
-// (key, ~pos); exactly K entries remain, in their original (position) order,
-// at [0..K).  The leading bits shared by every key (block min/max) are skipped,
-// so the first 8-bit digit already spreads clustered keys over the bins; each
-// wave counts into its own histogram (hist: NW*256 words).  Returns a lower
-// bound of the smallest kept key: an entry at a later position whose key is
-// <= the bound can never enter.
-template <int NW>
-__device__ uint32_t block_select(uint32_t* keys, int32_t* pos, int n, int K, uint32_t* hist, int32_t* sel,
+// Top-K of keys/pos[0..n) (K < n <= R * NW * 64) by radix select over the
+// composite (key, earlier position first); exactly K entries remain, in their
+// original (position) order, at [0..K).  Entries are read into registers once
+// (wave w holds one contiguous run, 64 entries per register slot), so the
+// histogram passes and the compaction touch LDS only for the histograms.
+// Digits are taken from the offset above the smallest candidate (key - min,
+// then pmax - pos among equal keys), 8 bits at a time from the top of the
+// range actually spanned: float scores of one magnitude then spread over many
+// bins instead of piling onto the one or two bins their exponent bits share,
+// which would serialise the LDS atomics.  Each wave counts into its own
+// histogram; two histogram sets alternate so clearing the next one needs no
+// barrier of its own.  Keys are >= 1 (0 marks an empty slot) and positions
+// are distinct.  hist: 2 * NW * 256 words; wtmp: 4 * NW words.  Returns the smallest kept key: an
+// entry at a later position whose key is <= it can never enter.
+template <int NW, int R>
+__device__ __forceinline__ uint32_t block_select(uint32_t* keys, int32_t* pos, int n, int K, uint32_t* hist, int32_t* sel,
                                  uint32_t* wtmp) {
   constexpr int NT = NW * 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // ---- common prefix of all keys
-  uint32_t mn = 0xffffffffu, mx = 0u;
-  for (int i = tid; i < n; i += NT) {
-    const uint32_t k = keys[i];
-    mn = min(mn, k);
-    mx = max(mx, k);
+  lds_barrier();  // entries appended by other waves are visible
+  const int chunk = (((n + NW - 1) / NW) + 63) & ~63;
+  const int wbeg = wave * chunk;
+  uint32_t rk[R];
+  int32_t rp[R];
+  uint32_t mn = 0xffffffffu, mx = 0u, pmn = 0xffffffffu, pmx = 0u;
+  // every slot is read (from a clamped index, so all reads go out at once)
+  // and masked afterwards
+#pragma unroll
+  for (int s = 0; s < R; ++s) {
+    const int i = wbeg + s * 64 + lane;
+    const int ic = min(i, n - 1);
+    const uint32_t k = keys[ic];
+    const int32_t ps = pos[ic];
+    const bool v = s * 64 < chunk && i < n;
+    rk[s] = v ? k : 0u;
+    rp[s] = ps;
   }
 #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, d, 64));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, d, 64));
+  for (int s = 0; s < R; ++s) {
+    const bool v = rk[s] != 0u;
+    mn = min(mn, v ? rk[s] : 0xffffffffu);
+    mx = max(mx, rk[s]);
+    pmn = min(pmn, v ? (uint32_t)rp[s] : 0xffffffffu);
+    pmx = max(pmx, v ? (uint32_t)rp[s] : 0u);
   }
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  pmn = wave_min_u32(pmn);
+  pmx = wave_max_u32(pmx);
+  uint32_t* red4 = wtmp;
   if (lane == 0) {
-    wtmp[wave] = mn;
-    wtmp[NW + wave] = mx;
+    red4[4 * wave + 0] = mn;
+    red4[4 * wave + 1] = mx;
+    red4[4 * wave + 2] = pmn;
+    red4[4 * wave + 3] = pmx;
   }
+  for (int i = tid; i < NW * 256; i += NT) hist[i] = 0u;
   lds_barrier();
   mn = 0xffffffffu;
   mx = 0u;
+  pmn = 0xffffffffu;
+  pmx = 0u;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
-    mn = min(mn, wtmp[w]);
-    mx = max(mx, wtmp[NW + w]);
+    mn = min(mn, red4[4 * w + 0]);
+    mx = max(mx, red4[4 * w + 1]);
+    pmn = min(pmn, red4[4 * w + 2]);
+    pmx = max(pmx, red4[4 * w + 3]);
   }
-  lds_barrier();
-  int kb = (mn == mx) ? 32 : __builtin_clz(mn ^ mx);  // key bits resolved
-  uint32_t kpref = kb >= 32 ? mn : (kb == 0 ? 0u : (mn & ~(0xffffffffu >> kb)));
-  int pb = 0;  // position bits resolved (of ~pos)
-  uint32_t ppref = 0;
+  // phase 0 resolves the key, phase 1 (equal keys) the position; in each,
+  // candidates lie in [lo, lo + 2^sb - 1] of the phase's value
+  auto bits_of = [](uint32_t r) { return r == 0u ? 0 : 32 - __builtin_clz(r); };
+  int phase = 0;
+  uint32_t klo = mn, lo = mn;
+  int sb = bits_of(mx - mn);
+  if (sb == 0) {
+    phase = 1;
+    lo = 0u;
+    sb = bits_of(pmx - pmn);
+  }
   int need = K;
   bool done = false;
-  while (!done && pb < 32) {
-    const bool onpos = kb >= 32;
-    const int rb = onpos ? pb : kb;
-    const int wd = min(8, 32 - rb);
-    const int shift = 32 - rb - wd;
-    for (int i = tid; i < NW * 256; i += NT) hist[i] = 0u;
-    lds_barrier();
-    uint32_t* wh = hist + wave * 256;
-    for (int i = tid; i < n; i += NT) {
-      const uint32_t k = keys[i];
-      const uint32_t pp = ~(uint32_t)pos[i];
-      bool m;
-      if (!onpos)
-        m = (kb == 0) || ((k >> (32 - kb)) == (kpref >> (32 - kb)));
-      else
-        m = (k == kpref) && ((pb == 0) || ((pp >> (32 - pb)) == (ppref >> (32 - pb))));
-      if (m) atomicAdd(&wh[((onpos ? pp : k) >> shift) & ((1u << wd) - 1u)], 1u);
+  int pass = 0;
+  while (!done && pass < 10) {  // at most 4 key and 4 position passes
+    const int wd = min(8, sb);
+    const int shift = sb - wd;
+    uint32_t* hb = hist + (pass & 1) * (NW * 256);
+    uint32_t* wh = hb + wave * 256;
+    // branch-free match: value in [lo, lo + span], and (phase 1) key == klo
+    const uint32_t span = sb >= 32 ? 0xffffffffu : (1u << sb) - 1u;
+    const bool ph1 = phase == 1;
+    const uint32_t kreq = ph1 ? klo : 0u;
+#pragma unroll
+    for (int s = 0; s < R; ++s) {
+      const uint32_t k = rk[s];
+      const uint32_t off = (ph1 ? pmx - (uint32_t)rp[s] : k) - lo;
+      const bool m = (k != 0u) & (off <= span) & ((k == kreq) | !ph1);
+      if (m) atomicAdd(&wh[off >> shift], 1u);
     }
+    // the other set is cleared for the next pass (its last reader, wave 0's
+    // scan of the previous pass, finished before the previous barrier)
+    uint32_t* ho = hist + ((pass + 1) & 1) * (NW * 256);
+    for (int i = tid; i < NW * 256; i += NT) ho[i] = 0u;
     lds_barrier();
     if (tid < 64) {
       // lane L owns bins 255-4L .. 252-4L (descending), summed over the waves
@@ -234,7 +274,7 @@ __device__ uint32_t block_select(uint32_t* keys, int32_t* pos, int n, int K, uin
       for (int j = 0; j < 4; ++j) {
         uint32_t v = 0;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) v += hist[w * 256 + 255 - 4 * lane - j];
+        for (int w = 0; w < NW; ++w) v += hb[w * 256 + 255 - 4 * lane - j];
         c[j] = v;
         sum += v;
       }
@@ -254,53 +294,64 @@ __device__ uint32_t block_select(uint32_t* keys, int32_t* pos, int n, int K, uin
       }
     }
     lds_barrier();
+    // sel is rewritten only after the next pass's first barrier, which every
+    // wave reaches after this read
     const int bin = sel[0], above = sel[1], cb = sel[2];
-    lds_barrier();
     need -= above;
-    if (!onpos) {
-      kpref |= (uint32_t)bin << shift;
-      kb += wd;
-    } else {
-      ppref |= (uint32_t)bin << shift;
-      pb += wd;
+    lo += (uint32_t)bin << shift;
+    sb = shift;
+    ++pass;
+    if (cb == need || (phase == 1 && sb == 0)) {
+      done = true;
+    } else if (sb == 0) {
+      // phase 0 resolved the key exactly; phase 1 cannot get here (positions
+      // are distinct, so a resolved bin holds one entry)
+      klo = lo;
+      phase = 1;
+      lo = 0u;
+      sb = bits_of(pmx - pmn);
     }
-    done = (cb == need);
   }
-  // ---- order-preserving compaction of the selected entries: the resolved
-  // prefix of (key, ~pos) must be >= the threshold prefix
-  int running = 0;
-  for (int base = 0; base < n; base += NT) {
-    const int i = base + tid;
-    uint32_t k = 0;
-    int32_t ps = 0;
-    bool s = false;
-    if (i < n) {
-      k = keys[i];
-      ps = pos[i];
-      if (kb < 32)
-        s = kb == 0 || (k >> (32 - kb)) >= (kpref >> (32 - kb));
-      else
-        s = (k > kpref) || (k == kpref && (pb == 0 || ((~(uint32_t)ps) >> (32 - pb)) >= (ppref >> (32 - pb))));
-    }
-    const uint64_t m = ballot(s);
-    if (lane == 0) wtmp[wave] = (uint32_t)__builtin_popcountll(m);
-    lds_barrier();
-    int pre = 0, tot = 0;
+  // ---- order-preserving compaction.  Waves own consecutive runs, so a wave's
+  // output offset is the count of the waves before it.
+  // keep = k > ka, or k == kb and pmx - pos >= lo (phase 0: k >= lo, and kb
+  // is a key no candidate has; empty slots, key 0, fail both)
+  const uint32_t ka = phase == 0 ? lo - 1u : klo;
+  const uint32_t kb = phase == 0 ? 0xffffffffu : klo;
+  auto keep = [&](uint32_t k, int32_t ps) { return (k > ka) | ((k == kb) & (pmx - (uint32_t)ps >= lo)); };
+  uint32_t wc = 0, kmin = 0xffffffffu;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const int c = (int)wtmp[w];
-      pre += (w < wave) ? c : 0;
-      tot += c;
-    }
-    if (s) {
-      const int o = running + pre + lanes_below(m);
-      keys[o] = k;
-      pos[o] = ps;
-    }
-    running += tot;
-    lds_barrier();
+  for (int s = 0; s < R; ++s) {
+    const bool kp = keep(rk[s], rp[s]);
+    wc += (uint32_t)__builtin_popcountll(ballot(kp));
+    if (kp) kmin = min(kmin, rk[s]);
   }
-  return kb >= 32 ? kpref : (kb == 0 ? 0u : (kpref & ~(0xffffffffu >> kb)));
+  kmin = wave_min_u32(kmin);
+  if (lane == 0) {
+    wtmp[wave] = wc;
+    wtmp[NW + wave] = kmin;
+  }
+  lds_barrier();
+  int run = 0;
+  kmin = 0xffffffffu;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    run += (w < wave) ? (int)wtmp[w] : 0;
+    kmin = min(kmin, wtmp[NW + w]);
+  }
+#pragma unroll
+  for (int s = 0; s < R; ++s) {
+    const bool kp = keep(rk[s], rp[s]);
+    const uint64_t m = ballot(kp);
+    if (kp) {
+      const int o = run + lanes_below(m);
+      keys[o] = rk[s];
+      pos[o] = rp[s];
+    }
+    run += (int)__builtin_popcountll(m);
+  }
+  lds_barrier();
+  return kmin;
 }
 
 // Order-preserving append of the entries (kk[s], pp[s]) held by this thread
@@ -308,7 +359,7 @@ __device__ uint32_t block_select(uint32_t* keys, int32_t* pos, int n, int K, uin
 // Returns the new count (the same in every thread).  wcnt: 2*SL*NW + 1 words of
 // LDS (counts per (slot, wave), then their exclusive scan and the total).
 template <int NW, int SL>
-__device__ int block_append(uint32_t* keys, int32_t* pos, int base, uint32_t thr, const uint32_t (&kk)[SL],
+__device__ __forceinline__ int block_append(uint32_t* keys, int32_t* pos, int base, uint32_t thr, const uint32_t (&kk)[SL],
                             const int32_t (&pp)[SL], uint32_t* wcnt) {
   static_assert(SL * NW <= 64, "one wave scans the (slot, wave) counts");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -341,18 +392,15 @@ __device__ int block_append(uint32_t* keys, int32_t* pos, int base, uint32_t thr
 
 // Smallest and largest key of keys[0..n) (block-wide; n >= 1).
 template <int NW>
-__device__ void block_minmax(const uint32_t* keys, int n, uint32_t* red, uint32_t& mn_out, uint32_t& mx_out) {
+__device__ __forceinline__ void block_minmax(const uint32_t* keys, int n, uint32_t* red, uint32_t& mn_out, uint32_t& mx_out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t mn = 0xffffffffu, mx = 0u;
   for (int i = tid; i < n; i += NW * 64) {
     mn = min(mn, keys[i]);
     mx = max(mx, keys[i]);
   }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, d, 64));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, d, 64));
-  }
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
   if (lane == 0) {
     red[wave] = mn;
     red[NW + wave] = mx;
@@ -382,17 +430,16 @@ template <int NW, int MQ>
 struct IdxSmem {
   static constexpr int CAP = CapOf<MQ>::value;
   static constexpr int NT = NW * 64;
-  static constexpr int SL = ROUND / NT;
+  static constexpr int R = CAP / NT;  // candidate entries per thread in a selection
+  static_assert(CAP % NT == 0, "selection register slots");
   uint32_t cand_key[MQ][CAP];
   int32_t cand_pos[MQ][CAP];
-  uint32_t rb[2][MQ][ROUND];
-  uint32_t hist[NW * 256];
-  uint32_t wcnt[2 * SL * NW + 1];
-  uint32_t red[2 * NW];
-  int32_t cnt[MQ];
-  uint32_t thr[MQ];
+  uint32_t hist[2 * NW * 256];
+  uint32_t wcnt[2][MQ][NW];  // per-round candidate counts of each wave (rounds alternate)
+  uint32_t red[4 * NW];
   int32_t sel[4];
   int32_t pages[SUB / PAGE + 1];  // the sub-chunk's block-table slice (-1 = invalid page); +1 when unaligned
+  float wq[MQ][64];               // head weight x query scale of the group's queries
 };
 
 template <int DT, int D>
@@ -414,11 +461,12 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
   using Sm = IdxSmem<NW, MQ>;
   constexpr int NT = NW * 64;
   constexpr int CAP = Sm::CAP;
-  constexpr int SL = Sm::SL;
+  constexpr int R = Sm::R;
   constexpr int GPW = ROUND / 16 / NW;  // 16-key groups per wave per round
-  constexpr int PF = MQ == 1 ? 8 : 4;    // register prefetch depth (groups)
   constexpr int ES = DT == 0 ? 2 : 1;   // bytes per element
   constexpr int ROWB = D * ES;          // bytes per key row
+  // register prefetch depth (16-key groups): up to about 17 KB of loads in flight per wave
+  constexpr int PF = (MQ == 1 && ROWB <= 128) ? 8 : 4;
   static_assert(GPW % PF == 0, "prefetch ring must divide the round");
   static_assert(DT == 0 || D == 128, "fp8 path is 128-wide");
 
@@ -438,19 +486,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
   const int a1 = min(a0 + slice, total);
   if (a0 >= a1) return;
 
-  // first group overlapping [a0, a1): the last one whose offset is <= a0
-  int g = 0;
-  {
-    int lo = 0, hi = n_groups - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (p.groups[(int64_t)mid * G_FIELDS + G_OFF] <= a0)
-        lo = mid;
-      else
-        hi = mid - 1;
-    }
-    g = lo;
-  }
+  // first group overlapping [a0, a1), found by the planning kernel
+  int g = uniform(p.wg_first[blockIdx.x]);
 
   for (; g < n_groups; ++g) {
     const int* gr = p.groups + (int64_t)g * G_FIELDS;
@@ -481,49 +518,69 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
       vis[q] = uniform(v);
     }
 
-    // ---- query operands and weights (identical in every wave)
+    // ---- query operands (identical in every wave).  Every load is issued
+    // unconditionally from a clamped index and masked afterwards, so they all
+    // go out back to back instead of one branch (and one wait) at a time.
+    // Head weights (times the query scales) go through LDS below, together
+    // with the first sub-chunk's page ids.
     Frag<DT, D> a[MQ][HT];
     float wv[MQ][HT][4];
 #pragma unroll
     for (int q = 0; q < MQ; ++q) {
+      const int64_t tq = t0 + min(q, nq - 1);
 #pragma unroll
       for (int mt = 0; mt < HT; ++mt) {
         const int h = mt * 16 + n16;
         const bool okh = q < nq && h < p.H_idx;
-        const uint8_t* row = p.q_idx + ((int64_t)(t0 + q) * p.H_idx + h) * ROWB;
+        const uint8_t* row = p.q_idx + (tq * p.H_idx + min(h, p.H_idx - 1)) * ROWB;
 #pragma unroll
         for (int j = 0; j < Frag<DT, D>::NP; ++j) {
           const int off_b = DT == 0 ? 2 * (32 * j + 8 * g4) : (64 * j + 16 * g4);
-          a[q][mt].d[j] = okh ? *reinterpret_cast<const v4i*>(row + off_b) : v4i{0, 0, 0, 0};
+          const v4i v = *reinterpret_cast<const v4i*>(row + off_b);
+          a[q][mt].d[j] = okh ? v : v4i{0, 0, 0, 0};
         }
+      }
+    }
+
+    // candidate count and filter bound of each query (identical in every thread)
+    int cnt[MQ];
+    uint32_t thr[MQ];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int hh = mt * 16 + 4 * g4 + i;
+    for (int q = 0; q < MQ; ++q) {
+      cnt[q] = 0;
+      thr[q] = 0u;
+    }
+    int rpar = 0;
+
+    // ---- stream the segment in sub-chunks (page ids of a sub-chunk staged in LDS)
+    for (int kb = seg_lo; kb < seg_hi; kb += SUB) {
+      const int ke = min(kb + SUB, seg_hi);
+      const int pg0 = kb >> 6;
+      if (kb == seg_lo) {
+        for (int i = tid; i < MQ * 64; i += NT) {
+          const int q = i >> 6, hh = i & 63;
           float wt = 0.f;
           if (q < nq && hh < p.H_idx) {
             const int64_t o = (int64_t)(t0 + q) * p.H_idx + hh;
             wt = p.w[o];
             if (DT == 1) wt *= p.q_scale[o];
           }
-          wv[q][mt][i] = wt;
+          sm.wq[q][hh] = wt;
         }
       }
-    }
-
-    if (tid < MQ) {
-      sm.cnt[tid] = 0;
-      sm.thr[tid] = 0u;
-    }
-
-    // ---- stream the segment in sub-chunks (page ids of a sub-chunk staged in LDS)
-    for (int kb = seg_lo; kb < seg_hi; kb += SUB) {
-      const int ke = min(kb + SUB, seg_hi);
-      const int pg0 = kb >> 6;
       for (int i = tid; i <= ((ke - 1) >> 6) - pg0; i += NT) {
         const int pg = bt[pg0 + i];
         sm.pages[i] = (pg >= 0 && (int64_t)pg < p.num_blocks) ? pg : -1;
       }
       lds_barrier();
+      if (kb == seg_lo) {
+#pragma unroll
+        for (int q = 0; q < MQ; ++q)
+#pragma unroll
+          for (int mt = 0; mt < HT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wv[q][mt][i] = sm.wq[q][mt * 16 + 4 * g4 + i];
+      }
       int lim[MQ];
 #pragma unroll
       for (int q = 0; q < MQ; ++q) lim[q] = min(vis[q], ke);
@@ -548,7 +605,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
         bf.ok = ok;
       };
 
-      auto score_group = [&](const BFrag<DT, D>& bf, int p0, int rs, int rbuf) {
+      auto score_group = [&](const BFrag<DT, D>& bf, int p0, uint32_t (&kk)[MQ][GPW], int s) {
 #pragma unroll
         for (int q = 0; q < MQ; ++q) {
           if (q < nq) {
@@ -581,9 +638,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
               }
             float sc = sum_lane_groups(part);
             if (DT == 1) sc *= bf.sc;
-            const int pp = p0 + n16;
-            const bool valid = bf.ok && pp < lim[q];
-            if (lane < 16) sm.rb[rbuf][q][pp - rs] = valid ? order_key(sc) : 0u;
+            const bool valid = bf.ok && p0 + n16 < lim[q];
+            kk[q][s] = valid ? order_key(sc) : 0u;
+          } else {
+            kk[q][s] = 0u;
           }
         }
       };
@@ -592,46 +650,72 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
       // past the sub-chunk end re-read its last 16-key group (a cache hit).
       const int last_p0 = kb + ((nkeys - 1) & ~15);
       auto load_p0 = [&](int j) { return min(group_p0(j), last_p0); };
+      // The prologue issues the ring in slot order (scheduling barriers keep
+      // the compiler from reordering it): the wait counts at the loop head
+      // are merged over the prologue and the back edge, and a slot loaded
+      // last here would force a wait for every load in flight each round.
       BFrag<DT, D> buf[PF];
 #pragma unroll
-      for (int s = 0; s < PF; ++s) load_b(buf[s], load_p0(s));
+      for (int s = 0; s < PF; ++s) {
+        load_b(buf[s], load_p0(s));
+        __builtin_amdgcn_sched_barrier(0);
+      }
       for (int r = 0; r < nrounds; ++r) {
-        const int rs = kb + r * ROUND;
-        const int rbuf = r & 1;
+        // score this wave's GPW groups (keys stay in lanes 0..15 of each)
+        uint32_t kk[MQ][GPW];
 #pragma unroll
         for (int s = 0; s < GPW; ++s) {
           const int j = r * GPW + s;
           const int p0 = group_p0(j);
-          if (p0 < ke) score_group(buf[s % PF], p0, rs, rbuf);
+          if (p0 < ke) {
+            score_group(buf[s % PF], p0, kk, s);
+          } else {
+#pragma unroll
+            for (int q = 0; q < MQ; ++q) kk[q][s] = 0u;
+          }
           load_b(buf[s % PF], load_p0(j + PF));
         }
+        // append the keys above each query's bound: a wave's groups are
+        // consecutive positions and waves follow each other, so a wave's
+        // offset is the count of the waves before it (one barrier per round)
+#pragma unroll
+        for (int q = 0; q < MQ; ++q) {
+          uint32_t wc = 0;
+#pragma unroll
+          for (int s = 0; s < GPW; ++s) wc += (uint32_t)__builtin_popcountll(ballot(lane < 16 && kk[q][s] > thr[q]));
+          if (lane == 0) sm.wcnt[rpar][q][wave] = wc;
+        }
         lds_barrier();
-        const int nr = min(ROUND, ke - rs);
 #pragma unroll
         for (int q = 0; q < MQ; ++q) {
           if (q < nq) {
-            uint32_t kk[SL];
-            int32_t pp[SL];
+            int o = cnt[q], tot = 0;
 #pragma unroll
-            for (int s = 0; s < SL; ++s) {
-              const int i = s * NT + tid;
-              kk[s] = i < nr ? sm.rb[rbuf][q][i] : 0u;
-              pp[s] = rs + i;
+            for (int w = 0; w < NW; ++w) {
+              const int c = (int)sm.wcnt[rpar][q][w];
+              o += (w < wave) ? c : 0;
+              tot += c;
             }
-            const int c = block_append<NW, SL>(sm.cand_key[q], sm.cand_pos[q], sm.cnt[q], sm.thr[q], kk, pp,
-                                               sm.wcnt);
-            if (c > CAP - ROUND) {
-              const uint32_t t = block_select<NW>(sm.cand_key[q], sm.cand_pos[q], c, p.K, sm.hist, sm.sel, sm.red);
-              if (tid == 0) {
-                sm.cnt[q] = p.K;
-                sm.thr[q] = t;
+#pragma unroll
+            for (int s = 0; s < GPW; ++s) {
+              const bool t = lane < 16 && kk[q][s] > thr[q];
+              const uint64_t m = ballot(t);
+              if (t) {
+                const int oo = o + lanes_below(m);
+                sm.cand_key[q][oo] = kk[q][s];
+                sm.cand_pos[q][oo] = group_p0(r * GPW + s) + lane;
               }
-            } else if (tid == 0) {
-              sm.cnt[q] = c;
+              o += (int)__builtin_popcountll(m);
             }
-            lds_barrier();
+            cnt[q] += tot;
+            if (cnt[q] > CAP - ROUND) {
+              thr[q] = max(thr[q], block_select<NW, R>(sm.cand_key[q], sm.cand_pos[q], cnt[q], p.K, sm.hist,
+                                                       sm.sel, sm.red));
+              cnt[q] = p.K;
+            }
           }
         }
+        rpar ^= 1;
       }
     }
 
@@ -639,10 +723,12 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
 #pragma unroll
     for (int q = 0; q < MQ; ++q) {
       if (q < nq) {
-        int c = sm.cnt[q];
+        int c = cnt[q];
         if (c > p.K) {
-          block_select<NW>(sm.cand_key[q], sm.cand_pos[q], c, p.K, sm.hist, sm.sel, sm.red);
+          block_select<NW, R>(sm.cand_key[q], sm.cand_pos[q], c, p.K, sm.hist, sm.sel, sm.red);
           c = p.K;
+        } else {
+          lds_barrier();  // other waves' appends are visible
         }
         if (nl == 1) {
           int32_t* out = p.indices + (int64_t)(t0 + q) * p.K;
@@ -697,9 +783,9 @@ constexpr int MRG_BITS = 11;
 struct MergeSmem {
   uint32_t cand_key[MRG_CAP];
   int32_t cand_pos[MRG_CAP];
-  uint32_t hist[MRG_NW * 256];  // also the 2^MRG_BITS-bin histogram of pass A
+  uint32_t hist[2 * MRG_NW * 256];  // also the 2^MRG_BITS-bin histogram of pass A
   uint32_t wcnt[2 * MRG_SL * MRG_NW + 1];
-  uint32_t red[2 * MRG_NW];
+  uint32_t red[4 * MRG_NW];
   int32_t sel[4];
   int32_t lcnt[MRG_MAX_LISTS];
 };
@@ -751,11 +837,8 @@ __global__ __launch_bounds__(MRG_NT, 1) void dsa_merge_kernel(IdxParams p) {
     if (n_c > 0) mx = max(mx, p.list_mm[2 * (unit0 + c) + 1]);
     if (n_c == K) lb = max(lb, p.list_mm[2 * (unit0 + c)]);
   }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    lb = max(lb, (uint32_t)__shfl_xor((int)lb, d, 64));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, d, 64));
-  }
+  lb = wave_max_u32(lb);
+  mx = wave_max_u32(mx);
   if (lane == 0) {
     sm.red[wave] = lb;
     sm.red[MRG_NW + wave] = mx;
@@ -954,19 +1037,19 @@ __global__ __launch_bounds__(MRG_NT, 1) void dsa_merge_kernel(IdxParams p) {
       load(b0 + MRG_BATCH, kb2, pb2, true);
       cnt = block_append<MRG_NW, MRG_SL>(sm.cand_key, sm.cand_pos, cnt, thr, ka, pa, sm.wcnt);
       if (cnt > MRG_CAP - MRG_BATCH) {
-        thr = max(thr, block_select<MRG_NW>(sm.cand_key, sm.cand_pos, cnt, K, sm.hist, sm.sel, sm.red));
+        thr = max(thr, block_select<MRG_NW, MRG_CAP / MRG_NT>(sm.cand_key, sm.cand_pos, cnt, K, sm.hist, sm.sel, sm.red));
         cnt = K;
       }
       load(b0 + 2 * MRG_BATCH, ka, pa, true);
       cnt = block_append<MRG_NW, MRG_SL>(sm.cand_key, sm.cand_pos, cnt, thr, kb2, pb2, sm.wcnt);
       if (cnt > MRG_CAP - MRG_BATCH) {
-        thr = max(thr, block_select<MRG_NW>(sm.cand_key, sm.cand_pos, cnt, K, sm.hist, sm.sel, sm.red));
+        thr = max(thr, block_select<MRG_NW, MRG_CAP / MRG_NT>(sm.cand_key, sm.cand_pos, cnt, K, sm.hist, sm.sel, sm.red));
         cnt = K;
       }
     }
   }
   if (cnt > K) {
-    block_select<MRG_NW>(sm.cand_key, sm.cand_pos, cnt, K, sm.hist, sm.sel, sm.red);
+    block_select<MRG_NW, MRG_CAP / MRG_NT>(sm.cand_key, sm.cand_pos, cnt, K, sm.hist, sm.sel, sm.red);
     cnt = K;
   }
   const int32_t* bt = p.block_table + (int64_t)max(seq, 0) * p.max_blocks;
