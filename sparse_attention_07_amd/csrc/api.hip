@@ -84,8 +84,9 @@ IdxPlan plan_indexer(const dsa_indexer_args* a, int K, size_t base, int nwg) {
   const int64_t T = a->T;
   // a query group is split over workgroups (and then needs candidate lists and
   // the merge) only if the whole key space exceeds one minimum slice
-  const int64_t max_total = T * std::max<int64_t>(16, (maxlen + 15) & ~15);
-  pl.need_merge = max_total > MIN_SLICE;
+  // (the last group's segment-cost weight holds no keys, hence - SEG_COST)
+  const int64_t max_total = T * (std::max<int64_t>(16, (maxlen + 15) & ~15) + SEG_COST);
+  pl.need_merge = max_total - SEG_COST > MIN_SLICE;
   pl.lists = pl.need_merge ? (int64_t)2 * pl.MQ * nwg : 0;
   size_t off = align_up(base, 256);
   pl.off_hdr = off;

@@ -18,6 +18,11 @@ constexpr int VDIM = 512;
 constexpr int KMAX = 2048;
 constexpr int ROUND = 1024;  // keys scored per streaming round of the indexer
 constexpr int MIN_SLICE = 4096;       // smallest key slice an indexer workgroup is given
+// Fixed cost of one indexer segment (a group's keys inside one workgroup's
+// slice: query setup, final selection, output), in keys streamed at full
+// bandwidth.  Each group is charged this many extra keys of weight in the
+// key-space partition, so slices that hold more segments get fewer keys.
+constexpr int SEG_COST = 2560;
 constexpr int SUB = 65536;            // keys whose page ids the indexer stages in LDS at once
 constexpr int MRG_MAX_LISTS = 1024;   // most candidate lists of one query the merge accepts
 

@@ -118,7 +118,7 @@ __global__ __launch_bounds__(PLAN_NT) void dsa_plan_kernel(IdxParams p) {
       }
       gr[G_NQ] = t1 - t0;
       gr[G_RANGE] = range;
-      wgt = max(16, (range + 15) & ~15);
+      wgt = max(16, (range + 15) & ~15) + SEG_COST;
     }
     const int so = block_scan_incl(wgt, s_w, false);
     if (g < n_groups) gr[G_OFF] = c_off + so - wgt;
@@ -137,12 +137,15 @@ __global__ __launch_bounds__(PLAN_NT) void dsa_plan_kernel(IdxParams p) {
     int* gr = p.groups + (int64_t)g * G_FIELDS;
     if (g < n_groups) {
       const int off = gr[G_OFF];
-      const int wgt = max(16, (gr[G_RANGE] + 15) & ~15);
-      const int w0 = off / slice, w1 = (off + wgt - 1) / slice;
+      // workgroups holding the group's keys (the extra weight that stands
+      // for the segment cost follows them and holds no keys)
+      const int wreal = max(16, (gr[G_RANGE] + 15) & ~15);
+      const int w0 = off / slice, w1 = (off + wreal - 1) / slice;
+      const int wlast = (off + wreal + SEG_COST - 1) / slice;
       gr[G_W0] = w0;
       gr[G_NL] = w1 - w0 + 1;
       // workgroups whose slice starts inside this group begin with it
-      for (int w = (off + slice - 1) / slice; w <= w1 && w < p.nwg; ++w) p.wg_first[w] = g;
+      for (int w = (off + slice - 1) / slice; w <= wlast && w < p.nwg; ++w) p.wg_first[w] = g;
       lists = w1 > w0 ? gr[G_NQ] * (w1 - w0 + 1) : 0;
     }
     const int sl = block_scan_incl(lists, s_w, false);
@@ -500,10 +503,11 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
     const int nl = uniform(gr[G_NL]);
     const int list_base = uniform(gr[G_LIST]);
     const int w0 = uniform(gr[G_W0]);
-    const int wgt = max(16, (range + 15) & ~15);
+    const int wreal = max(16, (range + 15) & ~15);
+    if ((int)blockIdx.x >= w0 + nl) continue;  // only the group's cost weight lies in this slice
     // this workgroup's keys of the group: [seg_lo, seg_hi), multiples of 16
     const int seg_lo = max(a0, off) - off;
-    const int seg_hi = min(min(a1, off + wgt) - off, range);
+    const int seg_hi = min(min(a1, off + wreal) - off, range);
     const int32_t* bt = p.block_table + (int64_t)max(seq, 0) * p.max_blocks;
 
     int vis[MQ];
