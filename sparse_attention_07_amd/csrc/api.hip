@@ -121,7 +121,7 @@ MlaPlan plan_mla(const dsa_mla_args* m, int K, size_t base) {
   size_t off = align_up(base, 256);
   if (S > 1) {
     pl.off_o = off;
-    off = align_up(off + (size_t)m->T * S * m->H * DSA_VALUE_DIM * 4, 256);
+    off = align_up(off + (size_t)m->T * S * m->H * DSA_VALUE_DIM * 2, 256);
     pl.off_ml = off;
     off = align_up(off + (size_t)m->T * S * m->H * 2 * 4, 256);
   }
@@ -175,7 +175,7 @@ MlaParams make_mla_params(const dsa_mla_args* m, const int32_t* indices, int K, 
   p.rows_per_split = pl.RPS;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.out = (uint16_t*)out;
-  p.part_o = pl.S > 1 ? (float*)(ws + pl.off_o) : nullptr;
+  p.part_o = pl.S > 1 ? (_Float16*)(ws + pl.off_o) : nullptr;
   p.part_ml = pl.S > 1 ? (float*)(ws + pl.off_ml) : nullptr;
   return p;
 }

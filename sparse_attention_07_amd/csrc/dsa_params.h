@@ -48,7 +48,7 @@ struct MlaParams {
   int32_t rows_per_split;   // multiple of 32
   float scale_log2;         // softmax scale * log2(e)
   uint16_t* out;            // [T][H][512] bf16
-  float* part_o;            // [T][S][H][512] fp32 (S > 1)
+  _Float16* part_o;         // [T][S][H][512] fp16, normalised O/l of each split (S > 1)
   float* part_ml;           // [T][S][H][2]   fp32 (S > 1)
 };
 

@@ -166,43 +166,37 @@ __global__ __launch_bounds__(PLAN_NT) void dsa_plan_kernel(IdxParams p) {
 // Block-wide selection primitives (shared by the indexer and the merge).
 // =============================================================================
 
-// Top-K of keys/pos[0..n) (K < n <= R * NW * 64) by radix select over the
-// composite (key, earlier position first); exactly K entries remain, in their
-// original (position) order, at [0..K).  Entries are read into registers once
-// (wave w holds one contiguous run, 64 entries per register slot), so the
-// histogram passes and the compaction touch LDS only for the histograms.
-// Digits are taken from the offset above the smallest candidate (key - min,
-// then pmax - pos among equal keys), 8 bits at a time from the top of the
-// range actually spanned: float scores of one magnitude then spread over many
-// bins instead of piling onto the one or two bins their exponent bits share,
-// which would serialise the LDS atomics.  Each wave counts into its own
-// histogram; two histogram sets alternate so clearing the next one needs no
-// barrier of its own.  Keys are >= 1 (0 marks an empty slot) and positions
-// are distinct.  hist: 2 * NW * 256 words; wtmp: 4 * NW words.  Returns the smallest kept key: an
-// entry at a later position whose key is <= it can never enter.
+// ---- Top-K selection over register-resident candidates --------------------
+//
+// A workgroup of NW waves holds candidates in registers, R slots per lane:
+// slot s of lane l in wave w is entry w * (64 R) + 64 s + l, so entries are in
+// position order wave by wave.  Keys are >= 1 (0 marks an empty slot) and
+// positions are distinct.  The Top-K under (larger key first, then earlier
+// position) is found by radix select over the composite: digits come from the
+// offset above the smallest candidate (key - min, then pmax - pos among equal
+// keys), 8 bits at a time from the top of the range actually spanned, so float
+// scores of one magnitude spread over many bins instead of piling onto the
+// one or two bins their exponent bits share (which would serialise the LDS
+// atomics).  Each wave counts into its own histogram and two histogram sets
+// alternate, so clearing the next one needs no barrier of its own.
+
+// Which candidates are kept: key > ka, or key == kb and pmx - pos >= lo.
+struct SelRule {
+  uint32_t ka, kb, lo, pmx;
+  __device__ __forceinline__ bool keep(uint32_t k, int32_t ps) const {
+    return (k > ka) | ((k == kb) & (pmx - (uint32_t)ps >= lo));
+  }
+};
+
+// Finds the rule that keeps exactly min(K, candidates) entries (all of them
+// when there are at most K).  hist: 2 * NW * 256 words; wtmp: 8 * NW words;
+// sel: 4 words.  Ends with every wave past its last LDS read of wtmp.
 template <int NW, int R>
-__device__ __forceinline__ uint32_t block_select(uint32_t* keys, int32_t* pos, int n, int K, uint32_t* hist, int32_t* sel,
-                                 uint32_t* wtmp) {
+__device__ __forceinline__ SelRule select_rule(const uint32_t (&rk)[R], const int32_t (&rp)[R], int K,
+                                               uint32_t* hist, int32_t* sel, uint32_t* wtmp) {
   constexpr int NT = NW * 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  lds_barrier();  // entries appended by other waves are visible
-  const int chunk = (((n + NW - 1) / NW) + 63) & ~63;
-  const int wbeg = wave * chunk;
-  uint32_t rk[R];
-  int32_t rp[R];
-  uint32_t mn = 0xffffffffu, mx = 0u, pmn = 0xffffffffu, pmx = 0u;
-  // every slot is read (from a clamped index, so all reads go out at once)
-  // and masked afterwards
-#pragma unroll
-  for (int s = 0; s < R; ++s) {
-    const int i = wbeg + s * 64 + lane;
-    const int ic = min(i, n - 1);
-    const uint32_t k = keys[ic];
-    const int32_t ps = pos[ic];
-    const bool v = s * 64 < chunk && i < n;
-    rk[s] = v ? k : 0u;
-    rp[s] = ps;
-  }
+  uint32_t mn = 0xffffffffu, mx = 0u, pmn = 0xffffffffu, pmx = 0u, cnt = 0u;
 #pragma unroll
   for (int s = 0; s < R; ++s) {
     const bool v = rk[s] != 0u;
@@ -210,17 +204,18 @@ __device__ __forceinline__ uint32_t block_select(uint32_t* keys, int32_t* pos, i
     mx = max(mx, rk[s]);
     pmn = min(pmn, v ? (uint32_t)rp[s] : 0xffffffffu);
     pmx = max(pmx, v ? (uint32_t)rp[s] : 0u);
+    cnt += (uint32_t)__builtin_popcountll(ballot(v));
   }
   mn = wave_min_u32(mn);
   mx = wave_max_u32(mx);
   pmn = wave_min_u32(pmn);
   pmx = wave_max_u32(pmx);
-  uint32_t* red4 = wtmp;
   if (lane == 0) {
-    red4[4 * wave + 0] = mn;
-    red4[4 * wave + 1] = mx;
-    red4[4 * wave + 2] = pmn;
-    red4[4 * wave + 3] = pmx;
+    wtmp[8 * wave + 0] = mn;
+    wtmp[8 * wave + 1] = mx;
+    wtmp[8 * wave + 2] = pmn;
+    wtmp[8 * wave + 3] = pmx;
+    wtmp[8 * wave + 4] = cnt;
   }
   for (int i = tid; i < NW * 256; i += NT) hist[i] = 0u;
   lds_barrier();
@@ -228,15 +223,18 @@ __device__ __forceinline__ uint32_t block_select(uint32_t* keys, int32_t* pos, i
   mx = 0u;
   pmn = 0xffffffffu;
   pmx = 0u;
+  cnt = 0u;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
-    mn = min(mn, red4[4 * w + 0]);
-    mx = max(mx, red4[4 * w + 1]);
-    pmn = min(pmn, red4[4 * w + 2]);
-    pmx = max(pmx, red4[4 * w + 3]);
+    mn = min(mn, wtmp[8 * w + 0]);
+    mx = max(mx, wtmp[8 * w + 1]);
+    pmn = min(pmn, wtmp[8 * w + 2]);
+    pmx = max(pmx, wtmp[8 * w + 3]);
+    cnt += wtmp[8 * w + 4];
   }
+  if (cnt <= (uint32_t)K) return SelRule{0u, 0xffffffffu, 0u, 0u};  // keep every candidate
   // phase 0 resolves the key, phase 1 (equal keys) the position; in each,
-  // candidates lie in [lo, lo + 2^sb - 1] of the phase's value
+  // the candidates still in play lie in [lo, lo + 2^sb - 1] of the phase's value
   auto bits_of = [](uint32_t r) { return r == 0u ? 0 : 32 - __builtin_clz(r); };
   int phase = 0;
   uint32_t klo = mn, lo = mn;
@@ -315,45 +313,81 @@ __device__ __forceinline__ uint32_t block_select(uint32_t* keys, int32_t* pos, i
       sb = bits_of(pmx - pmn);
     }
   }
-  // ---- order-preserving compaction.  Waves own consecutive runs, so a wave's
-  // output offset is the count of the waves before it.
-  // keep = k > ka, or k == kb and pmx - pos >= lo (phase 0: k >= lo, and kb
-  // is a key no candidate has; empty slots, key 0, fail both)
-  const uint32_t ka = phase == 0 ? lo - 1u : klo;
-  const uint32_t kb = phase == 0 ? 0xffffffffu : klo;
-  auto keep = [&](uint32_t k, int32_t ps) { return (k > ka) | ((k == kb) & (pmx - (uint32_t)ps >= lo)); };
-  uint32_t wc = 0, kmin = 0xffffffffu;
+  // phase 0 keeps keys >= lo (kb is a key no candidate has); empty slots fail both
+  return phase == 0 ? SelRule{lo - 1u, 0xffffffffu, 0u, 0u} : SelRule{klo, klo, lo, pmx};
+}
+
+// Order-preserving output of the kept candidates: write(o, key, pos) for the
+// o-th kept entry in position order.  Returns the kept count; kmin receives
+// the smallest kept key (0xffffffff if none).  wtmp: the 8 * NW words given
+// to select_rule (words 8w+5 and 8w+6, which it leaves alone, so a wave may get
+// here while others still read its results).  Ends with a barrier.
+template <int NW, int R, typename W>
+__device__ __forceinline__ int select_output(const uint32_t (&rk)[R], const int32_t (&rp)[R], const SelRule& rule,
+                                             uint32_t* wtmp, uint32_t& kmin, W&& write) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t wc = 0, km = 0xffffffffu;
 #pragma unroll
   for (int s = 0; s < R; ++s) {
-    const bool kp = keep(rk[s], rp[s]);
+    const bool kp = (rk[s] != 0u) & rule.keep(rk[s], rp[s]);
     wc += (uint32_t)__builtin_popcountll(ballot(kp));
-    if (kp) kmin = min(kmin, rk[s]);
+    km = min(km, kp ? rk[s] : 0xffffffffu);
   }
-  kmin = wave_min_u32(kmin);
+  km = wave_min_u32(km);
   if (lane == 0) {
-    wtmp[wave] = wc;
-    wtmp[NW + wave] = kmin;
+    wtmp[8 * wave + 5] = wc;
+    wtmp[8 * wave + 6] = km;
   }
   lds_barrier();
-  int run = 0;
-  kmin = 0xffffffffu;
+  int run = 0, total = 0;
+  km = 0xffffffffu;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
-    run += (w < wave) ? (int)wtmp[w] : 0;
-    kmin = min(kmin, wtmp[NW + w]);
+    run += (w < wave) ? (int)wtmp[8 * w + 5] : 0;
+    total += (int)wtmp[8 * w + 5];
+    km = min(km, wtmp[8 * w + 6]);
   }
 #pragma unroll
   for (int s = 0; s < R; ++s) {
-    const bool kp = keep(rk[s], rp[s]);
+    const bool kp = (rk[s] != 0u) & rule.keep(rk[s], rp[s]);
     const uint64_t m = ballot(kp);
-    if (kp) {
-      const int o = run + lanes_below(m);
-      keys[o] = rk[s];
-      pos[o] = rp[s];
-    }
+    if (kp) write(run + lanes_below(m), rk[s], rp[s]);
     run += (int)__builtin_popcountll(m);
   }
   lds_barrier();
+  kmin = km;
+  return total;
+}
+
+// Top-K of keys/pos[0..n) in LDS (K < n <= R * NW * 64), in place: exactly K
+// entries remain at [0..K), in their original (position) order.  Returns the
+// smallest kept key: an entry at a later position whose key is <= it can
+// never enter.  hist: 2 * NW * 256 words; wtmp: 8 * NW words.
+template <int NW, int R>
+__device__ __forceinline__ uint32_t block_select(uint32_t* keys, int32_t* pos, int n, int K, uint32_t* hist, int32_t* sel,
+                                                 uint32_t* wtmp) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  lds_barrier();  // entries appended by other waves are visible
+  const int chunk = (((n + NW - 1) / NW) + 63) & ~63;
+  const int wbeg = wave * chunk;
+  uint32_t rk[R];
+  int32_t rp[R];
+  // every slot is read (from a clamped index, so all reads go out at once)
+  // and masked afterwards
+#pragma unroll
+  for (int s = 0; s < R; ++s) {
+    const int i = wbeg + s * 64 + lane;
+    const int ic = min(i, n - 1);
+    const uint32_t k = keys[ic];
+    rp[s] = pos[ic];
+    rk[s] = (s * 64 < chunk && i < n) ? k : 0u;
+  }
+  const SelRule rule = select_rule<NW, R>(rk, rp, K, hist, sel, wtmp);
+  uint32_t kmin;
+  select_output<NW, R>(rk, rp, rule, wtmp, kmin, [&](int o, uint32_t k, int32_t ps) {
+    keys[o] = k;
+    pos[o] = ps;
+  });
   return kmin;
 }
 
@@ -439,7 +473,7 @@ struct IdxSmem {
   int32_t cand_pos[MQ][CAP];
   uint32_t hist[2 * NW * 256];
   uint32_t wcnt[2][MQ][NW];  // per-round candidate counts of each wave (rounds alternate)
-  uint32_t red[4 * NW];
+  uint32_t red[8 * NW];
   int32_t sel[4];
   int32_t pages[SUB / PAGE + 1];  // the sub-chunk's block-table slice (-1 = invalid page); +1 when unaligned
   float wq[MQ][64];               // head weight x query scale of the group's queries
@@ -746,9 +780,11 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
           }
         } else {
           const int64_t unit = (int64_t)list_base + (int64_t)q * nl + (blockIdx.x - w0);
-          for (int i = tid; i < c; i += NT) {
-            p.list_keys[unit * p.K + i] = sm.cand_key[q][i];
-            p.list_pos[unit * p.K + i] = sm.cand_pos[q][i];
+          // slots past the count get key 0 (no candidate), so a reader may
+          // take all K slots without looking at the count
+          for (int i = tid; i < p.K; i += NT) {
+            p.list_keys[unit * p.K + i] = i < c ? sm.cand_key[q][i] : 0u;
+            if (i < c) p.list_pos[unit * p.K + i] = sm.cand_pos[q][i];
           }
           uint32_t mn = 0u, mx = 0u;
           if (c > 0) block_minmax<NW>(sm.cand_key[q], c, sm.red, mn, mx);
@@ -789,7 +825,7 @@ struct MergeSmem {
   int32_t cand_pos[MRG_CAP];
   uint32_t hist[2 * MRG_NW * 256];  // also the 2^MRG_BITS-bin histogram of pass A
   uint32_t wcnt[2 * MRG_SL * MRG_NW + 1];
-  uint32_t red[4 * MRG_NW];
+  uint32_t red[8 * MRG_NW];
   int32_t sel[4];
   int32_t lcnt[MRG_MAX_LISTS];
 };
@@ -816,20 +852,20 @@ __global__ __launch_bounds__(MRG_NT, 1) void dsa_merge_kernel(IdxParams p) {
 
   // ---- small merges keep every list slot in registers: issue all loads now
   // (slots past a list's count are ignored once the counts are known)
+  // Layout: wave w holds entries [w * chunk, (w + 1) * chunk), 64 per slot,
+  // i.e. the lists' concatenation in position order (every load is issued
+  // from a clamped index; out-of-range slots are dropped afterwards).
   const bool in_regs = total <= MRG_RS * MRG_NT;
+  const int chunk = (((total + MRG_NW - 1) / MRG_NW) + 63) & ~63;
   uint32_t rk[MRG_RS];
   int32_t rp[MRG_RS];
   if (in_regs) {
 #pragma unroll
     for (int s = 0; s < MRG_RS; ++s) {
-      const int e = s * MRG_NT + tid;
-      rk[s] = 0u;
-      rp[s] = 0;
-      if (e < total) {
-        const int c = (int)(((uint64_t)e * inv_k) >> 32), i = e - c * K;
-        rk[s] = p.list_keys[(unit0 + c) * K + i];
-        rp[s] = p.list_pos[(unit0 + c) * K + i];
-      }
+      const int e = min(wave * chunk + s * 64 + lane, total - 1);
+      const int c = (int)(((uint64_t)e * inv_k) >> 32), i = e - c * K;
+      rk[s] = p.list_keys[(unit0 + c) * K + i];
+      rp[s] = p.list_pos[(unit0 + c) * K + i];
     }
   }
 
@@ -874,80 +910,38 @@ __global__ __launch_bounds__(MRG_NT, 1) void dsa_merge_kernel(IdxParams p) {
     }
   };
 
+  const int32_t* bt = p.block_table + (int64_t)max(seq, 0) * p.max_blocks;
+  int32_t* out = p.indices + (int64_t)t * K;
+  if (in_regs) {
+    // ---- register path: drop out-of-range slots and keys below lb (slots
+    // past a list's count hold key 0), select straight from the registers
+#pragma unroll
+    for (int s = 0; s < MRG_RS; ++s) {
+      const int e = wave * chunk + s * 64 + lane;
+      if (s * 64 >= chunk || e >= total || rk[s] < lb) rk[s] = 0u;
+    }
+    const SelRule rule = select_rule<MRG_NW, MRG_RS>(rk, rp, K, sm.hist, sm.sel, sm.red);
+    uint32_t kmin;
+    // kept positions go to LDS in order; the page lookups below are then
+    // independent loads instead of one dependent load per register slot
+    const int n = select_output<MRG_NW, MRG_RS>(rk, rp, rule, sm.red, kmin,
+                                                [&](int o, uint32_t, int32_t ps) { sm.cand_pos[o] = ps; });
+    for (int i = tid; i < K; i += MRG_NT) {
+      int v = -1;
+      if (i < n) {
+        const int ps = sm.cand_pos[i];
+        v = bt[ps >> 6] * PAGE + (ps & 63);
+      }
+      out[i] = v;
+    }
+    return;
+  }
+
   uint32_t ka[MRG_SL], kb2[MRG_SL];
   int32_t pa[MRG_SL], pb2[MRG_SL];
   int cnt = 0;
   bool streamed = true;
-  if (in_regs && mx >= lb && lb != mx) {
-    // ---- register path: drop slots past the counts and keys below lb
-#pragma unroll
-    for (int s = 0; s < MRG_RS; ++s) {
-      const int e = s * MRG_NT + tid;
-      const int c = min((int)(((uint64_t)e * inv_k) >> 32), nl - 1), i = e - c * K;
-      if (e >= total || i >= sm.lcnt[c] || rk[s] < lb) rk[s] = 0u;
-    }
-    const int cp = __builtin_clz(lb ^ mx);
-    const int wb = min(MRG_BITS, 32 - cp);
-    const int shift = 32 - cp - wb;
-    const uint32_t pref = cp == 0 ? 0u : (lb & ~(0xffffffffu >> cp));
-    for (int i = tid; i < (1 << MRG_BITS); i += MRG_NT) sm.hist[i] = 0u;
-    lds_barrier();
-#pragma unroll
-    for (int s = 0; s < MRG_RS; ++s)
-      if (rk[s] != 0u) atomicAdd(&sm.hist[(rk[s] >> shift) & ((1u << wb) - 1u)], 1u);
-    lds_barrier();
-    const int nb = 1 << wb;
-    uint32_t c4[4], sum = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int bin = nb - 1 - (4 * tid + j);
-      c4[j] = bin >= 0 ? sm.hist[bin] : 0u;
-      sum += c4[j];
-    }
-    const uint32_t winc = wave_incl_scan(sum);
-    if (lane == 63) sm.red[wave] = winc;
-    lds_barrier();
-    uint32_t before = 0, all = 0;
-#pragma unroll
-    for (int w = 0; w < MRG_NW; ++w) {
-      before += (w < wave) ? sm.red[w] : 0u;
-      all += sm.red[w];
-    }
-    const uint32_t excl = before + winc - sum;
-    if (tid == 0) sm.sel[0] = -1;
-    lds_barrier();
-    if (all > (uint32_t)K && excl < (uint32_t)K && (uint32_t)K <= excl + sum) {
-      uint32_t acc = excl;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (acc < (uint32_t)K && acc + c4[j] >= (uint32_t)K) {
-          sm.sel[0] = nb - 1 - (4 * tid + j);
-          sm.sel[2] = (int)(acc + c4[j]);
-        }
-        acc += c4[j];
-      }
-    }
-    lds_barrier();
-    const int bsel = sm.sel[0];
-    const int n_keep = bsel >= 0 ? sm.sel[2] : (int)all;
-    const uint32_t thr = (bsel >= 0 ? max(lb, pref | ((uint32_t)bsel << shift)) : lb) - 1u;
-    lds_barrier();
-    if (n_keep <= MRG_CAP) {
-      streamed = false;
-#pragma unroll
-      for (int s0 = 0; s0 < MRG_RS; s0 += MRG_SL) {
-        uint32_t kk[MRG_SL];
-        int32_t pp[MRG_SL];
-#pragma unroll
-        for (int s = 0; s < MRG_SL; ++s) {
-          kk[s] = rk[s0 + s];
-          pp[s] = rp[s0 + s];
-        }
-        // slot s of this call is entry (s0 + s) * NT + tid: the order is kept
-        cnt = block_append<MRG_NW, MRG_SL>(sm.cand_key, sm.cand_pos, cnt, thr, kk, pp, sm.wcnt);
-      }
-    }
-  } else if (!in_regs && mx >= lb) {
+  if (mx >= lb) {
     // ---- pass A: histogram of the digit below the common prefix of [lb, mx]
     const int cp = (lb == mx) ? 32 : __builtin_clz(lb ^ mx);
     const int wb = min(MRG_BITS, 32 - cp);
@@ -1056,8 +1050,6 @@ __global__ __launch_bounds__(MRG_NT, 1) void dsa_merge_kernel(IdxParams p) {
     block_select<MRG_NW, MRG_CAP / MRG_NT>(sm.cand_key, sm.cand_pos, cnt, K, sm.hist, sm.sel, sm.red);
     cnt = K;
   }
-  const int32_t* bt = p.block_table + (int64_t)max(seq, 0) * p.max_blocks;
-  int32_t* out = p.indices + (int64_t)t * K;
   for (int i = tid; i < K; i += MRG_NT) {
     int v = -1;
     if (i < cnt) {

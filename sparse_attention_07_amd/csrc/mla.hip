@@ -23,8 +23,9 @@
 //    accumulates O^T += C^T P^T, reading C^T with the gfx950 LDS transpose
 //    read (ds_read_b64_tr_b16) and P^T with plain 16-byte reads;
 //  * the O rescale is skipped for a wave when no head's running max moved;
-//  * with several splits, partial (O, m, l) go to the workspace and a small
-//    kernel merges them with log-sum-exp weights.
+//  * with several splits, each split stores its normalised partial output
+//    O/l as fp16 (|O/l| is bounded by the largest value entry) plus (m, l) in
+//    fp32, and a small kernel merges them with log-sum-exp weights.
 #include "dsa_device.h"
 #include "dsa_params.h"
 
@@ -231,9 +232,9 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
 #pragma unroll
   for (int nt = 0; nt < NW; ++nt) {
     const int h = 16 * nt + n16;
+    const float l_tot = sm.lfin[h];
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (p.S == 1) {
-      const float l_tot = sm.lfin[h];
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
       uint16_t* orow = p.out + ((int64_t)t * H + h) * VDIM;
 #pragma unroll
       for (int vt = 0; vt < VT; ++vt) {
@@ -244,9 +245,14 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
       }
     } else {
       const int64_t rowi = ((int64_t)t * p.S + s) * H + h;
-      float* prow = p.part_o + rowi * VDIM;
+      _Float16* prow = p.part_o + rowi * VDIM;
 #pragma unroll
-      for (int vt = 0; vt < VT; ++vt) *reinterpret_cast<v4f*>(prow + (wave * VT + vt) * 16 + 4 * g4) = o[vt][nt];
+      for (int vt = 0; vt < VT; ++vt) {
+        _Float16 h4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h4[i] = (_Float16)(o[vt][nt][i] * inv);
+        *reinterpret_cast<uint2*>(prow + (wave * VT + vt) * 16 + 4 * g4) = __builtin_bit_cast(uint2, h4);
+      }
     }
   }
   if (p.S > 1 && tid < H) {
@@ -256,7 +262,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
   }
 }
 
-// Merge S partial results per (query, head): out = sum_s e^(m_s-M) O_s / sum_s e^(m_s-M) l_s
+// Merge S partial results per (query, head), with O_s = l_s * (O/l)_s:
+// out = sum_s e^(m_s-M) l_s (O/l)_s / sum_s e^(m_s-M) l_s
 __global__ __launch_bounds__(128) void dsa_mla_combine_kernel(MlaParams p) {
   const int th = blockIdx.x;  // t * H + h
   const int t = th / p.H, h = th % p.H;
@@ -270,10 +277,13 @@ __global__ __launch_bounds__(128) void dsa_mla_combine_kernel(MlaParams p) {
       const int64_t rowi = ((int64_t)t * p.S + s) * p.H + h;
       const float ms = p.part_ml[rowi * 2], ls = p.part_ml[rowi * 2 + 1];
       if (ms == -INFINITY) continue;
-      const float wgt = exp2f(ms - M);
-      L += wgt * ls;
-      const v4f ov = *reinterpret_cast<const v4f*>(p.part_o + rowi * VDIM + v);
-      acc += wgt * ov;
+      const float wgt = exp2f(ms - M) * ls;
+      L += wgt;
+      const uint2 raw = *reinterpret_cast<const uint2*>(p.part_o + rowi * VDIM + v);
+      _Float16 h4[4];
+      __builtin_memcpy(h4, &raw, 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += wgt * (float)h4[i];
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
