@@ -78,7 +78,11 @@ int device_cus() {
 // same value must be used for sizing and for the call.
 IdxPlan plan_indexer(const dsa_indexer_args* a, int K, size_t base, int nwg) {
   IdxPlan pl;
-  pl.MQ = a->max_q_per_seq >= 3 ? 4 : a->max_q_per_seq;
+  // Adjacent queries of one sequence are scored together (sharing each key
+  // load) only when there are many of them (chunked prefill): for a handful
+  // of speculative queries the doubled per-key work costs more than the
+  // extra key reads save.
+  pl.MQ = a->max_q_per_seq >= 8 ? 2 : 1;
   pl.nwg = nwg;
   const int64_t maxlen = (int64_t)a->max_blocks * DSA_PAGE_TOKENS;
   const int64_t T = a->T;

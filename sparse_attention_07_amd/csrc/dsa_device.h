@@ -24,7 +24,6 @@ constexpr int MIN_SLICE = 4096;       // smallest key slice an indexer workgroup
 // key-space partition, so slices that hold more segments get fewer keys.
 constexpr int SEG_COST = 2560;
 constexpr int SUB = 65536;            // keys whose page ids the indexer stages in LDS at once
-constexpr int MRG_MAX_LISTS = 1024;   // most candidate lists of one query the merge accepts
 
 // Order-preserving map fp32 -> uint32 (a < b  <=>  key(a) < key(b)); -0 maps
 // like +0.  Key 0 is below every finite value and marks "no candidate".

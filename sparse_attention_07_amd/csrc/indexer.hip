@@ -460,7 +460,7 @@ __device__ __forceinline__ void block_minmax(const uint32_t* keys, int n, uint32
 // =============================================================================
 template <int MQ>
 struct CapOf {
-  static constexpr int value = MQ == 1 ? 8192 : (MQ == 2 ? 4096 : 3072);
+  static constexpr int value = MQ == 1 ? 8192 : 4096;
 };
 
 template <int NW, int MQ>
@@ -469,6 +469,7 @@ struct IdxSmem {
   static constexpr int NT = NW * 64;
   static constexpr int R = CAP / NT;  // candidate entries per thread in a selection
   static_assert(CAP % NT == 0, "selection register slots");
+  static_assert(CAP >= KMAX + ROUND, "after a cut to K the buffer holds one more round");
   uint32_t cand_key[MQ][CAP];
   int32_t cand_pos[MQ][CAP];
   uint32_t hist[2 * NW * 256];
@@ -715,25 +716,45 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
         }
         // append the keys above each query's bound: a wave's groups are
         // consecutive positions and waves follow each other, so a wave's
-        // offset is the count of the waves before it (one barrier per round)
-#pragma unroll
-        for (int q = 0; q < MQ; ++q) {
+        // offset is the count of the waves before it (one barrier per round).
+        // When the round's keys would not fit, the buffer is cut to K first
+        // (raising the bound) and the round is counted again.
+        auto count_round = [&](int q) {
           uint32_t wc = 0;
 #pragma unroll
           for (int s = 0; s < GPW; ++s) wc += (uint32_t)__builtin_popcountll(ballot(lane < 16 && kk[q][s] > thr[q]));
           if (lane == 0) sm.wcnt[rpar][q][wave] = wc;
-        }
+        };
+#pragma unroll
+        for (int q = 0; q < MQ; ++q) count_round(q);
         lds_barrier();
 #pragma unroll
         for (int q = 0; q < MQ; ++q) {
           if (q < nq) {
-            int o = cnt[q], tot = 0;
+            int pre = 0, tot = 0;
 #pragma unroll
             for (int w = 0; w < NW; ++w) {
               const int c = (int)sm.wcnt[rpar][q][w];
-              o += (w < wave) ? c : 0;
+              pre += (w < wave) ? c : 0;
               tot += c;
             }
+            if (cnt[q] + tot > CAP) {
+              // cnt[q] > CAP - ROUND >= K, so the select has work to do
+              thr[q] = max(thr[q], block_select<NW, R>(sm.cand_key[q], sm.cand_pos[q], cnt[q], p.K, sm.hist,
+                                                       sm.sel, sm.red));
+              cnt[q] = p.K;
+              count_round(q);  // every wave read the old counts before the select's first barrier
+              lds_barrier();
+              pre = 0;
+              tot = 0;
+#pragma unroll
+              for (int w = 0; w < NW; ++w) {
+                const int c = (int)sm.wcnt[rpar][q][w];
+                pre += (w < wave) ? c : 0;
+                tot += c;
+              }
+            }
+            int o = cnt[q] + pre;
 #pragma unroll
             for (int s = 0; s < GPW; ++s) {
               const bool t = lane < 16 && kk[q][s] > thr[q];
@@ -746,11 +767,6 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
               o += (int)__builtin_popcountll(m);
             }
             cnt[q] += tot;
-            if (cnt[q] > CAP - ROUND) {
-              thr[q] = max(thr[q], block_select<NW, R>(sm.cand_key[q], sm.cand_pos[q], cnt[q], p.K, sm.hist,
-                                                       sm.sel, sm.red));
-              cnt[q] = p.K;
-            }
           }
         }
         rpar ^= 1;
@@ -804,32 +820,28 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
 // Merge kernel: one workgroup per query whose keys span several slices.
 //
 // Every full list (K entries) is itself the Top-K of its slice, so the largest
-// list minimum lb bounds the final K-th key from below, and keys below lb are
-// out.  Pass A histograms the 11 bits that follow the common prefix of
-// [lb, max key] over all list entries in global memory and finds the bin that
-// holds the K-th key; pass B appends (in position order) only the entries at
-// or above that bin; a small LDS select then finishes.  If that bin is too
-// heavy for LDS (e.g. exact ties), the lists are streamed through the
-// filter-and-select loop instead.
+// list minimum lb bounds the final K-th key from below and keys below lb are
+// out.  The lists' concatenation (already in position order; slots past a
+// list's count hold key 0) is read in chunks of MRG_RS entries per lane, wide
+// and all at once.  A chunk's entries above the running bound are appended in
+// order to an LDS buffer; when they would not fit, the buffer is first cut to
+// its Top-K, which raises the bound.  A query whose lists fit one chunk (the
+// common case) selects straight from registers.
 // =============================================================================
 constexpr int MRG_NW = 8;
 constexpr int MRG_NT = MRG_NW * 64;
-constexpr int MRG_SL = 8;                       // entries per thread per batch
-constexpr int MRG_RS = 32;                      // entries per thread when a query's lists fit in registers
-constexpr int MRG_BATCH = MRG_SL * MRG_NT;      // 4096
-constexpr int MRG_CAP = 16384;
-constexpr int MRG_BITS = 11;
+constexpr int MRG_RS = 32;                  // entries per lane per chunk
+constexpr int MRG_CHUNK = MRG_RS * MRG_NT;  // 16384
+constexpr int MRG_CAP = 16384;              // LDS candidate buffer
 
 struct MergeSmem {
   uint32_t cand_key[MRG_CAP];
   int32_t cand_pos[MRG_CAP];
-  uint32_t hist[2 * MRG_NW * 256];  // also the 2^MRG_BITS-bin histogram of pass A
-  uint32_t wcnt[2 * MRG_SL * MRG_NW + 1];
+  uint32_t hist[2 * MRG_NW * 256];
   uint32_t red[8 * MRG_NW];
   int32_t sel[4];
-  int32_t lcnt[MRG_MAX_LISTS];
 };
-static_assert(MRG_NW * 256 >= (1 << MRG_BITS), "pass-A histogram fits the radix histogram space");
+static_assert(MRG_CAP >= 2 * KMAX, "the buffer cut to K takes a chunk cut to K");
 
 __global__ __launch_bounds__(MRG_NT, 1) void dsa_merge_kernel(IdxParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -846,210 +858,103 @@ __global__ __launch_bounds__(MRG_NT, 1) void dsa_merge_kernel(IdxParams p) {
   const int64_t unit0 = (int64_t)gr[G_LIST] + (int64_t)q * nl;
   const int K = p.K;
   const int total = nl * K;
-  // e / K as a multiply-high by ceil(2^32 / K): exact while e * K < 2^32
-  // (here e < nl * K <= 256 * 2048)
-  const uint64_t inv_k = (0x100000000ull + K - 1) / K;
+  const int nchunks = (total + MRG_CHUNK - 1) / MRG_CHUNK;
+  const uint32_t* keys0 = p.list_keys + unit0 * K;
+  const int32_t* pos0 = p.list_pos + unit0 * K;
 
-  // ---- small merges keep every list slot in registers: issue all loads now
-  // (slots past a list's count are ignored once the counts are known)
-  // Layout: wave w holds entries [w * chunk, (w + 1) * chunk), 64 per slot,
-  // i.e. the lists' concatenation in position order (every load is issued
-  // from a clamped index; out-of-range slots are dropped afterwards).
-  const bool in_regs = total <= MRG_RS * MRG_NT;
-  const int chunk = (((total + MRG_NW - 1) / MRG_NW) + 63) & ~63;
+  // Chunk layout: wave w holds entries [w * wch, (w + 1) * wch) of the chunk,
+  // 64 per slot; every load comes from a clamped index and out-of-range slots
+  // are dropped afterwards.
   uint32_t rk[MRG_RS];
   int32_t rp[MRG_RS];
-  if (in_regs) {
+  auto load_chunk = [&](int c) {
+    const int cb = c * MRG_CHUNK;
+    const int cn = min(MRG_CHUNK, total - cb);
+    const int wch = (((cn + MRG_NW - 1) / MRG_NW) + 63) & ~63;
 #pragma unroll
     for (int s = 0; s < MRG_RS; ++s) {
-      const int e = min(wave * chunk + s * 64 + lane, total - 1);
-      const int c = (int)(((uint64_t)e * inv_k) >> 32), i = e - c * K;
-      rk[s] = p.list_keys[(unit0 + c) * K + i];
-      rp[s] = p.list_pos[(unit0 + c) * K + i];
+      const int e = cb + min(wave * wch + s * 64 + lane, cn - 1);
+      rk[s] = keys0[e];
+      rp[s] = pos0[e];
     }
-  }
+    return wch;
+  };
+  int wch = load_chunk(0);
 
-  // ---- list sizes to LDS; lb = largest minimum over full lists; largest key
-  uint32_t lb = 1u, mx = 0u;
+  // ---- lb = largest minimum over full lists
+  uint32_t lb = 1u;
   for (int c = tid; c < nl; c += MRG_NT) {
-    const int n_c = p.list_cnt[unit0 + c];
-    sm.lcnt[c] = n_c;
-    if (n_c > 0) mx = max(mx, p.list_mm[2 * (unit0 + c) + 1]);
-    if (n_c == K) lb = max(lb, p.list_mm[2 * (unit0 + c)]);
+    if (p.list_cnt[unit0 + c] == K) lb = max(lb, p.list_mm[2 * (unit0 + c)]);
   }
   lb = wave_max_u32(lb);
-  mx = wave_max_u32(mx);
-  if (lane == 0) {
-    sm.red[wave] = lb;
-    sm.red[MRG_NW + wave] = mx;
-  }
+  if (lane == 0) sm.red[wave] = lb;
   lds_barrier();
   lb = 1u;
-  mx = 0u;
 #pragma unroll
-  for (int w = 0; w < MRG_NW; ++w) {
-    lb = max(lb, sm.red[w]);
-    mx = max(mx, sm.red[MRG_NW + w]);
-  }
+  for (int w = 0; w < MRG_NW; ++w) lb = max(lb, sm.red[w]);
   lds_barrier();
-
-  // entry e (list e / K, slot e % K), in list order = position order
-  auto load = [&](int b0, uint32_t (&kk)[MRG_SL], int32_t (&pp)[MRG_SL], bool with_pos) {
-#pragma unroll
-    for (int s = 0; s < MRG_SL; ++s) {
-      const int e = b0 + s * MRG_NT + tid;
-      kk[s] = 0u;
-      pp[s] = 0;
-      if (e < total) {
-        const int c = (int)(((uint64_t)e * inv_k) >> 32), i = e - c * K;
-        if (i < sm.lcnt[c]) {
-          kk[s] = p.list_keys[(unit0 + c) * K + i];
-          if (with_pos) pp[s] = p.list_pos[(unit0 + c) * K + i];
-        }
-      }
-    }
-  };
 
   const int32_t* bt = p.block_table + (int64_t)max(seq, 0) * p.max_blocks;
   int32_t* out = p.indices + (int64_t)t * K;
-  if (in_regs) {
-    // ---- register path: drop out-of-range slots and keys below lb (slots
-    // past a list's count hold key 0), select straight from the registers
-#pragma unroll
-    for (int s = 0; s < MRG_RS; ++s) {
-      const int e = wave * chunk + s * 64 + lane;
-      if (s * 64 >= chunk || e >= total || rk[s] < lb) rk[s] = 0u;
-    }
-    const SelRule rule = select_rule<MRG_NW, MRG_RS>(rk, rp, K, sm.hist, sm.sel, sm.red);
-    uint32_t kmin;
-    // kept positions go to LDS in order; the page lookups below are then
-    // independent loads instead of one dependent load per register slot
-    const int n = select_output<MRG_NW, MRG_RS>(rk, rp, rule, sm.red, kmin,
-                                                [&](int o, uint32_t, int32_t ps) { sm.cand_pos[o] = ps; });
-    for (int i = tid; i < K; i += MRG_NT) {
-      int v = -1;
-      if (i < n) {
-        const int ps = sm.cand_pos[i];
-        v = bt[ps >> 6] * PAGE + (ps & 63);
-      }
-      out[i] = v;
-    }
-    return;
-  }
-
-  uint32_t ka[MRG_SL], kb2[MRG_SL];
-  int32_t pa[MRG_SL], pb2[MRG_SL];
+  uint32_t thr = lb - 1u;  // keep keys > thr
   int cnt = 0;
-  bool streamed = true;
-  if (mx >= lb) {
-    // ---- pass A: histogram of the digit below the common prefix of [lb, mx]
-    const int cp = (lb == mx) ? 32 : __builtin_clz(lb ^ mx);
-    const int wb = min(MRG_BITS, 32 - cp);
-    const int shift = 32 - cp - wb;
-    const uint32_t pref = cp == 0 ? 0u : (lb & ~(0xffffffffu >> cp));
-    for (int i = tid; i < (1 << MRG_BITS); i += MRG_NT) sm.hist[i] = 0u;
-    lds_barrier();
-    if (wb > 0) {
-      load(0, ka, pa, false);
-      for (int b0 = 0; b0 < total; b0 += MRG_BATCH) {
-        uint32_t cur[MRG_SL];
+  for (int c = 0; c < nchunks; ++c) {
+    if (c > 0) wch = load_chunk(c);
+    const int cn = min(MRG_CHUNK, total - c * MRG_CHUNK);
+    auto mask = [&]() {
 #pragma unroll
-        for (int s = 0; s < MRG_SL; ++s) cur[s] = ka[s];
-        load(b0 + MRG_BATCH, ka, pa, false);
-#pragma unroll
-        for (int s = 0; s < MRG_SL; ++s)
-          if (cur[s] >= lb) atomicAdd(&sm.hist[(cur[s] >> shift) & ((1u << wb) - 1u)], 1u);
+      for (int s = 0; s < MRG_RS; ++s) {
+        const int e = wave * wch + s * 64 + lane;
+        if (s * 64 >= wch || e >= cn || rk[s] <= thr) rk[s] = 0u;
       }
+    };
+    mask();
+    if (nchunks == 1) {
+      // ---- single chunk: select straight from the registers
+      const SelRule rule = select_rule<MRG_NW, MRG_RS>(rk, rp, K, sm.hist, sm.sel, sm.red);
+      uint32_t kmin;
+      cnt = select_output<MRG_NW, MRG_RS>(rk, rp, rule, sm.red, kmin,
+                                          [&](int o, uint32_t, int32_t ps) { sm.cand_pos[o] = ps; });
+      break;
     }
-    lds_barrier();
-    // bin B holding the K-th largest: count(> B) < K <= count(>= B); each
-    // thread owns 4 consecutive bins, descending from the top
-    uint32_t thr_key = lb;  // keep keys >= thr_key
-    int n_keep = 0;
-    if (wb > 0) {
-      const int nb = 1 << wb;
-      uint32_t c4[4], sum = 0;
+    // survivors of this chunk (word 8w+7 of red is used by nothing else)
+    auto count_valid = [&]() {
+      uint32_t wc = 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int bin = nb - 1 - (4 * tid + j);
-        c4[j] = bin >= 0 ? sm.hist[bin] : 0u;
-        sum += c4[j];
-      }
-      const uint32_t winc = wave_incl_scan(sum);
-      if (lane == 63) sm.red[wave] = winc;
+      for (int s = 0; s < MRG_RS; ++s) wc += (uint32_t)__builtin_popcountll(ballot(rk[s] != 0u));
+      if (lane == 0) sm.red[8 * wave + 7] = wc;
       lds_barrier();
-      uint32_t before = 0, all = 0;
+      int n = 0;
 #pragma unroll
-      for (int w = 0; w < MRG_NW; ++w) {
-        before += (w < wave) ? sm.red[w] : 0u;
-        all += sm.red[w];
-      }
-      const uint32_t excl = before + winc - sum;
-      if (tid == 0) {
-        sm.sel[0] = -1;
-        sm.sel[1] = (int)all;
-      }
-      lds_barrier();
-      if (all > (uint32_t)K && excl < (uint32_t)K && (uint32_t)K <= excl + sum) {
-        uint32_t acc = excl;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (acc < (uint32_t)K && acc + c4[j] >= (uint32_t)K) {
-            sm.sel[0] = nb - 1 - (4 * tid + j);
-            sm.sel[2] = (int)(acc + c4[j]);  // entries at or above the bin
-          }
-          acc += c4[j];
-        }
-      }
-      lds_barrier();
-      const int bsel = sm.sel[0];
-      if (bsel >= 0) {
-        thr_key = max(lb, pref | ((uint32_t)bsel << shift));
-        n_keep = sm.sel[2];
-      } else {
-        n_keep = sm.sel[1];  // at most K entries reach lb: keep them all
-      }
-      lds_barrier();
-    } else {
-      n_keep = MRG_CAP + 1;  // one key value only: decided by position, stream
+      for (int w = 0; w < MRG_NW; ++w) n += (int)sm.red[8 * w + 7];
+      return n;
+    };
+    int tot = count_valid();
+    if (cnt + tot > MRG_CAP && cnt > K) {
+      // cut the buffer to its Top-K (raising the bound), then drop the chunk's
+      // entries that no longer pass
+      thr = max(thr, block_select<MRG_NW, MRG_CAP / MRG_NT>(sm.cand_key, sm.cand_pos, cnt, K, sm.hist, sm.sel,
+                                                             sm.red));
+      cnt = K;
+      mask();
+      tot = count_valid();
     }
-    // ---- pass B: append the kept entries in order (fits LDS by construction)
-    if (n_keep <= MRG_CAP - MRG_BATCH) {
-      streamed = false;
-      const uint32_t thr = thr_key - 1u;
-      load(0, ka, pa, true);
-      for (int b0 = 0; b0 < total; b0 += 2 * MRG_BATCH) {
-        load(b0 + MRG_BATCH, kb2, pb2, true);
-        cnt = block_append<MRG_NW, MRG_SL>(sm.cand_key, sm.cand_pos, cnt, thr, ka, pa, sm.wcnt);
-        load(b0 + 2 * MRG_BATCH, ka, pa, true);
-        cnt = block_append<MRG_NW, MRG_SL>(sm.cand_key, sm.cand_pos, cnt, thr, kb2, pb2, sm.wcnt);
-      }
-    }
+    // append in order: every valid entry, or only the chunk's own Top-K when
+    // that does not fit (cnt <= K then, and cnt + K <= MRG_CAP)
+    const SelRule rule = cnt + tot > MRG_CAP ? select_rule<MRG_NW, MRG_RS>(rk, rp, K, sm.hist, sm.sel, sm.red)
+                                             : SelRule{0u, 0xffffffffu, 0u, 0u};
+    uint32_t kmin;
+    cnt += select_output<MRG_NW, MRG_RS>(rk, rp, rule, sm.red, kmin,
+                                         [&](int o, uint32_t k, int32_t ps) {
+                                           sm.cand_key[cnt + o] = k;
+                                           sm.cand_pos[cnt + o] = ps;
+                                         });
   }
-  if (streamed) {
-    // ---- fallback: stream every entry >= lb through filter-and-select
-    uint32_t thr = lb - 1u;
-    cnt = 0;
-    load(0, ka, pa, true);
-    for (int b0 = 0; b0 < total; b0 += 2 * MRG_BATCH) {
-      load(b0 + MRG_BATCH, kb2, pb2, true);
-      cnt = block_append<MRG_NW, MRG_SL>(sm.cand_key, sm.cand_pos, cnt, thr, ka, pa, sm.wcnt);
-      if (cnt > MRG_CAP - MRG_BATCH) {
-        thr = max(thr, block_select<MRG_NW, MRG_CAP / MRG_NT>(sm.cand_key, sm.cand_pos, cnt, K, sm.hist, sm.sel, sm.red));
-        cnt = K;
-      }
-      load(b0 + 2 * MRG_BATCH, ka, pa, true);
-      cnt = block_append<MRG_NW, MRG_SL>(sm.cand_key, sm.cand_pos, cnt, thr, kb2, pb2, sm.wcnt);
-      if (cnt > MRG_CAP - MRG_BATCH) {
-        thr = max(thr, block_select<MRG_NW, MRG_CAP / MRG_NT>(sm.cand_key, sm.cand_pos, cnt, K, sm.hist, sm.sel, sm.red));
-        cnt = K;
-      }
-    }
-  }
-  if (cnt > K) {
+  if (nchunks > 1 && cnt > K) {
     block_select<MRG_NW, MRG_CAP / MRG_NT>(sm.cand_key, sm.cand_pos, cnt, K, sm.hist, sm.sel, sm.red);
     cnt = K;
   }
+  // ---- output: kept positions (in LDS, in order) to pool slots
   for (int i = tid; i < K; i += MRG_NT) {
     int v = -1;
     if (i < cnt) {
@@ -1075,11 +980,7 @@ static hipError_t launch_indexer_t(const IdxParams& p, int grid, hipStream_t st)
 
 template <int DT, int D, int HT>
 static hipError_t launch_indexer_mq(const IdxParams& p, int grid, hipStream_t st) {
-  switch (p.MQ) {
-    case 1: return launch_indexer_t<DT, D, HT, 1, 8>(p, grid, st);
-    case 2: return launch_indexer_t<DT, D, HT, 2, 8>(p, grid, st);
-    default: return launch_indexer_t<DT, D, HT, 4, 4>(p, grid, st);
-  }
+  return p.MQ == 1 ? launch_indexer_t<DT, D, HT, 1, 8>(p, grid, st) : launch_indexer_t<DT, D, HT, 2, 8>(p, grid, st);
 }
 
 hipError_t launch_indexer(const IdxParams& p, int is_fp8, int D, int grid, bool need_merge, hipStream_t st) {

@@ -56,6 +56,12 @@ def test_speculative_multi_query_groups():
     run_case(spec("spec_mix", lens=[3000, 9000, 20000, 130], queries_per_seq=[1, 4, 2, 3], seed=7))
 
 
+def test_many_queries_per_sequence_paired_groups():
+    # 8 or more queries of one sequence are scored two at a time; odd counts
+    # leave a single-query group, and the sequences span several slices
+    run_case(spec("spec_many", lens=[30000, 700, 12000], queries_per_seq=[9, 1, 8], seed=29))
+
+
 @pytest.mark.parametrize("chunk", [0, 1, 2])
 def test_prefill_chunks_causal(chunk):
     run_case(spec("prefill_small", prefill=(6000, 2048), K=512, H=64, seed=11), prefill_chunk=chunk,
