@@ -7,7 +7,9 @@ benchmark times, with sampled queries checked one by one."""
 import pytest
 import torch
 
-from gpu_cases import check_queries, say
+from dsa_check import check_outputs
+from gpu_cases import bits16, check_queries, say
+from oracle import dsa_oracle as O
 from sparse_attention_07_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -119,3 +121,27 @@ def test_all_scores_tied_picks_lowest_positions():
         expect = (bt[t, pos // 64] * 64 + pos % 64).to(torch.int32)
         assert torch.equal(idx[t, :k], expect)
         assert (idx[t, k:] == -1).all()
+
+
+def test_mla_score_outrun_takes_exact_max_path():
+    # one head's logit on a row in the second tile of a split exceeds that
+    # split's first-tile maximum by far more than the exponent slack of the
+    # 128-head kernel, which then recomputes the split with exact maxima
+    sp = spec("outrun", lens=[4096], H=128, K=2048, seed=31)
+    case = synth.build_case(sp, device=DEV)
+    bt = case.block_table[0].cpu()
+    pos = torch.arange(sp.K)
+    idx = (bt[pos // 64] * 64 + pos % 64).to(torch.int32).view(1, -1).to(DEV)
+    h0, j = 5, 300
+    slot = int(idx[0, j])
+    case.kv_pool[slot] = (3.0 * case.q[0, h0].float()).to(torch.bfloat16)
+    out = dsa.sparse_mla_attn(case.q, case.kv_pool, idx, sp.scale)
+    torch.cuda.synchronize()
+    qh = O.bf16_to_f64(bits16(case.q[0]))
+    rows = O.bf16_to_f64(bits16(case.kv_pool[idx[0].long()]))
+    ref = O.sparse_mla(qh, rows, sp.scale)
+    got = out[0].float().cpu().numpy()
+    assert abs(ref[h0] - rows[j, :512]).max() < 1e-3  # the planted row dominates head h0
+    ok, msg = check_outputs(got, ref)
+    say("  outrun case:", msg)
+    assert ok, msg
