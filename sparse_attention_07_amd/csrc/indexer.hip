@@ -12,27 +12,31 @@
 //
 // Design for CDNA4 (not the pages' accelerator):
 //  * a planning kernel turns (seq_lens, q_seq, q_visible) into query groups
-//    (adjacent queries of one sequence, up to MQ) and equal-size key chunks;
-//  * one persistent workgroup per CU walks chunks.  Each wave streams 16-key
-//    slices of 64-token pages straight into MFMA operand registers (per lane
-//    64 contiguous bytes per key per load pair) with a 4-deep register prefetch
-//    ring; page ids come from an LDS copy of the chunk's block-table slice, so
-//    no load in the prefetch chain depends on another;
+//    (adjacent queries of one sequence, up to MQ) laid end to end in one key
+//    space, each charged a fixed extra weight for its per-segment cost, and
+//    cuts that space into one equal slice per CU (stream-K): every workgroup
+//    streams the same amount, whatever the sequence lengths;
+//  * each wave streams 16-key slices of 64-token pages straight into MFMA
+//    operand registers (per lane 64 contiguous bytes per key per load pair)
+//    through an 8-deep register prefetch ring; page ids come from an LDS copy
+//    of the segment's block-table slice, so no load in the ring depends on
+//    another;
 //  * MFMA M = 16 indexer heads per tile, N = 16 keys, K = head dim
 //    (FP8: one 16x16x128 e4m3 MFMA per head tile; BF16: 16x16x32 steps);
 //    ReLU (an integer max on the bit pattern) and the head-weighted reduction
 //    run on the accumulators, then a 2-step permlane butterfly sums the four
 //    head groups of the tile;
-//  * selection streams: each 1024-key round's scores are filtered against a
-//    lower bound of the current K-th score into an LDS candidate buffer; when
-//    the buffer fills, a block-wide 8-bit radix select (ties broken by position
-//    through a 64-bit composite key) cuts it back to K.  Candidates stay in
-//    position order throughout;
-//  * a query whose keys span several chunks gets one list per chunk; a merge
+//  * selection streams: after each 1024-key round the keys above the current
+//    bound (a lower bound of the K-th score) are appended, in position order,
+//    to an LDS candidate buffer (one barrier per round: a wave's offset is
+//    the count of the waves before it); only when a round would not fit is
+//    the buffer cut back to K by a block radix select, which raises the
+//    bound;
+//  * a query whose keys span several slices gets one list per slice; a merge
 //    kernel (after a kernel boundary, so no cross-workgroup fences) starts from
 //    the largest minimum key of any full list -- that list alone already holds
-//    K entries at or above it -- filters the lists' entries against it, and
-//    selects the final K.
+//    K entries at or above it -- and selects the final K from the lists held
+//    in registers.
 #include "dsa_device.h"
 #include "dsa_params.h"
 
