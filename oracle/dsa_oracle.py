@@ -24,6 +24,9 @@ Readings where the pages are silent (each also listed in the design notes):
   * one index key per token, shared by all indexer heads; w is per query token;
   * FP8 data is OCP e4m3fn codes times an fp32 scale (per token for keys, per
     (token, head) for queries), dequantized before the dot product;
+  * MXFP8 data ("Optimizing Inference for Hybrid-Architecture LLMs", section
+    4.2: one shared scale per group of 32 elements) is OCP microscaling:
+    e4m3fn codes times the group's E8M0 scale 2^(byte - 127);
   * Top-K keeps k_t = min(K, n_t) positions; ties go to the lower logical
     position; outputs are physical pool slots, valid ones first, then -1;
   * a query with no visible position attends over nothing and outputs zeros.
@@ -64,6 +67,23 @@ def fp8_e4m3fn_to_f64(codes: np.ndarray) -> np.ndarray:
     return np.where((e == 0xF) & (m == 0x7), np.nan, v)
 
 
+MX_GROUP = 32
+
+
+def e8m0_to_f64(scale_bytes: np.ndarray) -> np.ndarray:
+    """E8M0 scale byte b -> 2^(b - 127) as float64 (an exponent-only format
+    with bias 127); b = 255 is NaN."""
+    b = np.asarray(scale_bytes, dtype=np.uint8).astype(np.int64)
+    return np.where(b == 255, np.nan, np.exp2(b - 127.0))
+
+
+def mxfp8_to_f64(codes: np.ndarray, scale_bytes: np.ndarray) -> np.ndarray:
+    """MXFP8 dequantization along the last axis: each run of MX_GROUP
+    consecutive e4m3fn codes is multiplied by the E8M0 scale of its group.
+    codes [..., D], scale_bytes [..., D / MX_GROUP]."""
+    return fp8_e4m3fn_to_f64(codes) * np.repeat(e8m0_to_f64(scale_bytes), MX_GROUP, axis=-1)
+
+
 # --------------------------------------------------------------------------- paged cache access
 def logical_slots(block_row: np.ndarray, n: int) -> np.ndarray:
     """Physical slot of logical positions 0..n-1 of one sequence: the page id
@@ -86,6 +106,13 @@ def index_keys(k_idx_pool: np.ndarray, idx_dtype: str, D: int, slots: np.ndarray
         sbytes = pages[page[:, None], PAGE * D + 4 * row[:, None] + np.arange(4)[None, :]]
         scale = np.ascontiguousarray(sbytes).view("<f4").reshape(-1).astype(np.float64)
         return fp8_e4m3fn_to_f64(codes) * scale[:, None]
+    if idx_dtype == "mxfp8":
+        pages = np.asarray(k_idx_pool, dtype=np.uint8)
+        page, row = slots // PAGE, slots % PAGE
+        ng = D // MX_GROUP
+        codes = pages[page[:, None], row[:, None] * D + np.arange(D)[None, :]]
+        sbytes = pages[page[:, None], PAGE * D + ng * row[:, None] + np.arange(ng)[None, :]]
+        return mxfp8_to_f64(codes, sbytes)
     raise ValueError(idx_dtype)
 
 
@@ -93,6 +120,8 @@ def index_query(q_idx_t: np.ndarray, q_scale_t, idx_dtype: str) -> np.ndarray:
     """Dequantized indexer query of one token, [H_idx, D] float64."""
     if idx_dtype == "bf16":
         return bf16_to_f64(q_idx_t)
+    if idx_dtype == "mxfp8":
+        return mxfp8_to_f64(q_idx_t, q_scale_t)
     return fp8_e4m3fn_to_f64(q_idx_t) * np.asarray(q_scale_t, dtype=np.float64)[:, None]
 
 

@@ -15,17 +15,25 @@ fp32 and rounded to bf16 (round-to-nearest-even); head weights are N(0,1)/2.
 FP8 index data (keys: one fp32 scale per token; queries: one fp32 scale per
 (token, head)) is produced with scale = amax/448 and torch's
 round-to-nearest-even float8_e4m3fn conversion after clamping to +-448
-(scale 1 when amax is 0).  This is input preparation; the method consumes the
-codes and scales as given.
+(scale 1 when amax is 0).  MXFP8 index data (one E8M0 power-of-two scale per
+32 consecutive elements, "Optimizing Inference for Hybrid-Architecture LLMs",
+section 4.2) follows the OCP microscaling recipe: the group scale is
+2^(floor(log2(amax)) - 8) (8 = the largest e4m3 exponent; 2^0 for an all-zero
+group), elements are x / scale rounded to nearest-even e4m3fn after clamping
+to +-448.  This is input preparation; the method consumes the codes and scales
+as given.
 
 Layouts (all contiguous):
   * index-K pool, bf16:  [NB, 64, D_idx] bf16
   * index-K pool, fp8:   [NB, 64*D_idx + 64*4] uint8 per page: 64 rows of
     D_idx e4m3fn codes, then 64 little-endian fp32 scales (8448 B for D_idx=128)
+  * index-K pool, mxfp8: [NB, 64*D_idx + 64*D_idx/32] uint8 per page: 64 rows of
+    D_idx e4m3fn codes, then per row D_idx/32 E8M0 group-scale bytes
   * latent pool:          [NB*64, 576] bf16 (512 nope + 64 rope)
   * block_table:          [B, max_blocks] int32 (unused entries are 0)
   * seq_lens:             [B] int32
   * q_idx:                [T, H_idx, D_idx] bf16, or uint8 codes + q_idx_scale [T, H_idx] fp32
+                          (fp8) or [T, H_idx, D_idx/32] uint8 E8M0 (mxfp8)
   * w:                    [T, H_idx] fp32
   * q:                    [T, H, 576] bf16
   * q_seq / q_visible:    [T] int32 (query -> sequence, causal horizon)
@@ -55,7 +63,7 @@ class CaseSpec:
     name: str
     H_idx: int
     D_idx: int
-    idx_dtype: str  # "bf16" | "fp8"
+    idx_dtype: str  # "bf16" | "fp8" | "mxfp8"
     K: int
     H: int
     lens: Optional[Sequence[int]] = None
@@ -75,6 +83,9 @@ PRESETS = {
                                lens=[32768] * 32),
     "decode_b64_128k_fp8": CaseSpec("decode_b64_128k_fp8", H_idx=64, D_idx=128, idx_dtype="fp8", K=2048, H=128,
                                     len_range=(65536, 131072), B=64),
+    # the benchmark decode shape with the pages' MXFP8 (group-32) index quantization
+    "decode_b64_128k_mxfp8": CaseSpec("decode_b64_128k_mxfp8", H_idx=64, D_idx=128, idx_dtype="mxfp8", K=2048,
+                                      H=128, len_range=(65536, 131072), B=64),
     "prefill_16k": CaseSpec("prefill_16k", H_idx=64, D_idx=128, idx_dtype="fp8", K=2048, H=128,
                             prefill=(16384, 4096)),
     "mixed_1m": CaseSpec("mixed_1m", H_idx=64, D_idx=128, idx_dtype="fp8", K=2048, H=128,
@@ -134,8 +145,28 @@ def quantize_fp8_rows(x: torch.Tensor):
     return codes, scale
 
 
-def _page_bytes(D: int) -> int:
-    return PAGE * D + PAGE * 4
+MX_GROUP = 32
+E4M3_EMAX = 8  # largest e4m3 exponent: 448 = 1.75 * 2^8
+
+
+def quantize_mxfp8_rows(x: torch.Tensor):
+    """OCP microscaling e4m3 along the last dim (a multiple of 32): per group of
+    32, scale = 2^(floor(log2(amax)) - 8) (2^0 if amax == 0, exponent clamped
+    to [-127, 127]); codes = RNE(x/scale) after clamping to +-448.  Returns
+    (uint8 codes, uint8 E8M0 scale bytes = exponent + 127, one per group)."""
+    xf = x.to(torch.float32)
+    g = xf.reshape(*xf.shape[:-1], xf.shape[-1] // MX_GROUP, MX_GROUP)
+    amax = g.abs().amax(dim=-1)
+    _, ex = torch.frexp(amax)                      # amax = m * 2^ex, m in [0.5, 1)
+    e = torch.where(amax > 0, ex - 1 - E4M3_EMAX, torch.zeros_like(ex)).clamp_(-127, 127)
+    scale = torch.ldexp(torch.ones_like(amax), e)
+    y = (g / scale.unsqueeze(-1)).clamp_(-FP8_MAX, FP8_MAX)
+    codes = y.to(torch.float8_e4m3fn).view(torch.uint8).reshape(xf.shape)
+    return codes, (e + 127).to(torch.uint8)
+
+
+def _page_bytes(D: int, idx_dtype: str = "fp8") -> int:
+    return PAGE * D + (PAGE * D // MX_GROUP if idx_dtype == "mxfp8" else PAGE * 4)
 
 
 def build_case(spec: CaseSpec, device="cpu", prefill_chunk: Optional[int] = None) -> Case:
@@ -192,6 +223,12 @@ def build_case(spec: CaseSpec, device="cpu", prefill_chunk: Optional[int] = None
         k_pool[:, : PAGE * D] = codes.reshape(NB, PAGE * D)
         k_pool[:, PAGE * D:] = ks.contiguous().view(torch.uint8).reshape(NB, PAGE * 4)
         del codes, ks
+    elif spec.idx_dtype == "mxfp8":
+        codes, ks = quantize_mxfp8_rows(kf)
+        k_pool = torch.empty(NB, _page_bytes(D, "mxfp8"), dtype=torch.uint8, device=device)
+        k_pool[:, : PAGE * D] = codes.reshape(NB, PAGE * D)
+        k_pool[:, PAGE * D:] = ks.reshape(NB, PAGE * D // MX_GROUP)
+        del codes, ks
     else:
         raise ValueError(spec.idx_dtype)
     del kf
@@ -226,6 +263,8 @@ def build_case(spec: CaseSpec, device="cpu", prefill_chunk: Optional[int] = None
     if spec.idx_dtype == "fp8":
         qcodes, qscale = quantize_fp8_rows(qi)
         q_idx, q_idx_scale = qcodes, qscale
+    elif spec.idx_dtype == "mxfp8":
+        q_idx, q_idx_scale = quantize_mxfp8_rows(qi)
     else:
         q_idx, q_idx_scale = qi, None
     w = torch.randn(T_all, H_i, generator=gen, device=device, dtype=torch.float32) * 0.5

@@ -106,6 +106,27 @@ def test_synth_fp8_quantization_roundtrip():
         assert np.allclose(np.abs(deq).max(1), amax[:, 0], rtol=1e-6)
 
 
+def test_synth_mxfp8_quantization_roundtrip():
+    spec = synth.CaseSpec("t", H_idx=8, D_idx=128, idx_dtype="mxfp8", K=16, H=16, lens=[100, 64, 1])
+    c = synth.build_case(spec)
+    d = synth.to_numpy(c)
+    assert c.k_idx_pool.shape == (c.num_blocks, 8448)
+    assert c.q_idx_scale.shape == (c.T, 8, 4) and c.q_idx_scale.dtype == torch.uint8
+    assert int(c.k_idx_pool[:, 8192:].max()) < 255 and int(c.q_idx_scale.max()) < 255
+    gen = torch.Generator().manual_seed(1)
+    raw = synth._randn_bf16(gen, (c.num_blocks, 64, 128), "cpu").to(torch.float64).numpy().reshape(-1, 128)
+    for b, L in enumerate([100, 64, 1]):
+        slots = O.logical_slots(d["block_table"][b], L)
+        deq = O.index_keys(d["k_idx_pool"], "mxfp8", 128, slots)
+        x = raw[slots].reshape(L, 4, 32)
+        amax = np.abs(x).max(2, keepdims=True)
+        scale = np.exp2(np.floor(np.log2(amax)) - 8)          # the group's power of two
+        err = np.abs(deq.reshape(L, 4, 32) - x)
+        bound = np.abs(x) * 2 ** -4 + scale * 2 ** -9 + np.maximum(np.abs(x) - 448 * scale, 0) + 1e-12
+        assert np.all(err <= bound)
+        assert np.all(amax / scale >= 256) and np.all(amax / scale < 512)
+
+
 def test_synth_speculative_and_prefill_horizons():
     spec = synth.CaseSpec("t", H_idx=4, D_idx=64, idx_dtype="bf16", K=8, H=16, lens=[70, 300],
                           queries_per_seq=[1, 4])

@@ -26,6 +26,14 @@ def make_case(idx_dtype, D, H_idx, k_rows, q_idx, w, seq_len, block_row, NB, q_s
         pool = np.zeros((NB * 64, D), dtype=np.uint16)
         pool[O.logical_slots(block_row, len(k_rows))] = bf16_bits(k_rows)
         pool = pool.reshape(NB, 64, D)
+    elif idx_dtype == "mxfp8":
+        ng = D // 32
+        pool = np.zeros((NB, 64 * D + 64 * ng), dtype=np.uint8)
+        slots = O.logical_slots(block_row, len(k_rows))
+        for p, s in enumerate(slots):
+            pg, r = divmod(int(s), 64)
+            pool[pg, r * D:(r + 1) * D] = np.asarray(k_rows[p], dtype=np.uint8)
+            pool[pg, 64 * D + ng * r: 64 * D + ng * (r + 1)] = np.asarray(k_scales[p], dtype=np.uint8)
     else:
         pool = np.zeros((NB, 64 * D + 256), dtype=np.uint8)
         slots = O.logical_slots(block_row, len(k_rows))
@@ -43,7 +51,7 @@ def make_case(idx_dtype, D, H_idx, k_rows, q_idx, w, seq_len, block_row, NB, q_s
         q_seq=np.array([0], np.int32), q_visible=np.array([seq_len if q_visible is None else q_visible], np.int32),
         w=np.array([w], np.float32),
         q_idx=(bf16_bits([q_idx]) if idx_dtype == "bf16" else np.array([q_idx], np.uint8)),
-        q_idx_scale=None if q_scale is None else np.array([q_scale], np.float32),
+        q_idx_scale=None if q_scale is None else np.array([q_scale], np.uint8 if idx_dtype == "mxfp8" else np.float32),
         k_idx_pool=pool, q=q, kv_pool=kv)
 
 
@@ -58,6 +66,23 @@ def test_fp8_decode_all_256_codes_match_torch():
     assert np.array_equal(ours[~nan], ref[~nan])
     assert O.fp8_e4m3fn_to_f64(np.uint8(0x7E)) == 448.0
     assert O.fp8_e4m3fn_to_f64(np.uint8(0x01)) == 2.0 ** -9
+
+
+def test_e8m0_decode_all_256_bytes_match_torch():
+    b = np.arange(256, dtype=np.uint8)
+    ours = O.e8m0_to_f64(b)
+    ref = torch.from_numpy(b).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    assert np.isnan(ours[255]) and np.isnan(ref[255])
+    assert np.array_equal(ours[:255], ref[:255])
+    assert [math.ldexp(1.0, int(x) - 127) for x in b[:255]] == ours[:255].tolist()
+
+
+def test_mxfp8_dequant_group_boundaries():
+    # 64 codes of 1.0 with group scales 2^1 and 2^-3: the first 32 decode to 2,
+    # the next 32 to 1/8 (a shifted or transposed group index fails)
+    codes = np.full((1, 64), 0x38, dtype=np.uint8)
+    v = O.mxfp8_to_f64(codes, np.array([[128, 124]], dtype=np.uint8))
+    assert v[0, :32].tolist() == [2.0] * 32 and v[0, 32:].tolist() == [0.125] * 32
 
 
 def test_bf16_decode_matches_torch():
@@ -96,6 +121,56 @@ def test_scores_hand_worked_fp8():
     S, slots = O.query_scores(case, 0)
     assert S.tolist() == [-2.0, 1.75]
     assert slots.tolist() == [192, 193]
+
+
+def test_scores_hand_worked_mxfp8():
+    # D = 64: two groups of 32.  e4m3fn codes 0x38=1, 0x40=2, 0x44=3, 0xB8=-1;
+    # E8M0 bytes 125=1/4, 126=1/2, 127=1, 128=2, 129=4, 130=8.
+    # q head 0: dim 0 = 1 (x2), dim 32 = 2 (x1/2)  -> [2 @0, 1 @32]
+    # q head 1: dim 1 = 2 (x1)                     -> [2 @1]
+    # k0: dim 0 = 3, dim 1 = 1 (group x1/4), dim 32 = -1 (x8) -> [.75 @0, .25 @1, -8 @32]
+    # k1: dim 0 = 1 (x1), dim 32 = 1 (x4)                    -> [1 @0, 4 @32]
+    # head dots: k0 (1.5 - 8 = -6.5, 0.5), k1 (2 + 4 = 6, 0); w = [1.5, -2]
+    # S0 = 1.5*0 - 2*0.5 = -1;  S1 = 1.5*6 - 2*0 = 9
+    D = 64
+    q = np.zeros((2, D), np.uint8)
+    q[0, 0], q[0, 32], q[1, 1] = 0x38, 0x40, 0x40
+    k = np.zeros((2, D), np.uint8)
+    k[0, 0], k[0, 1], k[0, 32] = 0x44, 0x38, 0xB8
+    k[1, 0], k[1, 32] = 0x38, 0x38
+    case = make_case("mxfp8", D, 2, k, q, [1.5, -2.0], 2, [1], 2, q_scale=[[128, 126], [127, 127]],
+                     k_scales=[[125, 130], [127, 129]])
+    S, slots = O.query_scores(case, 0)
+    assert S.tolist() == [-1.0, 9.0]
+    assert slots.tolist() == [64, 65]
+
+
+def test_mxfp8_with_equal_group_scales_equals_fp8_per_token():
+    rng = np.random.default_rng(3)
+    codes = rng.integers(0, 0x7E, (5, 128)).astype(np.uint8) | (rng.integers(0, 2, (5, 128)) << 7).astype(np.uint8)
+    byte = rng.integers(110, 140, 5).astype(np.uint8)
+    mx = O.mxfp8_to_f64(codes, np.repeat(byte[:, None], 4, axis=1))
+    fp = O.fp8_e4m3fn_to_f64(codes) * np.exp2(byte.astype(np.float64) - 127)[:, None]
+    assert np.array_equal(mx, fp)
+
+
+def test_mxfp8_key_group_scale_only_touches_its_group():
+    rng = np.random.default_rng(4)
+    D = 128
+    k = rng.integers(0, 0x60, (3, D)).astype(np.uint8)
+    ks = rng.integers(120, 135, (3, 4)).astype(np.uint8)
+    q = np.zeros((1, D), np.uint8)
+    q[0, 64:96] = rng.integers(0x20, 0x50, 32)  # query lives in group 2 only
+    base = make_case("mxfp8", D, 1, k, q, [1.0], 3, [0], 1, q_scale=[[127, 127, 127, 127]], k_scales=ks)
+    S0, _ = O.query_scores(base, 0)
+    ks2 = ks.copy()
+    ks2[:, [0, 1, 3]] += 3      # other groups: no effect
+    S1, _ = O.query_scores(make_case("mxfp8", D, 1, k, q, [1.0], 3, [0], 1, q_scale=[[127] * 4], k_scales=ks2), 0)
+    assert np.array_equal(S0, S1)
+    ks3 = ks.copy()
+    ks3[:, 2] += 2              # its own group: the (positive) scores scale by 4
+    S2, _ = O.query_scores(make_case("mxfp8", D, 1, k, q, [1.0], 3, [0], 1, q_scale=[[127] * 4], k_scales=ks3), 0)
+    assert np.array_equal(S2, 4 * S0) and (S0 > 0).all()
 
 
 def test_scores_closed_form_ramp_through_permuted_pages():
