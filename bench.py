@@ -79,11 +79,13 @@ def algorithmic_bytes(case, indices):
     import torch
     s = case.spec
     lens = case.seq_lens.tolist()
-    per_key = s.D_idx + 4 if s.idx_dtype == "fp8" else 2 * s.D_idx
+    # bytes per key: codes + scale (fp32 per token, or one E8M0 byte per 32 elements)
+    scale_b = {"fp8": 4, "mxfp8": s.D_idx // 32}.get(s.idx_dtype, 0)
+    per_key = s.D_idx + scale_b if scale_b else 2 * s.D_idx
     idx_bytes = sum(per_key * L for L in lens)
     idx_bytes += 4 * sum((L + 63) // 64 for L in lens) + 4 * len(lens)
     T = case.T
-    qi = s.H_idx * s.D_idx * (1 if s.idx_dtype == "fp8" else 2) + (4 * s.H_idx if s.idx_dtype == "fp8" else 0)
+    qi = s.H_idx * per_key
     idx_bytes += T * (qi + 4 * s.H_idx + 4 * s.K)
     rows = 0
     seqs = case.q_seq.tolist()
@@ -119,8 +121,8 @@ def cpu_baseline(case, n_sample):
                  q_visible=np.array([int(case.q_visible[t])], np.int32), w=case.w[t:t + 1].cpu().numpy(),
                  q=bits16(case.q[t:t + 1]),
                  kv_pool=bits16(case.kv_pool.view(-1, 64, 576)[pages].reshape(-1, 576)),
-                 k_idx_pool=kp.cpu().numpy() if s.idx_dtype == "fp8" else bits16(kp))
-        if s.idx_dtype == "fp8":
+                 k_idx_pool=kp.cpu().numpy() if s.idx_dtype != "bf16" else bits16(kp))
+        if s.idx_dtype != "bf16":
             d["q_idx"], d["q_idx_scale"] = case.q_idx[t:t + 1].cpu().numpy(), case.q_idx_scale[t:t + 1].cpu().numpy()
         else:
             d["q_idx"], d["q_idx_scale"] = bits16(case.q_idx[t:t + 1]), None
@@ -205,7 +207,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8+bf16" if spec.idx_dtype == "fp8" else "bf16",
+        "dtype": "bf16" if spec.idx_dtype == "bf16" else f"{spec.idx_dtype}+bf16",
         "data": "synthetic",
         "config": {
             "workload": spec.name, "queries": case.T, "sequences": case.B,

@@ -38,6 +38,12 @@
  *   - index-K pool, FP8:   num_blocks pages of (64*D_idx + 256) bytes: 64 rows of
  *                          D_idx OCP e4m3fn codes, then 64 fp32 dequantisation
  *                          scales (one per token).  8448 B per page at D_idx=128.
+ *   - index-K pool, MXFP8: num_blocks pages of (64*D_idx + 64*D_idx/32) bytes:
+ *                          64 rows of D_idx e4m3fn codes, then per row D_idx/32
+ *                          E8M0 scale bytes (row-major; the value of code c in
+ *                          group g is e4m3(c) * 2^(scale[g] - 127)).  Group size
+ *                          32 ("Optimizing Inference for Hybrid-Architecture
+ *                          LLMs", section 4.2).  8448 B per page at D_idx=128.
  *   - latent pool:         [num_blocks*64][576] bf16 (512 nope + 64 rope), row
  *                          `slot` = page*64 + offset.
  *   - block_table:         [B][max_blocks] int32, logical page -> physical page.
@@ -54,7 +60,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 1
+#define DSA_ABI_VERSION 2
 #define DSA_PAGE_TOKENS 64
 #define DSA_LATENT_DIM 576
 #define DSA_VALUE_DIM 512
@@ -74,8 +80,9 @@ typedef enum dsa_status {
 } dsa_status;
 
 typedef enum dsa_idx_dtype {
-  DSA_IDX_BF16 = 0,       /* q_idx and the index-K pool are bf16                   */
-  DSA_IDX_FP8_E4M3FN = 1  /* OCP e4m3fn codes with fp32 scales (see layout above) */
+  DSA_IDX_BF16 = 0,        /* q_idx and the index-K pool are bf16                       */
+  DSA_IDX_FP8_E4M3FN = 1,  /* OCP e4m3fn codes with fp32 per-token / per-head scales    */
+  DSA_IDX_MXFP8_E4M3 = 2   /* OCP e4m3fn codes with an E8M0 scale per 32 elements      */
 } dsa_idx_dtype;
 
 /*
@@ -85,11 +92,12 @@ typedef enum dsa_idx_dtype {
  *   T            query tokens in this call (>= 1)
  *   B            sequences (>= 1)
  *   H_idx        indexer heads, 1..64
- *   D_idx        indexer head dim: 64 or 128 (BF16), 128 (FP8)
+ *   D_idx        indexer head dim: 64 or 128 (BF16), 128 (FP8, MXFP8)
  *   idx_dtype    dsa_idx_dtype
  *   q_idx        [T][H_idx][D_idx] bf16, or e4m3fn codes (uint8)
- *   q_idx_scale  [T][H_idx] fp32 dequantisation scale per (token, head); FP8
- *                only, must be NULL for BF16.  Scales must be > 0.
+ *   q_idx_scale  FP8: [T][H_idx] fp32 dequantisation scale per (token, head),
+ *                > 0.  MXFP8: [T][H_idx][D_idx/32] uint8 E8M0 group scales
+ *                (255, the E8M0 NaN, is not allowed).  Must be NULL for BF16.
  *   w            [T][H_idx] fp32 head weights (any sign)
  *   k_idx_pool   paged index-K pool (layout above)
  *   num_blocks   pages in both pools
@@ -108,7 +116,7 @@ typedef struct dsa_indexer_args {
   int32_t T, B, H_idx, D_idx;
   int32_t idx_dtype;
   const void* q_idx;
-  const float* q_idx_scale;
+  const void* q_idx_scale;
   const float* w;
   const void* k_idx_pool;
   int64_t num_blocks;

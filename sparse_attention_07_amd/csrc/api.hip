@@ -10,7 +10,7 @@
 #include "dsa_params.h"
 
 namespace dsa {
-hipError_t launch_indexer(const IdxParams& p, int is_fp8, int D, int grid, bool need_merge, hipStream_t st);
+hipError_t launch_indexer(const IdxParams& p, int idx_dtype, int D, int grid, bool need_merge, hipStream_t st);
 hipError_t launch_mla(const MlaParams& p, hipStream_t st);
 
 namespace {
@@ -37,14 +37,15 @@ struct MlaPlan {
 dsa_status check_indexer(const dsa_indexer_args* a, int K) {
   if (!a) return DSA_ERR_NULL;
   if (K <= 0 || K > DSA_MAX_K) return DSA_ERR_K;
-  if (a->idx_dtype != DSA_IDX_BF16 && a->idx_dtype != DSA_IDX_FP8_E4M3FN) return DSA_ERR_DTYPE;
+  if (a->idx_dtype != DSA_IDX_BF16 && a->idx_dtype != DSA_IDX_FP8_E4M3FN && a->idx_dtype != DSA_IDX_MXFP8_E4M3)
+    return DSA_ERR_DTYPE;
   if (!a->q_idx || !a->w || !a->k_idx_pool || !a->block_table || !a->seq_lens) return DSA_ERR_NULL;
-  if (a->idx_dtype == DSA_IDX_FP8_E4M3FN && !a->q_idx_scale) return DSA_ERR_NULL;
+  if (a->idx_dtype != DSA_IDX_BF16 && !a->q_idx_scale) return DSA_ERR_NULL;
   if (a->idx_dtype == DSA_IDX_BF16 && a->q_idx_scale) return DSA_ERR_DTYPE;
   if (a->T < 1 || a->B < 1 || a->max_blocks < 1 || a->num_blocks < 1 || a->max_q_per_seq < 1) return DSA_ERR_SHAPE;
   if (a->H_idx < 1 || a->H_idx > DSA_MAX_INDEX_HEADS) return DSA_ERR_SHAPE;
   if (a->idx_dtype == DSA_IDX_BF16 && a->D_idx != 64 && a->D_idx != 128) return DSA_ERR_SHAPE;
-  if (a->idx_dtype == DSA_IDX_FP8_E4M3FN && a->D_idx != 128) return DSA_ERR_UNSUPPORTED;
+  if (a->idx_dtype != DSA_IDX_BF16 && a->D_idx != 128) return DSA_ERR_UNSUPPORTED;
   if (!a->q_seq && a->T != a->B) return DSA_ERR_SHAPE;
   if ((int64_t)a->max_blocks * DSA_PAGE_TOKENS > (int64_t)INT32_MAX / 2) return DSA_ERR_SHAPE;
   if ((int64_t)a->num_blocks * DSA_PAGE_TOKENS > (int64_t)INT32_MAX) return DSA_ERR_SHAPE;
@@ -141,7 +142,9 @@ IdxParams make_idx_params(const dsa_indexer_args* a, int K, int32_t* indices, un
   p.k_pool = (const uint8_t*)a->k_idx_pool;
   p.num_blocks = a->num_blocks;
   const int es = a->idx_dtype == DSA_IDX_BF16 ? 2 : 1;
-  p.page_bytes = (int64_t)DSA_PAGE_TOKENS * a->D_idx * es + (a->idx_dtype == DSA_IDX_BF16 ? 0 : DSA_PAGE_TOKENS * 4);
+  // per-row scale bytes after the codes: fp32 per token, or one E8M0 byte per 32 elements
+  const int scale_bytes = a->idx_dtype == DSA_IDX_FP8_E4M3FN ? 4 : (a->idx_dtype == DSA_IDX_MXFP8_E4M3 ? a->D_idx / 32 : 0);
+  p.page_bytes = (int64_t)DSA_PAGE_TOKENS * (a->D_idx * es + scale_bytes);
   p.block_table = a->block_table;
   p.seq_lens = a->seq_lens;
   p.q_seq = a->q_seq;
@@ -233,7 +236,7 @@ dsa_status dsa_indexer_topk(const dsa_indexer_args* a, int K, int32_t* indices_o
   const IdxPlan pl = plan_indexer(a, K, 0, device_cus());
   if (!ws || ws_bytes < pl.end || !aligned(ws, 256)) return DSA_ERR_WORKSPACE;
   IdxParams p = make_idx_params(a, K, indices_out, (unsigned char*)ws, pl);
-  return hip_status(launch_indexer(p, a->idx_dtype == DSA_IDX_FP8_E4M3FN, a->D_idx, pl.nwg, pl.need_merge,
+  return hip_status(launch_indexer(p, a->idx_dtype, a->D_idx, pl.nwg, pl.need_merge,
                                    (hipStream_t)stream));
 }
 
@@ -267,7 +270,7 @@ dsa_status dsa_layer(const dsa_indexer_args* idx, const dsa_mla_args* mla, int K
   int32_t* indices = indices_out ? indices_out : (int32_t*)(w + off_idx);
   hipStream_t s = (hipStream_t)stream;
   IdxParams p = make_idx_params(idx, K, indices, w, ip);
-  st = hip_status(launch_indexer(p, idx->idx_dtype == DSA_IDX_FP8_E4M3FN, idx->D_idx, ip.nwg, ip.need_merge, s));
+  st = hip_status(launch_indexer(p, idx->idx_dtype, idx->D_idx, ip.nwg, ip.need_merge, s));
   if (st != DSA_OK) return st;
   MlaParams q = make_mla_params(mla, indices, K, scale, out, w, mp);
   return hip_status(launch_mla(q, s));

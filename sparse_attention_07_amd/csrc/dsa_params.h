@@ -13,7 +13,7 @@ enum GroupField { G_T0 = 0, G_NQ, G_SEQ, G_RANGE, G_OFF, G_NL, G_LIST, G_W0, G_F
 
 struct IdxParams {
   const uint8_t* q_idx;   // [T][H_idx][D_idx] bf16 or e4m3fn codes
-  const float* q_scale;   // [T][H_idx] (FP8 only)
+  const void* q_scale;    // FP8: [T][H_idx] fp32; MXFP8: [T][H_idx][D/32] E8M0 bytes
   const float* w;         // [T][H_idx]
   const uint8_t* k_pool;  // paged index-K pool
   int64_t num_blocks;

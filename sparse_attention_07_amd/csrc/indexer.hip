@@ -494,7 +494,7 @@ struct Frag {
 template <int DT, int D>
 struct BFrag {
   Frag<DT, D> f;
-  float sc;
+  float sc;  // FP8: key scale; MXFP8: E8M0 group byte (as bits)
   int ok;
 };
 
@@ -568,6 +568,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
     // with the first sub-chunk's page ids.
     Frag<DT, D> a[MQ][HT];
     float wv[MQ][HT][4];
+    // MXFP8: this lane's E8M0 scale operand = group g4 of head n16 of the tile
+    // (the block-scaled MFMA takes the scale of (row, k-group) from lane
+    // row + 16 * group)
+    int qsx[MQ][HT];
 #pragma unroll
     for (int q = 0; q < MQ; ++q) {
       const int64_t tq = t0 + min(q, nq - 1);
@@ -575,13 +579,15 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
       for (int mt = 0; mt < HT; ++mt) {
         const int h = mt * 16 + n16;
         const bool okh = q < nq && h < p.H_idx;
-        const uint8_t* row = p.q_idx + (tq * p.H_idx + min(h, p.H_idx - 1)) * ROWB;
+        const int64_t hrow = tq * p.H_idx + min(h, p.H_idx - 1);
+        const uint8_t* row = p.q_idx + hrow * ROWB;
 #pragma unroll
         for (int j = 0; j < Frag<DT, D>::NP; ++j) {
           const int off_b = DT == 0 ? 2 * (32 * j + 8 * g4) : (64 * j + 16 * g4);
           const v4i v = *reinterpret_cast<const v4i*>(row + off_b);
           a[q][mt].d[j] = okh ? v : v4i{0, 0, 0, 0};
         }
+        qsx[q][mt] = DT == 2 ? (int)reinterpret_cast<const uint8_t*>(p.q_scale)[hrow * (D / 32) + g4] : 0;
       }
     }
 
@@ -606,7 +612,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
           if (q < nq && hh < p.H_idx) {
             const int64_t o = (int64_t)(t0 + q) * p.H_idx + hh;
             wt = p.w[o];
-            if (DT == 1) wt *= p.q_scale[o];
+            if (DT == 1) wt *= reinterpret_cast<const float*>(p.q_scale)[o];
           }
           sm.wq[q][hh] = wt;
         }
@@ -644,7 +650,11 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
           const int off_b = DT == 0 ? 2 * (32 * j + 8 * g4) : (64 * j + 16 * g4);
           bf.f.d[j] = *reinterpret_cast<const v4i*>(rowp + off_b);
         }
-        bf.sc = DT == 1 ? *reinterpret_cast<const float*>(pgp + PAGE * ROWB + 4 * r) : 1.f;
+        // FP8: the key's fp32 scale; MXFP8: the E8M0 byte of group g4 of key r
+        // (carried in sc's bits)
+        if (DT == 1) bf.sc = *reinterpret_cast<const float*>(pgp + PAGE * ROWB + 4 * r);
+        else if (DT == 2) bf.sc = __int_as_float((int)pgp[PAGE * ROWB + (D / 32) * r + g4]);
+        else bf.sc = 1.f;
         bf.ok = ok;
       };
 
@@ -661,6 +671,12 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
                 const v8i av = __builtin_shufflevector(a[q][mt].d[0], a[q][mt].d[1], 0, 1, 2, 3, 4, 5, 6, 7);
                 const v8i bv = __builtin_shufflevector(bf.f.d[0], bf.f.d[1], 0, 1, 2, 3, 4, 5, 6, 7);
                 acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[mt], 0, 0, 0, 0, 0, 0);
+              } else if constexpr (DT == 2) {
+                // group scales applied by the MFMA: A = q (E8M0 in qsx), B = keys
+                const v8i av = __builtin_shufflevector(a[q][mt].d[0], a[q][mt].d[1], 0, 1, 2, 3, 4, 5, 6, 7);
+                const v8i bv = __builtin_shufflevector(bf.f.d[0], bf.f.d[1], 0, 1, 2, 3, 4, 5, 6, 7);
+                acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[mt], 0, 0, 0, qsx[q][mt], 0,
+                                                                           __float_as_int(bf.sc));
               } else {
 #pragma unroll
                 for (int j = 0; j < Frag<DT, D>::NP; ++j)
@@ -987,13 +1003,15 @@ static hipError_t launch_indexer_mq(const IdxParams& p, int grid, hipStream_t st
   return p.MQ == 1 ? launch_indexer_t<DT, D, HT, 1, 8>(p, grid, st) : launch_indexer_t<DT, D, HT, 2, 8>(p, grid, st);
 }
 
-hipError_t launch_indexer(const IdxParams& p, int is_fp8, int D, int grid, bool need_merge, hipStream_t st) {
+hipError_t launch_indexer(const IdxParams& p, int idx_dtype, int D, int grid, bool need_merge, hipStream_t st) {
   hipLaunchKernelGGL(dsa_plan_kernel, dim3(1), dim3(PLAN_NT), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const bool small_heads = p.H_idx <= 16;
-  if (is_fp8)
+  if (idx_dtype == 1)
     e = small_heads ? launch_indexer_mq<1, 128, 1>(p, grid, st) : launch_indexer_mq<1, 128, 4>(p, grid, st);
+  else if (idx_dtype == 2)
+    e = small_heads ? launch_indexer_mq<2, 128, 1>(p, grid, st) : launch_indexer_mq<2, 128, 4>(p, grid, st);
   else if (D == 64)
     e = small_heads ? launch_indexer_mq<0, 64, 1>(p, grid, st) : launch_indexer_mq<0, 64, 4>(p, grid, st);
   else

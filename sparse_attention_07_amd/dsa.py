@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 IDX_BF16 = 0
 IDX_FP8_E4M3FN = 1
+IDX_MXFP8_E4M3 = 2
 PAGE = 64
 LATENT = 576
 VDIM = 512
@@ -99,11 +100,14 @@ def _stream() -> int:
 def indexer_args(q_idx, w, k_idx_pool, block_table, seq_lens, *, q_idx_scale=None, q_seq=None, q_visible=None,
                  max_q_per_seq: int = 1, num_blocks: Optional[int] = None) -> IndexerArgs:
     """Build the C struct from tensors (no copies; tensors must stay alive)."""
+    # uint8 codes with fp32 scales: FP8 (per token / head); with uint8 scales:
+    # MXFP8 (E8M0 per 32 elements)
     fp8 = q_idx.dtype == torch.uint8
+    mx = fp8 and q_idx_scale is not None and q_idx_scale.dtype == torch.uint8
     T, H_idx, D_idx = q_idx.shape
     a = IndexerArgs()
     a.T, a.B, a.H_idx, a.D_idx = T, seq_lens.shape[0], H_idx, D_idx
-    a.idx_dtype = IDX_FP8_E4M3FN if fp8 else IDX_BF16
+    a.idx_dtype = IDX_MXFP8_E4M3 if mx else (IDX_FP8_E4M3FN if fp8 else IDX_BF16)
     a.q_idx, a.q_idx_scale, a.w = _ptr(q_idx), _ptr(q_idx_scale), _ptr(w)
     a.k_idx_pool = _ptr(k_idx_pool)
     a.num_blocks = k_idx_pool.shape[0] if num_blocks is None else num_blocks

@@ -34,9 +34,9 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert dsa.LIB.dsa_abi_version() == 1
     m = re.search(r"#define DSA_ABI_VERSION (\d+)", open(HEADER).read())
-    assert int(m.group(1)) == 1
+    assert int(m.group(1)) == 2
+    assert dsa.LIB.dsa_abi_version() == int(m.group(1))
     assert dsa.status_str(0) == "ok"
     for s in range(1, 9):
         assert dsa.status_str(s) and dsa.status_str(s) != "unknown status"

@@ -54,6 +54,16 @@ def test_fp8_decode_two_level_merge_tree():
     run_case(spec("fp8_tree", lens=[40000, 1000, 3], seed=5))
 
 
+def test_mxfp8_decode_ragged_multichunk():
+    # E8M0 group scales applied inside the block-scaled MFMA
+    run_case(spec("mx_ragged", idx_dtype="mxfp8", lens=[40000, 1000, 3, 9000], seed=37))
+
+
+def test_mxfp8_prefill_paired_queries():
+    run_case(spec("mx_prefill", idx_dtype="mxfp8", prefill=(6000, 2048), K=512, H=64, seed=41), prefill_chunk=1,
+             queries=[0, 1, 511, 512, 1000, 2047])
+
+
 def test_speculative_multi_query_groups():
     run_case(spec("spec_mix", lens=[3000, 9000, 20000, 130], queries_per_seq=[1, 4, 2, 3], seed=7))
 
@@ -93,6 +103,10 @@ def test_full_decode_b32_32k():
 
 def test_full_decode_b64_128k_fp8():
     run_case(synth.PRESETS["decode_b64_128k_fp8"], queries=[0, 40, 63])
+
+
+def test_full_decode_b64_128k_mxfp8():
+    run_case(synth.PRESETS["decode_b64_128k_mxfp8"], queries=[0, 21, 63])
 
 
 def test_full_prefill_16k_last_chunk():
