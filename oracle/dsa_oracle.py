@@ -27,6 +27,10 @@ Readings where the pages are silent (each also listed in the design notes):
   * MXFP8 data ("Optimizing Inference for Hybrid-Architecture LLMs", section
     4.2: one shared scale per group of 32 elements) is OCP microscaling:
     e4m3fn codes times the group's E8M0 scale 2^(byte - 127);
+  * quantizing a query: an FP8 scale is amax/448 in float32 (1 for an
+    all-zero row), an MXFP8 group scale 2^(floor(log2 amax) - 8) (2^0 for an
+    all-zero group); values are divided by the scale, clamped to +-448 and
+    rounded to nearest even e4m3fn;
   * Top-K keeps k_t = min(K, n_t) positions; ties go to the lower logical
     position; outputs are physical pool slots, valid ones first, then -1;
   * a query with no visible position attends over nothing and outputs zeros.
@@ -82,6 +86,69 @@ def mxfp8_to_f64(codes: np.ndarray, scale_bytes: np.ndarray) -> np.ndarray:
     consecutive e4m3fn codes is multiplied by the E8M0 scale of its group.
     codes [..., D], scale_bytes [..., D / MX_GROUP]."""
     return fp8_e4m3fn_to_f64(codes) * np.repeat(e8m0_to_f64(scale_bytes), MX_GROUP, axis=-1)
+
+
+# --------------------------------------------------------------------------- index-query quantization
+# The step before the path: the projected indexer query (bf16) becomes e4m3fn
+# codes plus scales ("Inference Acceleration for a New Domestic LLM
+# Architecture", section 3: a Q-quantization launch in the index pre-stage;
+# "Optimizing Inference for Hybrid-Architecture LLMs", sections 3.2 and 4.2;
+# "Hybrid Attention LLM Inference Acceleration", sections 4 and 5).  The pages
+# give the group size (32) but no scale rule: a per-(token, head) scale is
+# amax/448, an MX group scale the power of two that puts amax's exponent at
+# e4m3's largest (8).  Scale arithmetic is float32, as an fp32 device computes
+# it, so the integer codes are decided in the same precision on both sides;
+# the e4m3 rounding itself is exact.
+E4M3_MAX = 448.0
+
+
+def e4m3fn_encode(y: np.ndarray) -> np.ndarray:
+    """Round-to-nearest-even of finite values with |y| <= 448 to OCP e4m3fn
+    codes (bit patterns), from the format's definition: subnormals are
+    multiples of 2^-9 below 2^-6; a normal value 2^e (1 + m/8) has exponent
+    field e + 7 (1..15) and mantissa m; ties go to the even mantissa."""
+    y = np.asarray(y, dtype=np.float64)
+    sign = (np.signbit(y)).astype(np.int64) << 7
+    a = np.abs(y)
+    codes = np.zeros(a.shape, dtype=np.int64)
+    sub = a < 2.0 ** -6
+    # subnormal: n = RNE(a / 2^-9), n in 0..8 (8 = the smallest normal, code 0x08)
+    codes[sub] = np.round(a[sub] * 2.0 ** 9).astype(np.int64)   # np.round is half-to-even
+    nrm = ~sub
+    e = np.floor(np.log2(a[nrm])).astype(np.int64)
+    frac = a[nrm] / np.exp2(e.astype(np.float64))                 # in [1, 2), exact
+    m = np.round((frac - 1.0) * 8.0).astype(np.int64)             # 0..8, half-to-even
+    e = e + (m == 8)
+    m = np.where(m == 8, 0, m)
+    codes[nrm] = ((e + 7) << 3) | m
+    return (codes | sign).astype(np.uint8)
+
+
+def quantize_fp8_per_row(x: np.ndarray):
+    """Per-row e4m3fn quantization of float values x [..., D]: s = amax/448 in
+    float32 (1 when amax = 0); codes = e4m3(RNE(clamp(x/s, +-448))) with x/s
+    rounded to float32.  Returns (uint8 codes, float32 scales [...])."""
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.abs(x32).max(axis=-1)
+    s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    s = np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
+    y = np.clip((x32 / s[..., None]).astype(np.float32), -E4M3_MAX, E4M3_MAX)
+    return e4m3fn_encode(y), s
+
+
+def quantize_mxfp8(x: np.ndarray):
+    """OCP microscaling e4m3 along the last axis in groups of 32: group scale
+    2^e with e = floor(log2(amax)) - 8 (8 = e4m3's largest exponent; e = 0 when
+    amax = 0; clamped to [-127, 127]); codes = e4m3(RNE(clamp(x / 2^e, +-448))).
+    Returns (uint8 codes, uint8 E8M0 bytes e + 127)."""
+    x32 = np.asarray(x, dtype=np.float32)
+    g = x32.reshape(*x32.shape[:-1], x32.shape[-1] // MX_GROUP, MX_GROUP).astype(np.float64)
+    amax = np.abs(g).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8, 0).astype(np.int64)
+    e = np.clip(e, -127, 127)
+    y = np.clip(g / np.exp2(e.astype(np.float64))[..., None], -E4M3_MAX, E4M3_MAX)   # exact: power of two
+    return e4m3fn_encode(y).reshape(x32.shape), (e + 127).astype(np.uint8)
 
 
 # --------------------------------------------------------------------------- paged cache access

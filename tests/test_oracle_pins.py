@@ -336,3 +336,106 @@ def test_layer_invariant_under_page_permutation():
     assert ra["positions"].tolist() == rb["positions"].tolist()
     np.testing.assert_array_equal(ra["out"], rb["out"])
     assert ra["indices"].tolist() != rb["indices"].tolist()  # slots differ, positions do not
+
+
+# --------------------------------------------------------------------------- index-query quantization
+def _all_e4m3_midpoints():
+    pos = O.fp8_e4m3fn_to_f64(np.arange(0x7F, dtype=np.uint8))   # 0 .. 448, ascending
+    mids = (pos[1:] + pos[:-1]) / 2                                # exact in float32 (one more bit)
+    return np.concatenate([mids, -mids]).astype(np.float32)
+
+
+def test_e4m3_encode_matches_torch_float8_including_every_tie():
+    # library routine: torch's round-to-nearest-even float -> float8_e4m3fn cast
+    rng = np.random.default_rng(11)
+    y = np.concatenate([rng.uniform(-448, 448, 100_000), rng.uniform(-0.02, 0.02, 100_000),
+                        rng.normal(0, 1, 100_000), _all_e4m3_midpoints(), [0.0, -0.0, 448.0, -448.0, 2.0 ** -9,
+                                                                          2.0 ** -10, 3 * 2.0 ** -11]]).astype(np.float32)
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3fn_encode(y), ref)
+
+
+def test_e4m3_encode_inverts_decode_on_every_finite_code():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    assert np.array_equal(O.e4m3fn_encode(O.fp8_e4m3fn_to_f64(codes)), codes)
+
+
+def test_quantize_fp8_hand_worked_row():
+    # amax 896 -> s = 2; x/s = 448, 0.5, -1.5, 0.25, 8.5 (a tie: 8 and 9 -> 8), 9.5 (tie -> 10)
+    x = np.array([896.0, 1.0, -3.0, 0.5, 17.0, 19.0, 0.0, -896.0], np.float32)
+    codes, s = O.quantize_fp8_per_row(x[None])
+    assert s.tolist() == [2.0]
+    # 448 = 0x7e; 0.5 = 2^-1 -> exp field 6; -1.5 -> 0x80 | (7 << 3) | 4; 0.25 -> field 5;
+    # 8 = 2^3 -> field 10; 10 = 1.25 * 2^3 -> field 10, mantissa 2
+    assert codes[0].tolist() == [0x7E, 0x30, 0xBC, 0x28, 0x50, 0x52, 0x00, 0xFE]
+
+
+def test_quantize_fp8_zero_row_and_subnormal_codes():
+    codes, s = O.quantize_fp8_per_row(np.zeros((2, 64), np.float32))
+    assert s.tolist() == [1.0, 1.0] and not codes.any()
+    # amax 448 -> s = 1.  Subnormals are n * 2^-9: 2^-7 is n = 4; 3 * 2^-10 is the tie n = 1.5 -> 2;
+    # 7 * 2^-10 the tie n = 3.5 -> 4; 2^-10 the tie n = 0.5 -> 0
+    x = np.zeros((1, 32), np.float32)
+    x[0, :5] = [448.0, 2.0 ** -7, 3 * 2.0 ** -10, 7 * 2.0 ** -10, -(2.0 ** -10)]
+    codes, s = O.quantize_fp8_per_row(x)
+    assert s.tolist() == [1.0] and codes[0, :5].tolist() == [0x7E, 0x04, 0x02, 0x04, 0x80]
+
+
+def test_quantize_fp8_error_bound_and_amax_code():
+    rng = np.random.default_rng(12)
+    x = (rng.normal(0, 1, (500, 128)) * np.exp(rng.normal(0, 3, (500, 1)))).astype(np.float32)
+    codes, s = O.quantize_fp8_per_row(x)
+    y = x.astype(np.float64) / s[:, None].astype(np.float64)
+    deq = O.fp8_e4m3fn_to_f64(codes)
+    # round to nearest: half an e4m3 ulp (2^-4 relative for normals, 2^-10 absolute below 2^-6), plus
+    # the float32 rounding of x/s
+    bound = np.maximum(np.abs(y) * 2.0 ** -4, 2.0 ** -10) * (1 + 1e-6) + np.abs(y) * 2.0 ** -23
+    assert np.all(np.abs(deq - np.clip(y, -448, 448)) <= bound)
+    # the element holding amax lands on +-448 (code 0x7e or 0xfe)
+    am = np.abs(x).argmax(axis=1)
+    assert np.all((codes[np.arange(500), am] & 0x7F) == 0x7E)
+
+
+def test_quantize_mxfp8_hand_worked_groups():
+    x = np.zeros((1, 128), np.float32)
+    x[0, :3] = [1.0, -0.75, 2.0 ** -7]          # group 0: amax 1 -> e = -8, x * 256 = 256, -192, 2
+    x[0, 64:66] = [500.0, 3.0]                  # group 2: amax 500 -> e = 0; 500 clamps to 448
+    x[0, 96] = 2.0 ** -130                      # group 3: float32 subnormal amax -> e clamps to -127
+    codes, sc = O.quantize_mxfp8(x)
+    assert sc[0].tolist() == [119, 127, 127, 0]   # group 1 is all zero -> byte 127
+    assert codes[0, :3].tolist() == [0x78, 0xF4, 0x40]
+    assert not codes[0, 32:64].any()
+    assert codes[0, 64:66].tolist() == [0x7E, 0x44]   # 3 = 1.5 * 2^1 -> exp field 8, mantissa 4
+    assert codes[0, 96] == 0x20                  # 2^-130 * 2^127 = 2^-3 -> exp field 4
+
+
+def test_quantize_mxfp8_scale_is_power_of_two_below_amax_and_error_bound():
+    rng = np.random.default_rng(13)
+    x = (rng.normal(0, 1, (300, 128)) * np.exp(rng.normal(0, 4, (300, 4))).repeat(32, axis=1)).astype(np.float32)
+    codes, sc = O.quantize_mxfp8(x)
+    amax = np.abs(x.astype(np.float64)).reshape(300, 4, 32).max(axis=2)
+    e = sc.astype(np.int64) - 127
+    for a, ee in zip(amax.ravel(), e.ravel()):
+        m, ex = math.frexp(float(a))             # a = m * 2^ex, m in [0.5, 1): floor(log2 a) = ex - 1
+        assert ee == ex - 1 - 8
+    y = x.astype(np.float64) / np.exp2(e.astype(np.float64)).repeat(32, axis=1)
+    deq = O.fp8_e4m3fn_to_f64(codes)
+    assert np.all(np.abs(y) < 512)
+    bound = np.maximum(np.abs(y) * 2.0 ** -4, 2.0 ** -10) * (1 + 1e-9)
+    clipped = np.clip(y, -448, 448)
+    assert np.all(np.abs(deq - clipped) <= bound)
+
+
+def test_quantizers_agree_with_the_input_generators_recipe():
+    # the seeded generators quantize their own inputs with torch ops; the oracle's
+    # bit-level quantizers must give the same codes on bf16 data
+    from sparse_attention_07_amd import synth
+    g = torch.Generator().manual_seed(14)
+    xb = (torch.randn(64, 64, 128, generator=g) * torch.exp(torch.randn(64, 64, 1, generator=g) * 2)).to(torch.bfloat16)
+    x = xb.float().numpy()
+    c_t, s_t = synth.quantize_fp8_rows(xb)
+    c_o, s_o = O.quantize_fp8_per_row(x)
+    assert np.array_equal(c_t.numpy(), c_o) and np.array_equal(s_t.numpy(), s_o)
+    m_t, e_t = synth.quantize_mxfp8_rows(xb)
+    m_o, e_o = O.quantize_mxfp8(x)
+    assert np.array_equal(m_t.numpy(), m_o) and np.array_equal(e_t.numpy(), e_o)
