@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 2
+#define DSA_ABI_VERSION 3
 #define DSA_PAGE_TOKENS 64
 #define DSA_LATENT_DIM 576
 #define DSA_VALUE_DIM 512
@@ -175,6 +175,32 @@ dsa_status dsa_sparse_mla_attn(const dsa_mla_args* a, const int32_t* indices, in
  */
 dsa_status dsa_layer(const dsa_indexer_args* idx, const dsa_mla_args* mla, int K, float scale,
                      int32_t* indices_out, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Index-query quantization, the step before step 1 ("Inference Acceleration
+ * for a New Domestic LLM Architecture", section 3: a Q-quantization launch
+ * prepares the fused indexer's query; "Optimizing Inference for
+ * Hybrid-Architecture LLMs", section 3.2 for its place in the input
+ * preparation and section 4.2 for per-group dynamic quantization with one
+ * scale per 32 elements).  Each row of D bf16 values is quantized on its own:
+ *   DSA_IDX_FP8_E4M3FN  s = amax|x| / 448 rounded to fp32 (s = 1 when that is
+ *                       0); code = e4m3fn(x / s) with x / s rounded to fp32,
+ *                       clamped to +-448, round-to-nearest-even.
+ *                       scales: fp32 [rows] (the s above).
+ *   DSA_IDX_MXFP8_E4M3  per group of 32: e = floor(log2 amax|x|) - 8 clamped
+ *                       to [-127, 127] (e = 0 for an all-zero group); code =
+ *                       e4m3fn(clamp(x * 2^-e, +-448)), round-to-nearest-even.
+ *                       scales: uint8 [rows][D/32], byte e + 127.
+ *   q       [rows][D] bf16 device, finite values, 16-byte aligned
+ *   rows    >= 0 (0 enqueues nothing); for an indexer query rows = T * H_idx
+ *   D       32, 64, 128, 256 or 512
+ *   codes   [rows][D] uint8 device (written), 16-byte aligned
+ *   scales  as above (written), 4-byte aligned for FP8
+ * codes and scales are exactly the q_idx and q_idx_scale dsa_indexer_topk
+ * takes.  Needs no workspace.
+ */
+dsa_status dsa_quantize_index_q(const void* q, int64_t rows, int32_t D, int32_t idx_dtype, void* codes,
+                                void* scales, void* stream);
 
 /* Static string for a status code ("unknown status" for anything else). */
 const char* dsa_status_str(dsa_status s);

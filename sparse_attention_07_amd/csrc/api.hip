@@ -12,6 +12,8 @@
 namespace dsa {
 hipError_t launch_indexer(const IdxParams& p, int idx_dtype, int D, int grid, bool need_merge, hipStream_t st);
 hipError_t launch_mla(const MlaParams& p, hipStream_t st);
+hipError_t launch_quantize_q(const void* q, int64_t rows, int D, int idx_dtype, void* codes, void* scales,
+                             hipStream_t st);
 
 namespace {
 
@@ -274,6 +276,18 @@ dsa_status dsa_layer(const dsa_indexer_args* idx, const dsa_mla_args* mla, int K
   if (st != DSA_OK) return st;
   MlaParams q = make_mla_params(mla, indices, K, scale, out, w, mp);
   return hip_status(launch_mla(q, s));
+}
+
+dsa_status dsa_quantize_index_q(const void* q, int64_t rows, int32_t D, int32_t idx_dtype, void* codes,
+                                void* scales, void* stream) {
+  if (idx_dtype != DSA_IDX_FP8_E4M3FN && idx_dtype != DSA_IDX_MXFP8_E4M3) return DSA_ERR_DTYPE;
+  if (D != 32 && D != 64 && D != 128 && D != 256 && D != 512) return DSA_ERR_SHAPE;
+  if (rows < 0 || rows > (int64_t)INT32_MAX * 8 / D) return DSA_ERR_SHAPE;
+  if (rows == 0) return DSA_OK;
+  if (!q || !codes || !scales) return DSA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(codes, 16) || (idx_dtype == DSA_IDX_FP8_E4M3FN && !aligned(scales, 4)))
+    return DSA_ERR_ALIGN;
+  return hip_status(launch_quantize_q(q, rows, D, idx_dtype, codes, scales, (hipStream_t)stream));
 }
 
 }  // extern "C"

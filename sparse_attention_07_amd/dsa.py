@@ -24,8 +24,8 @@ VDIM = 512
 MAX_K = 2048
 
 # Every symbol the header declares (checked by the tests against include/dsa.h).
-EXPORTS = ("dsa_workspace_bytes", "dsa_indexer_topk", "dsa_sparse_mla_attn", "dsa_layer", "dsa_status_str",
-           "dsa_abi_version")
+EXPORTS = ("dsa_workspace_bytes", "dsa_indexer_topk", "dsa_sparse_mla_attn", "dsa_layer", "dsa_quantize_index_q",
+           "dsa_status_str", "dsa_abi_version")
 
 
 class DSAError(RuntimeError):
@@ -70,6 +70,9 @@ def _load() -> ctypes.CDLL:
     lib.dsa_layer.restype = ctypes.c_int
     lib.dsa_layer.argtypes = [P(IndexerArgs), P(MlaArgs), ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.dsa_quantize_index_q.restype = ctypes.c_int
+    lib.dsa_quantize_index_q.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.dsa_status_str.restype = ctypes.c_char_p
     lib.dsa_status_str.argtypes = [ctypes.c_int]
     lib.dsa_abi_version.restype = ctypes.c_int
@@ -163,6 +166,25 @@ def sparse_mla_attn(q, kv_pool, indices, scale: float, *, out: Optional[torch.Te
     _check(LIB.dsa_sparse_mla_attn(ctypes.byref(m), _ptr(indices), K, float(scale), _ptr(out),
                                    _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream()))
     return out
+
+
+def quantize_index_q(q: torch.Tensor, idx_dtype: int = IDX_FP8_E4M3FN, *, codes: Optional[torch.Tensor] = None,
+                     scales: Optional[torch.Tensor] = None):
+    """Index-query quantization of bf16 q [..., D]: returns (uint8 codes [..., D],
+    scales) with scales fp32 [...] (FP8) or uint8 E8M0 [..., D/32] (MXFP8), the
+    q_idx / q_idx_scale pair indexer_topk takes."""
+    if q.dtype != torch.bfloat16 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bf16 tensor")
+    D = q.shape[-1]
+    lead = tuple(q.shape[:-1])
+    if codes is None:
+        codes = torch.empty(q.shape, dtype=torch.uint8, device=q.device)
+    if scales is None:
+        scales = (torch.empty(lead, dtype=torch.float32, device=q.device) if idx_dtype == IDX_FP8_E4M3FN
+                  else torch.empty(lead + (max(D // 32, 1),), dtype=torch.uint8, device=q.device))
+    rows = q.numel() // max(D, 1)
+    _check(LIB.dsa_quantize_index_q(_ptr(q), rows, D, idx_dtype, _ptr(codes), _ptr(scales), _stream()))
+    return codes, scales
 
 
 class Layer:

@@ -34,6 +34,7 @@ Layouts (all contiguous):
   * seq_lens:             [B] int32
   * q_idx:                [T, H_idx, D_idx] bf16, or uint8 codes + q_idx_scale [T, H_idx] fp32
                           (fp8) or [T, H_idx, D_idx/32] uint8 E8M0 (mxfp8)
+  * q_idx_src:            [T, H_idx, D_idx] bf16 index query before quantization
   * w:                    [T, H_idx] fp32
   * q:                    [T, H, 576] bf16
   * q_seq / q_visible:    [T] int32 (query -> sequence, causal horizon)
@@ -109,6 +110,8 @@ class Case:
     q_seq: torch.Tensor
     q_visible: torch.Tensor
     max_q_per_seq: int
+    # the bf16 index query the codes were quantized from (== q_idx for bf16)
+    q_idx_src: Optional[torch.Tensor] = None
 
     @property
     def T(self) -> int:
@@ -292,6 +295,7 @@ def build_case(spec: CaseSpec, device="cpu", prefill_chunk: Optional[int] = None
         q_seq=dev(q_seq_all[sel]),
         q_visible=dev(q_vis_all[sel]),
         max_q_per_seq=min(max_q, sel.stop - sel.start),
+        q_idx_src=qi[sel].contiguous(),
     )
 
 

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     m = re.search(r"#define DSA_ABI_VERSION (\d+)", open(HEADER).read())
-    assert int(m.group(1)) == 2
+    assert int(m.group(1)) == 3
     assert dsa.LIB.dsa_abi_version() == int(m.group(1))
     assert dsa.status_str(0) == "ok"
     for s in range(1, 9):
@@ -181,3 +181,26 @@ def test_workspace_bytes_invalid_and_scaling():
     # a single short-context decode needs no candidate lists (one chunk per query)
     small = dsa.workspace_bytes(good_idx(T=1, B=1, max_blocks=64), None, 256)
     assert 0 < small < 4096
+
+
+def call_quant(q=_base, rows=64, D=128, dt=None, codes=_base, scales=_base):
+    dt = dsa.IDX_FP8_E4M3FN if dt is None else dt
+    return dsa.LIB.dsa_quantize_index_q(q, rows, D, dt, codes, scales, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(dt=dsa.IDX_BF16), E_DTYPE), (dict(dt=9), E_DTYPE),
+    (dict(D=96), E_SHAPE), (dict(D=16), E_SHAPE), (dict(D=1024), E_SHAPE), (dict(rows=-1), E_SHAPE),
+    (dict(rows=1 << 40), E_SHAPE),
+    (dict(q=None), E_NULL), (dict(codes=None), E_NULL), (dict(scales=None), E_NULL),
+    (dict(q=_base + 8), E_ALIGN), (dict(codes=_base + 8), E_ALIGN), (dict(scales=_base + 2), E_ALIGN),
+    (dict(rows=0, q=None, codes=None, scales=None), OK),   # nothing to do, nothing enqueued
+])
+def test_quantize_argument_errors(kw, expect):
+    assert call_quant(**kw) == expect
+
+
+def test_quantize_mxfp8_scale_bytes_need_no_alignment():
+    # the E8M0 bytes are written one per group: any address; rows=0 stops before a launch
+    assert call_quant(dt=dsa.IDX_MXFP8_E4M3, scales=_base + 1, rows=0) == OK
+    assert call_quant(dt=dsa.IDX_MXFP8_E4M3, scales=_base + 1, q=_base + 4) == E_ALIGN

@@ -1,0 +1,134 @@
+"""GPU parity of the index-query quantization (dsa_quantize_index_q, through
+the C ABI) against the CPU oracle: codes and scales are integer decisions
+taken in float32 on both sides, so they must match bit for bit.  Cases cover
+every supported row width with ragged row counts, exact rounding ties,
+subnormal and huge inputs, all-zero rows and groups, the prefill chunk at full
+size, and the quantized query fed on through the indexer and sparse MLA."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_cases import check_queries, say
+from oracle import dsa_oracle as O
+from sparse_attention_07_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from sparse_attention_07_amd import dsa
+DEV = "cuda"
+
+
+def oracle_quant(xb_cpu: torch.Tensor, kind: str):
+    x = xb_cpu.float().numpy()          # bf16 -> float32 is exact (done on the host)
+    return O.quantize_fp8_per_row(x) if kind == "fp8" else O.quantize_mxfp8(x)
+
+
+def check_quant(xb_cpu: torch.Tensor, kind: str, label: str):
+    say(f"[quant] {label} {kind} shape={tuple(xb_cpu.shape)}")
+    dt = dsa.IDX_FP8_E4M3FN if kind == "fp8" else dsa.IDX_MXFP8_E4M3
+    codes, scales = dsa.quantize_index_q(xb_cpu.to(DEV), dt)
+    torch.cuda.synchronize()
+    rc, rs = oracle_quant(xb_cpu, kind)
+    gc, gs = codes.cpu().numpy(), scales.cpu().numpy()
+    assert gc.shape == rc.shape and gs.shape == rs.shape
+    bad = np.argwhere(gc != rc)
+    assert bad.size == 0, f"{len(bad)} codes differ, first {bad[:3].tolist()}: gpu {gc[tuple(bad[0])]:#x} " \
+                          f"oracle {rc[tuple(bad[0])]:#x}"
+    gsb = gs.view(np.uint32) if kind == "fp8" else gs
+    rsb = rs.astype(np.float32).view(np.uint32) if kind == "fp8" else rs
+    bad = np.argwhere(gsb != rsb)
+    assert bad.size == 0, f"{len(bad)} scales differ, first {bad[:3].tolist()}"
+    say(f"  bit-exact: {gc.size} codes, {gs.size} scales")
+    return codes, scales
+
+
+def lognormal_rows(shape, seed, spread=2.0):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(*shape, generator=g) * torch.exp(torch.randn(*shape[:-1], 1, generator=g) * spread)
+    return x.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("kind", ["fp8", "mxfp8"])
+def test_decode_query_b64(kind):
+    # one decode step's index query: 64 tokens x 64 heads x 128
+    check_quant(lognormal_rows((64, 64, 128), 1), kind, "decode_b64")
+
+
+@pytest.mark.parametrize("kind", ["fp8", "mxfp8"])
+@pytest.mark.parametrize("D", [32, 64, 128, 256, 512])
+def test_every_width_ragged_rows(kind, D):
+    # row counts that leave a partial workgroup and a partial wave
+    for rows, seed in ((1, 2), (37, 3), (1027, 4)):
+        check_quant(lognormal_rows((rows, D), seed + D), kind, f"D{D}_rows{rows}")
+
+
+def tie_rows(kind: str) -> torch.Tensor:
+    """Rows whose scaled values sit exactly on e4m3 rounding midpoints."""
+    pos = O.fp8_e4m3fn_to_f64(np.arange(0x7F, dtype=np.uint8))
+    mids = (pos[1:] + pos[:-1]) / 2                       # 126 midpoints, bf16-exact (4 significant bits)
+    vals = np.concatenate([mids, -mids])                  # 252
+    if kind == "fp8":
+        # amax 448 gives s = 1 exactly; 127 midpoints per row after the 448
+        per = 127
+        rows = [np.concatenate([[448.0], vals[i:i + per]]) for i in range(0, len(vals), per)]
+        rows = [np.pad(r, (0, 128 - len(r))) for r in rows]
+    else:
+        # a group whose amax lies in [256, 512) gets e = 0, so x is its own scaled value
+        per = 31
+        groups = [np.concatenate([[256.0], vals[i:i + per]]) for i in range(0, len(vals), per)]
+        groups = [np.pad(gp, (0, 32 - len(gp))) for gp in groups]
+        while len(groups) % 4:
+            groups.append(np.zeros(32))
+        rows = [np.concatenate(groups[i:i + 4]) for i in range(0, len(groups), 4)]
+    x = torch.from_numpy(np.stack(rows).astype(np.float32))
+    assert torch.equal(x.to(torch.bfloat16).float(), x)   # every tie is representable in bf16
+    return x.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("kind", ["fp8", "mxfp8"])
+def test_exact_rounding_ties(kind):
+    check_quant(tie_rows(kind), kind, "ties")
+
+
+@pytest.mark.parametrize("kind", ["fp8", "mxfp8"])
+def test_zero_subnormal_and_huge_rows(kind):
+    g = torch.Generator().manual_seed(9)
+    base = torch.randn(8, 128, generator=g)
+    rows = torch.stack([
+        torch.zeros(128),                                   # all zero: scale 1 / byte 127
+        base[0] * 1e-39,                                    # bf16 subnormals throughout
+        base[1] * 1e-41,                                    # amax/448 underflows in float32
+        base[2] * 1e38,                                     # near the bf16 maximum
+        torch.cat([torch.zeros(64), base[3, :64]]),         # zero groups next to live ones
+        torch.cat([base[4, :32] * 1e30, base[5, :32] * 1e-30, base[6, :64]]),   # groups 2^200 apart
+        torch.full((128,), -3.0),                           # constant negative row
+        torch.cat([torch.tensor([448.0, -448.0]), base[7, 2:] * 1e-3]),
+    ])
+    check_quant(rows.to(torch.bfloat16), kind, "special")
+
+
+@pytest.mark.parametrize("kind", ["fp8", "mxfp8"])
+def test_full_prefill_chunk_query(kind):
+    # the 4096-token prefill chunk: 4096 x 64 heads x 128 = 33.5M elements
+    check_quant(lognormal_rows((4096, 64, 128), 21, spread=1.0), kind, "prefill_chunk_4096")
+
+
+@pytest.mark.parametrize("kind", ["fp8", "mxfp8"])
+def test_quantized_query_through_the_layer(kind):
+    # the bf16 index query is quantized on the GPU and fed to the indexer; the
+    # oracle quantizes the same bf16 query itself and runs its own layer
+    spec = synth.CaseSpec(f"quant_e2e_{kind}", lens=[9000, 40000, 77, 2048], H_idx=64, D_idx=128,
+                          idx_dtype=kind, K=2048, H=128, seed=41)
+    case = synth.build_case(spec, device=DEV)
+    src = case.q_idx_src.cpu()
+    codes, scales = check_quant(src, kind, "e2e_query")
+    rc, rs = oracle_quant(src, kind)
+    case.q_idx, case.q_idx_scale = codes, scales          # the HIP path runs on its own quantization
+    layer = dsa.layer_from_case(case)
+    layer()
+    torch.cuda.synchronize()
+    # the oracle side reads its own codes and scales
+    case.q_idx = torch.from_numpy(rc).to(DEV)
+    case.q_idx_scale = torch.from_numpy(np.ascontiguousarray(rs)).to(DEV)
+    check_queries(case, layer.indices, layer.out, range(case.T))
