@@ -32,6 +32,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_b64_128k_fp8")
+    ap.add_argument("--op", choices=("layer", "quantize"), default="layer",
+                    help="layer: the DSA layer step (default); quantize: the index-query quantization that "
+                         "prepares the workload's q_idx from its bf16 projection")
+    ap.add_argument("--quant-dtype", choices=("fp8", "mxfp8"), default=None,
+                    help="--op quantize: the code format (default: the workload's index dtype)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=48, help="queries the CPU oracle is timed on")
     ap.add_argument("--copies", type=int, default=2,
@@ -43,13 +48,19 @@ def parse():
     return ap.parse_args()
 
 
-def source_digest():
-    """sha256 over the kernel and ABI sources: a stored traffic measurement is
-    reported only while the code it was taken on is unchanged."""
-    import glob
+# sources each measured call depends on: a stored counter measurement is
+# reported only while these are unchanged
+KERNEL_SOURCES = {
+    "indexer": ["api.hip", "indexer.hip", "dsa_device.h", "dsa_params.h"],
+    "quantize": ["api.hip", "quant.hip"],
+}
+
+
+def source_digest(kind="indexer"):
+    """sha256 over the kernel and ABI sources of one measured call."""
     import hashlib
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(ROOT, "sparse_attention_07_amd", "csrc", "*")))
+    files = [os.path.join(ROOT, "sparse_attention_07_amd", "csrc", f) for f in KERNEL_SOURCES[kind]]
     files.append(os.path.join(ROOT, "include", "dsa.h"))
     for f in files:
         h.update(os.path.basename(f).encode())
@@ -58,17 +69,29 @@ def source_digest():
     return h.hexdigest()
 
 
-def stored_traffic(workload):
-    """HBM bytes per indexer call from the counter runs recorded under
-    profiles/, or None when absent or taken on other sources."""
-    path = os.path.join(ROOT, "profiles", f"indexer_traffic_{workload}.json")
+def stored_traffic(name, kind="indexer"):
+    """HBM bytes per call from the counter runs recorded under profiles/
+    (profiles/<name>.json), or None when absent or taken on other sources."""
+    path = os.path.join(ROOT, "profiles", f"{name}.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    if rec.get("sources_sha256") != source_digest():
+    if rec.get("sources_sha256") != source_digest(kind):
         return None
     return rec.get("traffic_bytes_per_call")
+
+
+def copy_calibration(dev):
+    """A plain 1 GiB device copy, three times: the reference kernel that scales
+    the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": 1 << 30, "launches": 3}), flush=True)
 
 
 def algorithmic_bytes(case, indices):
@@ -135,6 +158,78 @@ def cpu_baseline(case, n_sample):
                        f"numpy fp64, {secs:.1f} s")
 
 
+def quant_cpu_baseline(src, kind, label):
+    """Time the oracle's quantizer (numpy) on the whole query of the workload."""
+    from oracle import dsa_oracle as O
+    x = src.cpu().float().numpy()
+    rows = x.size // x.shape[-1]
+    t0 = time.perf_counter()
+    if kind == "fp8":
+        O.quantize_fp8_per_row(x)
+    else:
+        O.quantize_mxfp8(x)
+    secs = time.perf_counter() - t0
+    return dict(value=round(rows / secs, 1), unit="rows/s", cores=len(os.sched_getaffinity(0)), kind="oracle",
+                sample=f"all {rows} rows of {label}'s index query ({x.shape[-1]} wide), numpy, {secs:.2f} s")
+
+
+def bench_quantize(args, spec, case):
+    """Index-query quantization: bf16 q_idx [T, H_idx, D_idx] -> e4m3fn codes +
+    scales, rotating through enough input/output copies that no launch reads
+    the previous launch's data from the last-level cache."""
+    import torch
+    from sparse_attention_07_amd import dsa
+    kind = args.quant_dtype or (spec.idx_dtype if spec.idx_dtype != "bf16" else "fp8")
+    dt = dsa.IDX_FP8_E4M3FN if kind == "fp8" else dsa.IDX_MXFP8_E4M3
+    src = case.q_idx_src
+    D = src.shape[-1]
+    rows = src.numel() // D
+    scale_b = 4 if kind == "fp8" else D // 32
+    per_call = rows * (D * 2 + D + scale_b)
+    ncopy = max(2, min(16, -(-(512 << 20) // per_call)))
+    ins = [src.clone() for _ in range(ncopy)]
+    outs = [dsa.quantize_index_q(x, dt) for x in ins]
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        dsa.quantize_index_q(ins[i % ncopy], dt, codes=outs[i % ncopy][0], scales=outs[i % ncopy][1])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        dsa.quantize_index_q(ins[i % ncopy], dt, codes=outs[i % ncopy][0], scales=outs[i % ncopy][1])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = e0.elapsed_time(e1) / args.steps
+    achieved = per_call / (launch_ms * 1e-3) / 1e9
+    line = {
+        "metric": "index-Q quantization rows/s + % HBM roofline",
+        "value": round(rows * args.steps / wall, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"bf16->{kind}",
+        "data": "synthetic",
+        "config": {"workload": f"{spec.name} index query", "rows": rows, "row_width": D,
+                   "codes": kind, "input_copies_rotated": ncopy, "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": stored_traffic(f"quantize_traffic_{spec.name}_{kind}", "quantize"),
+            "kernel": "quantize_q_kernel", "launch_ms": round(launch_ms, 5), "algorithmic_bytes": per_call,
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = quant_cpu_baseline(src, kind, spec.name)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -151,6 +246,11 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     case = synth.build_case(spec, device=dev, prefill_chunk=prefill_chunk)
+    if args.op == "quantize":
+        bench_quantize(args, spec, case)
+        if args.copy_calibration:
+            copy_calibration(dev)
+        return
     layers = [dsa.layer_from_case(case)]
     extra_cases = []
     for _ in range(max(0, args.copies - 1)):
@@ -217,7 +317,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": stored_traffic(spec.name),
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": stored_traffic(f"indexer_traffic_{spec.name}"),
             "kernel": "dsa_indexer_topk: planning + dsa_indexer_kernel + dsa_merge_kernel",
             "launch_ms": round(idx_ms, 5), "algorithmic_bytes": idx_bytes,
         },
@@ -230,12 +330,7 @@ def main():
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_sample)
     print(json.dumps(line), flush=True)
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes": 1 << 30, "launches": 3}), flush=True)
+        copy_calibration(dev)
 
 
 if __name__ == "__main__":

@@ -104,6 +104,9 @@ def test_zero_subnormal_and_huge_rows(kind):
         torch.cat([base[4, :32] * 1e30, base[5, :32] * 1e-30, base[6, :64]]),   # groups 2^200 apart
         torch.full((128,), -3.0),                           # constant negative row
         torch.cat([torch.tensor([448.0, -448.0]), base[7, 2:] * 1e-3]),
+        base[0] * 2.0 ** -79,                               # s just above / below 2^-90, where the
+        base[1] * 2.0 ** -82,                               # kernel's division method changes
+        torch.cat([torch.tensor([2.0 ** -81 * 448]), base[2, 1:] * 2.0 ** -84]),
     ])
     check_quant(rows.to(torch.bfloat16), kind, "special")
 
