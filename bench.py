@@ -125,6 +125,7 @@ def cpu_baseline(case, n_sample):
     import numpy as np
     import torch
     from oracle import dsa_oracle as O
+    from sparse_attention_07_amd import synth
 
     def bits16(t):
         return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
@@ -143,7 +144,9 @@ def cpu_baseline(case, n_sample):
                  block_table=np.arange(nblk, dtype=np.int32)[None], q_seq=np.array([0], np.int32),
                  q_visible=np.array([int(case.q_visible[t])], np.int32), w=case.w[t:t + 1].cpu().numpy(),
                  q=bits16(case.q[t:t + 1]),
-                 kv_pool=bits16(case.kv_pool.view(-1, 64, 576)[pages].reshape(-1, 576)),
+                 kv_pool=(case.kv_pool.view(-1, 64, synth.KV_FP8_ROW)[pages].reshape(-1, synth.KV_FP8_ROW).cpu().numpy()
+                          if s.kv_dtype == "fp8" else bits16(case.kv_pool.view(-1, 64, 576)[pages].reshape(-1, 576))),
+                 kv_dtype=s.kv_dtype,
                  k_idx_pool=kp.cpu().numpy() if s.idx_dtype != "bf16" else bits16(kp))
         if s.idx_dtype != "bf16":
             d["q_idx"], d["q_idx_scale"] = case.q_idx[t:t + 1].cpu().numpy(), case.q_idx_scale[t:t + 1].cpu().numpy()

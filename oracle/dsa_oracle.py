@@ -33,7 +33,9 @@ Readings where the pages are silent (each also listed in the design notes):
     rounded to nearest even e4m3fn;
   * Top-K keeps k_t = min(K, n_t) positions; ties go to the lower logical
     position; outputs are physical pool slots, valid ones first, then -1;
-  * a query with no visible position attends over nothing and outputs zeros.
+  * a query with no visible position attends over nothing and outputs zeros;
+  * FP8 latent KV: per token, 4 scales over the 512 nope dims (tiles of 128),
+    the 64 rope dims kept in bf16; attention runs over the dequantized rows.
 
 Every function here is pinned by tests/test_oracle_pins.py against closed
 forms, hand-worked values, a library routine (torch's float8 decode and its
@@ -47,6 +49,8 @@ import numpy as np
 PAGE = 64
 LATENT = 576
 VDIM = 512
+KV_TILE = 128                       # FP8 latent: one scale per 128 nope elements of a token
+KV_FP8_ROW = VDIM + 4 * (VDIM // KV_TILE) + 2 * (LATENT - VDIM)   # 656 bytes per token
 
 
 # --------------------------------------------------------------------------- decoding
@@ -241,8 +245,27 @@ def query_scores(case: dict, t: int):
     return indexer_scores(qv, case["w"][t], keys), slots
 
 
+def latent_rows_fp8(rows: np.ndarray) -> np.ndarray:
+    """FP8 latent rows (uint8 [n][656]) -> float64 [n][576].  The main attention
+    KV is FP8 with one scale per token and 128-element tile ("Hybrid Attention
+    LLM Inference Acceleration", section 5 table; "Inference Acceleration for a
+    New Domestic LLM Architecture", section 4).  A token's row: 512 e4m3fn codes
+    of the nope dims, then 4 little-endian fp32 scales (tile t covers dims
+    128t..128t+127), then the 64 rope dims in bf16 (the pages do not say how
+    rope dims are stored; kept in bf16).  Nope dim d = e4m3(code[d]) * scale[d // 128]."""
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.uint8).reshape(-1, KV_FP8_ROW))
+    ntile = VDIM // KV_TILE
+    scales = r[:, VDIM: VDIM + 4 * ntile].copy().view("<f4").astype(np.float64)
+    rope = r[:, VDIM + 4 * ntile:].copy().view("<u2")
+    nope = fp8_e4m3fn_to_f64(r[:, :VDIM]) * np.repeat(scales, KV_TILE, axis=1)
+    return np.concatenate([nope, bf16_to_f64(rope)], axis=1)
+
+
 def latent_rows(case: dict, slots: np.ndarray) -> np.ndarray:
-    return bf16_to_f64(np.asarray(case["kv_pool"]).reshape(-1, LATENT)[np.asarray(slots, dtype=np.int64)])
+    slots = np.asarray(slots, dtype=np.int64)
+    if case.get("kv_dtype", "bf16") == "fp8":
+        return latent_rows_fp8(np.asarray(case["kv_pool"]).reshape(-1, KV_FP8_ROW)[slots])
+    return bf16_to_f64(np.asarray(case["kv_pool"]).reshape(-1, LATENT)[slots])
 
 
 def mla_query(case: dict, t: int, slots) -> np.ndarray:

@@ -29,7 +29,9 @@ Layouts (all contiguous):
     D_idx e4m3fn codes, then 64 little-endian fp32 scales (8448 B for D_idx=128)
   * index-K pool, mxfp8: [NB, 64*D_idx + 64*D_idx/32] uint8 per page: 64 rows of
     D_idx e4m3fn codes, then per row D_idx/32 E8M0 group-scale bytes
-  * latent pool:          [NB*64, 576] bf16 (512 nope + 64 rope)
+  * latent pool:          [NB*64, 576] bf16 (512 nope + 64 rope), or with kv_dtype
+                          "fp8" uint8 [NB*64, 656]: 512 e4m3fn codes, 4 fp32 scales
+                          (one per 128 nope dims), 64 bf16 rope dims
   * block_table:          [B, max_blocks] int32 (unused entries are 0)
   * seq_lens:             [B] int32
   * q_idx:                [T, H_idx, D_idx] bf16, or uint8 codes + q_idx_scale [T, H_idx] fp32
@@ -75,6 +77,7 @@ class CaseSpec:
     seed: int = 0
     scale: float = 1.0 / math.sqrt(LATENT)
     permute_pages: bool = True
+    kv_dtype: str = "bf16"  # "bf16" | "fp8" (e4m3fn nope dims, one fp32 scale per 128, bf16 rope)
 
 
 # The five workloads the pages' path is measured on.
@@ -87,6 +90,9 @@ PRESETS = {
     # the benchmark decode shape with the pages' MXFP8 (group-32) index quantization
     "decode_b64_128k_mxfp8": CaseSpec("decode_b64_128k_mxfp8", H_idx=64, D_idx=128, idx_dtype="mxfp8", K=2048,
                                       H=128, len_range=(65536, 131072), B=64),
+    # the benchmark decode shape with the latent cache in FP8 (one scale per token and 128 nope dims)
+    "decode_b64_128k_fp8kv": CaseSpec("decode_b64_128k_fp8kv", H_idx=64, D_idx=128, idx_dtype="fp8", K=2048, H=128,
+                                      len_range=(65536, 131072), B=64, kv_dtype="fp8"),
     "prefill_16k": CaseSpec("prefill_16k", H_idx=64, D_idx=128, idx_dtype="fp8", K=2048, H=128,
                             prefill=(16384, 4096)),
     "mixed_1m": CaseSpec("mixed_1m", H_idx=64, D_idx=128, idx_dtype="fp8", K=2048, H=128,
@@ -168,6 +174,27 @@ def quantize_mxfp8_rows(x: torch.Tensor):
     return codes, (e + 127).to(torch.uint8)
 
 
+KV_TILE = 128
+KV_FP8_ROW = VDIM + 4 * (VDIM // KV_TILE) + 2 * (LATENT - VDIM)  # 656 bytes per token
+
+
+def pack_fp8_latent(kv: torch.Tensor) -> torch.Tensor:
+    """bf16 latent rows [N, 576] -> FP8 rows uint8 [N, 656]: the 512 nope dims as
+    e4m3fn codes with one fp32 scale per 128 (scale = amax/448 of the tile, as
+    for the index data), then the 4 scales, then the 64 rope dims unchanged."""
+    N = kv.shape[0]
+    out = torch.empty(N, KV_FP8_ROW, dtype=torch.uint8, device=kv.device)
+    step = 1 << 20
+    for a in range(0, N, step):
+        b = min(N, a + step)
+        nope = kv[a:b, :VDIM].reshape(b - a, VDIM // KV_TILE, KV_TILE)
+        codes, sc = quantize_fp8_rows(nope)
+        out[a:b, :VDIM] = codes.reshape(b - a, VDIM)
+        out[a:b, VDIM: VDIM + 4 * (VDIM // KV_TILE)] = sc.contiguous().view(torch.uint8).reshape(b - a, -1)
+        out[a:b, VDIM + 4 * (VDIM // KV_TILE):] = kv[a:b, VDIM:].contiguous().view(torch.uint8)
+    return out
+
+
 def _page_bytes(D: int, idx_dtype: str = "fp8") -> int:
     return PAGE * D + (PAGE * D // MX_GROUP if idx_dtype == "mxfp8" else PAGE * 4)
 
@@ -239,6 +266,10 @@ def build_case(spec: CaseSpec, device="cpu", prefill_chunk: Optional[int] = None
     # ---- latent cache
     kv = _randn_bf16(gen, (NB * PAGE, LATENT), device)
     kv.masked_fill_(~valid.to(device).unsqueeze(-1), 0)
+    if spec.kv_dtype == "fp8":
+        kv = pack_fp8_latent(kv)
+    elif spec.kv_dtype != "bf16":
+        raise ValueError(spec.kv_dtype)
 
     # ---- queries
     if spec.prefill is not None:
@@ -321,5 +352,9 @@ def to_numpy(case: Case) -> dict:
         d["k_idx_pool"] = case.k_idx_pool.cpu().numpy()
         d["q_idx"] = case.q_idx.cpu().numpy()
         d["q_idx_scale"] = case.q_idx_scale.cpu().numpy()
-    d["kv_pool"] = bits16(case.kv_pool)
+    if case.spec.kv_dtype == "fp8":
+        d["kv_pool"] = case.kv_pool.cpu().numpy()
+    else:
+        d["kv_pool"] = bits16(case.kv_pool)
+    d["kv_dtype"] = case.spec.kv_dtype
     return d

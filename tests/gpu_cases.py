@@ -31,13 +31,14 @@ def query_case(case: synth.Case, t: int):
         kp = bits16(case.k_idx_pool[pages]) if nblk else np.zeros((0, 64, spec.D_idx), np.uint16)
     else:
         kp = case.k_idx_pool[pages].cpu().numpy() if nblk else np.zeros((0, 64 * spec.D_idx + 256), np.uint8)
-    kv = case.kv_pool.view(-1, 64, synth.LATENT)[pages].reshape(-1, synth.LATENT) if nblk else \
-        case.kv_pool[:0]
+    row_w = synth.KV_FP8_ROW if spec.kv_dtype == "fp8" else synth.LATENT
+    kv = case.kv_pool.view(-1, 64, row_w)[pages].reshape(-1, row_w) if nblk else case.kv_pool[:0]
     d = dict(T=1, B=1, H_idx=spec.H_idx, D_idx=spec.D_idx, idx_dtype=spec.idx_dtype, K=spec.K, H=spec.H,
              scale=spec.scale, num_blocks=max(nblk, 1),
              seq_lens=np.array([L], np.int32), block_table=np.arange(max(nblk, 1), dtype=np.int32)[None],
              q_seq=np.array([0], np.int32), q_visible=np.array([int(case.q_visible[t])], np.int32),
-             w=case.w[t:t + 1].cpu().numpy(), q=bits16(case.q[t:t + 1]), kv_pool=bits16(kv), k_idx_pool=kp)
+             w=case.w[t:t + 1].cpu().numpy(), q=bits16(case.q[t:t + 1]), k_idx_pool=kp,
+             kv_pool=kv.cpu().numpy() if spec.kv_dtype == "fp8" else bits16(kv), kv_dtype=spec.kv_dtype)
     if spec.idx_dtype == "bf16":
         d["q_idx"], d["q_idx_scale"] = bits16(case.q_idx[t:t + 1]), None
     else:

@@ -127,6 +127,25 @@ def test_synth_mxfp8_quantization_roundtrip():
         assert np.all(amax / scale >= 256) and np.all(amax / scale < 512)
 
 
+def test_synth_fp8_latent_roundtrip():
+    # the same draw in bf16 and in FP8 latent form: dequantized rows (oracle decode) sit within the e4m3
+    # rounding of the bf16 rows, rope dims unchanged, tile amax mapped to +-448 * scale
+    kw = dict(H_idx=8, D_idx=128, idx_dtype="fp8", K=16, H=16, lens=[100, 64, 1])
+    cb = synth.build_case(synth.CaseSpec("t", **kw))
+    cf = synth.build_case(synth.CaseSpec("t", kv_dtype="fp8", **kw))
+    assert cf.kv_pool.shape == (cb.kv_pool.shape[0], 656) and cf.kv_pool.dtype == torch.uint8
+    assert torch.equal(cb.q, cf.q) and torch.equal(cb.k_idx_pool, cf.k_idx_pool)
+    x = O.bf16_to_f64(synth.to_numpy(cb)["kv_pool"]).reshape(-1, 576)
+    deq = O.latent_rows(synth.to_numpy(cf), np.arange(x.shape[0]))
+    assert np.array_equal(deq[:, 512:], x[:, 512:])
+    xt = x[:, :512].reshape(-1, 4, 128)
+    amax = np.abs(xt).max(2, keepdims=True)
+    err = np.abs(deq[:, :512].reshape(-1, 4, 128) - xt)
+    assert np.all(err <= np.abs(xt) * 2 ** -4 + amax / 448 * 2 ** -9 + 1e-12)
+    live = amax[:, :, 0] > 0
+    assert np.allclose(np.abs(deq[:, :512].reshape(-1, 4, 128)).max(2)[live], amax[:, :, 0][live], rtol=1e-6)
+
+
 def test_synth_speculative_and_prefill_horizons():
     spec = synth.CaseSpec("t", H_idx=4, D_idx=64, idx_dtype="bf16", K=8, H=16, lens=[70, 300],
                           queries_per_seq=[1, 4])

@@ -439,3 +439,79 @@ def test_quantizers_agree_with_the_input_generators_recipe():
     m_t, e_t = synth.quantize_mxfp8_rows(xb)
     m_o, e_o = O.quantize_mxfp8(x)
     assert np.array_equal(m_t.numpy(), m_o) and np.array_equal(e_t.numpy(), e_o)
+
+
+# --------------------------------------------------------------------------- FP8 latent KV (tile 128)
+def bf16_round_bits(x):
+    """float values -> bf16 bit patterns, rounded to nearest even."""
+    return torch.tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def fp8_kv_row(codes, scales, rope_bf16_bits):
+    r = np.zeros(O.KV_FP8_ROW, np.uint8)
+    r[:512] = codes
+    r[512:528] = np.asarray(scales, "<f4").view(np.uint8)
+    r[528:656] = np.asarray(rope_bf16_bits, "<u2").view(np.uint8)
+    return r
+
+
+def test_fp8_kv_row_layout_hand_worked():
+    codes = np.zeros(512, np.uint8)
+    codes[0] = 0x38            # 1.0
+    codes[127] = 0xC0          # -2.0 (last dim of tile 0)
+    codes[128] = 0x38          # first dim of tile 1
+    codes[511] = 0x01          # smallest subnormal 2^-9, tile 3
+    rope = bf16_bits([3.0] + [0.0] * 62 + [-0.5])
+    row = fp8_kv_row(codes, [2.0, 0.25, 1.0, 8.0], rope)
+    assert row.size == 656
+    x = O.latent_rows_fp8(row[None])[0]
+    assert x.shape == (576,)
+    assert x[0] == 2.0 and x[127] == -4.0 and x[128] == 0.25 and x[511] == 8.0 * 2.0 ** -9
+    assert x[1:127].tolist() == [0.0] * 126
+    assert x[512] == 3.0 and x[575] == -0.5          # rope untouched by the scales
+
+
+def test_fp8_kv_tile_scale_moves_only_its_tile():
+    rng = np.random.default_rng(21)
+    codes = rng.integers(0, 0x7E, 512).astype(np.uint8) | (rng.integers(0, 2, 512).astype(np.uint8) << 7)
+    rope = bf16_round_bits(rng.normal(0, 1, 64))
+    base = O.latent_rows_fp8(fp8_kv_row(codes, [1.0, 1.0, 1.0, 1.0], rope)[None])[0]
+    for t in range(4):
+        sc = [1.0] * 4
+        sc[t] = 4.0
+        x = O.latent_rows_fp8(fp8_kv_row(codes, sc, rope)[None])[0]
+        moved = np.flatnonzero(x != base)
+        assert set(moved) <= set(range(128 * t, 128 * t + 128))
+        assert np.array_equal(x[128 * t: 128 * t + 128], 4.0 * base[128 * t: 128 * t + 128])
+
+
+def test_fp8_kv_attention_equals_bf16_attention_on_representable_rows():
+    # rows whose nope values are e4m3 codes times a power-of-two tile scale are exact in bf16 too:
+    # the FP8 and bf16 caches must then give identical attention
+    rng = np.random.default_rng(22)
+    n, H = 40, 4
+    codes = rng.integers(0, 0x7E, (n, 512)).astype(np.uint8) | (rng.integers(0, 2, (n, 512)).astype(np.uint8) << 7)
+    scales = 2.0 ** rng.integers(-8, 3, (n, 4))
+    rope = bf16_round_bits(rng.normal(0, 1, (n, 64)))
+    fp8_pool = np.stack([fp8_kv_row(codes[i], scales[i], rope[i]) for i in range(n)])
+    vals = O.fp8_e4m3fn_to_f64(codes) * np.repeat(scales, 128, axis=1)
+    bf_pool = np.concatenate([bf16_bits(vals), rope], axis=1)
+    assert np.array_equal(O.bf16_to_f64(bf_pool[:, :512]), vals)      # representable, so exact
+    q = bf16_round_bits(rng.normal(0, 1, (1, H, 576)))
+    slots = rng.permutation(n)[:25]
+    a = O.mla_query(dict(q=q, kv_pool=fp8_pool, kv_dtype="fp8", scale=0.05), 0, slots)
+    b = O.mla_query(dict(q=q, kv_pool=bf_pool, scale=0.05), 0, slots)
+    assert np.array_equal(a, b)
+
+
+def test_fp8_kv_rows_follow_slots_and_skip_padding():
+    rng = np.random.default_rng(23)
+    n = 6
+    pool = np.stack([fp8_kv_row(np.full(512, 0x38, np.uint8), [float(i + 1)] * 4, bf16_bits(np.full(64, float(i))))
+                     for i in range(n)])
+    rows = O.latent_rows(dict(kv_pool=pool, kv_dtype="fp8"), np.array([4, 1]))
+    assert rows[0, 0] == 5.0 and rows[1, 0] == 2.0 and rows[0, 512 + 24] == 4.0
+    # the attention of a single selected row returns that row's value dims whatever the query
+    q = bf16_round_bits(rng.normal(0, 1, (1, 2, 576)))
+    out = O.mla_query(dict(q=q, kv_pool=pool, kv_dtype="fp8", scale=0.1), 0, np.array([-1, 3, -1]))
+    assert np.array_equal(out, np.tile(O.latent_rows(dict(kv_pool=pool, kv_dtype="fp8"), [3])[0, :512], (2, 1)))
