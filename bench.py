@@ -115,7 +115,8 @@ def algorithmic_bytes(case, indices):
     for b in sorted(set(seqs)):
         sel = indices[torch.tensor([t for t in range(T) if seqs[t] == b])]
         rows += int(torch.unique(sel[sel >= 0]).numel())
-    mla_bytes = rows * 1152 + T * (s.H * 576 * 2 + s.H * 512 * 2 + 4 * s.K)
+    row_b = 656 if s.kv_dtype == "fp8" else 1152  # FP8 latent: 512 codes + 4 fp32 scales + 64 bf16 rope
+    mla_bytes = rows * row_b + T * (s.H * 576 * 2 + s.H * 512 * 2 + 4 * s.K)
     return idx_bytes, idx_bytes + mla_bytes
 
 
@@ -310,12 +311,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if spec.idx_dtype == "bf16" else f"{spec.idx_dtype}+bf16",
+        "dtype": ("bf16" if spec.idx_dtype == "bf16" else f"{spec.idx_dtype}+bf16")
+                 + ("+fp8kv" if spec.kv_dtype == "fp8" else ""),
         "data": "synthetic",
         "config": {
             "workload": spec.name, "queries": case.T, "sequences": case.B,
             "context_tokens_total": int(case.seq_lens.sum()), "index": f"{spec.idx_dtype} {spec.H_idx}x{spec.D_idx}",
-            "top_k": spec.K, "mla_heads": spec.H, "latent_dim": 576, "page_tokens": 64,
+            "top_k": spec.K, "mla_heads": spec.H, "latent_dim": 576, "latent_cache": spec.kv_dtype,
+            "page_tokens": 64,
             "input_copies_rotated": len(layers), "parallelism": "single GPU",
         },
         "roofline": {

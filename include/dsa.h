@@ -44,8 +44,16 @@
  *                          group g is e4m3(c) * 2^(scale[g] - 127)).  Group size
  *                          32 ("Optimizing Inference for Hybrid-Architecture
  *                          LLMs", section 4.2).  8448 B per page at D_idx=128.
- *   - latent pool:         [num_blocks*64][576] bf16 (512 nope + 64 rope), row
+ *   - latent pool, BF16:   [num_blocks*64][576] bf16 (512 nope + 64 rope), row
  *                          `slot` = page*64 + offset.
+ *   - latent pool, FP8:    [num_blocks*64] rows of 656 bytes: the 512 nope dims
+ *                          as e4m3fn codes, 4 little-endian fp32 scales (scale t
+ *                          covers nope dims 128t..128t+127), the 64 rope dims in
+ *                          bf16.  Nope dim d = e4m3(code[d]) * scale[d / 128]
+ *                          ("Hybrid Attention LLM Inference Acceleration",
+ *                          section 5: main KV in FP8 with one scale per token and
+ *                          128-element tile; the rope dims' storage is not given
+ *                          there and stays bf16).
  *   - block_table:         [B][max_blocks] int32, logical page -> physical page.
  *   - seq_lens:            [B] int32 cached tokens per sequence.
  *   Logical position p of sequence b lives at slot block_table[b][p/64]*64 + p%64.
@@ -60,7 +68,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 3
+#define DSA_ABI_VERSION 4
 #define DSA_PAGE_TOKENS 64
 #define DSA_LATENT_DIM 576
 #define DSA_VALUE_DIM 512
@@ -78,6 +86,11 @@ typedef enum dsa_status {
   DSA_ERR_UNSUPPORTED = 7, /* a valid but unimplemented combination               */
   DSA_ERR_HIP = 8          /* a HIP launch failed                                 */
 } dsa_status;
+
+typedef enum dsa_kv_dtype {
+  DSA_KV_BF16 = 0,         /* latent rows of 576 bf16                                   */
+  DSA_KV_FP8_TILE128 = 1   /* latent rows of 656 B: e4m3fn nope + fp32 per 128 + bf16 rope */
+} dsa_kv_dtype;
 
 typedef enum dsa_idx_dtype {
   DSA_IDX_BF16 = 0,        /* q_idx and the index-K pool are bf16                       */
@@ -135,14 +148,18 @@ typedef struct dsa_indexer_args {
  *   T          query tokens (>= 1)
  *   H          attention heads: 16, 32, 64 or 128
  *   q          [T][H][576] bf16 (rope part already applied)
- *   kv_pool    [num_blocks*64][576] bf16 latent rows
+ *   kv_pool    latent rows (layout above: bf16 [num_blocks*64][576], or FP8 rows
+ *              of 656 bytes)
  *   num_blocks pages in the pool
+ *   kv_dtype   dsa_kv_dtype of kv_pool.  FP8 rows are dequantized to bf16 on
+ *              chip (one rounding of code * scale) and attended like bf16 rows.
  */
 typedef struct dsa_mla_args {
   int32_t T, H;
   const void* q;
   const void* kv_pool;
   int64_t num_blocks;
+  int32_t kv_dtype;
 } dsa_mla_args;
 
 /* Bytes of workspace the call needs.  Pass NULL for the struct a call does not

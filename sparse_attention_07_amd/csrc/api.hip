@@ -64,6 +64,7 @@ dsa_status check_mla(const dsa_mla_args* m, int K) {
   if (!m->q || !m->kv_pool) return DSA_ERR_NULL;
   if (m->T < 1 || m->num_blocks < 1) return DSA_ERR_SHAPE;
   if (m->H != 16 && m->H != 32 && m->H != 64 && m->H != 128) return DSA_ERR_SHAPE;
+  if (m->kv_dtype != DSA_KV_BF16 && m->kv_dtype != DSA_KV_FP8_TILE128) return DSA_ERR_DTYPE;
   if ((int64_t)m->num_blocks * DSA_PAGE_TOKENS > (int64_t)INT32_MAX) return DSA_ERR_SHAPE;
   if (!aligned(m->q, 16) || !aligned(m->kv_pool, 16)) return DSA_ERR_ALIGN;
   return DSA_OK;
@@ -175,6 +176,7 @@ MlaParams make_mla_params(const dsa_mla_args* m, const int32_t* indices, int K, 
   MlaParams p{};
   p.q = (const uint16_t*)m->q;
   p.kv = (const uint16_t*)m->kv_pool;
+  p.kv8 = m->kv_dtype == DSA_KV_FP8_TILE128 ? 1 : 0;
   p.num_slots = m->num_blocks * DSA_PAGE_TOKENS;
   p.indices = indices;
   p.T = m->T;

@@ -40,7 +40,8 @@ struct IdxParams {
 
 struct MlaParams {
   const uint16_t* q;        // [T][H][576] bf16
-  const uint16_t* kv;       // [num_slots][576] bf16
+  const uint16_t* kv;       // [num_slots][576] bf16, or rows of 656 bytes (FP8, kv8 = 1)
+  int32_t kv8;              // latent rows are FP8 (e4m3fn nope, fp32 per 128, bf16 rope)
   int64_t num_slots;
   const int32_t* indices;   // [T][K]
   int32_t T, H, K;

@@ -25,7 +25,14 @@
 //  * the O rescale is skipped for a wave when no head's running max moved;
 //  * with several splits, each split stores its normalised partial output
 //    O/l as fp16 (|O/l| is bounded by the largest value entry) plus (m, l) in
-//    fp32, and a small kernel merges them with log-sum-exp weights.
+//    fp32, and a small kernel merges them with log-sum-exp weights;
+//  * FP8 latent rows (656 B: e4m3fn nope, one fp32 scale per 128 dims, bf16
+//    rope) are gathered the same way into their own 3-stage ring (41 units per
+//    row instead of 72), then all waves dequantize the tile once into the bf16
+//    tile layout above (code * scale rounded to bf16), so the MFMA phases are
+//    the bf16 ones.  That saves 43 % of the gathered bytes and of the cache's
+//    footprint, but adds LDS traffic and a barrier per tile to a kernel whose
+//    logits phase is bound by LDS reads, so it runs slightly slower than bf16.
 #include "dsa_device.h"
 #include "dsa_params.h"
 
@@ -38,12 +45,20 @@ constexpr int TILE_LOADS = (TILE_ROWS * ROW_STRIDE + 63) / 64;     // 37 wave-lo
 constexpr int STAGES = 3;
 constexpr int STAGE_BYTES = TILE_LOADS * 64 * 16;
 
+// FP8 latent rows: 512 code bytes, 4 fp32 scales, 64 bf16 rope dims
+constexpr int KV8_ROW_UNITS = 41;                                   // 656 B
+constexpr int KV8_SCALE_OFF = 512;
+constexpr int KV8_ROPE_OFF = 528;
+constexpr int KV8_TILE_LOADS = (TILE_ROWS * KV8_ROW_UNITS + 63) / 64;  // 21 wave-loads of 64 units
+constexpr int KV8_STAGE_BYTES = KV8_TILE_LOADS * 64 * 16;
+
 // byte offset, inside a stage, of bf16 element (row r, column col)
 __device__ __forceinline__ int stage_off(int r, int col) { return 16 * (r * ROW_STRIDE + (col >> 3)) + 2 * (col & 7); }
 
-template <int NW>
+template <int NW, bool KV8>
 struct MlaSmem {
-  unsigned char stage[STAGES][STAGE_BYTES];
+  unsigned char stage[STAGES][KV8 ? KV8_STAGE_BYTES : STAGE_BYTES];  // gather ring
+  unsigned char tile[KV8 ? STAGE_BYTES : 16];  // FP8 only: the dequantized bf16 tile
   uint16_t pt[16 * NW][TILE_ROWS];  // P^T as [head][row] bf16
   float alpha[16 * NW];
   float mfin[16 * NW];
@@ -51,16 +66,34 @@ struct MlaSmem {
   // followed by the slice's slots (int32)
 };
 
-template <int NW>
+// 16 e4m3fn codes times one scale -> 16 bf16 (round to nearest even)
+__device__ __forceinline__ void dequant16(const v4i c, float sc, v4i& lo, v4i& hi) {
+  uint32_t w[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const v2f a = __builtin_amdgcn_cvt_pk_f32_fp8(c[j], false);
+    const v2f b = __builtin_amdgcn_cvt_pk_f32_fp8(c[j], true);
+    __bf16 o4[4] = {(__bf16)(a[0] * sc), (__bf16)(a[1] * sc), (__bf16)(b[0] * sc), (__bf16)(b[1] * sc)};
+    const uint2 u = __builtin_bit_cast(uint2, o4);
+    w[2 * j] = u.x;
+    w[2 * j + 1] = u.y;
+  }
+  lo = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+  hi = v4i{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+}
+
+template <int NW, bool KV8>
 __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) {
   constexpr int NT = NW * 64;
   constexpr int H = 16 * NW;
   constexpr int VT = 32 / NW;  // 16-wide value tiles per wave in PV
-  constexpr int LMIN = TILE_LOADS / NW;                // DMA loads of every wave per tile
-  constexpr int LEXTRA = TILE_LOADS - LMIN * NW;       // waves [0, LEXTRA) issue one more
+  constexpr int LOADS = KV8 ? KV8_TILE_LOADS : TILE_LOADS;
+  constexpr int RUNITS = KV8 ? KV8_ROW_UNITS : ROW_STRIDE;  // units per row in the gather ring
+  constexpr int LMIN = LOADS / NW;                     // DMA loads of every wave per tile
+  constexpr int LEXTRA = LOADS - LMIN * NW;            // waves [0, LEXTRA) issue one more
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  MlaSmem<NW>& sm = *reinterpret_cast<MlaSmem<NW>*>(smem_raw);
-  int32_t* sidx = reinterpret_cast<int32_t*>(smem_raw + sizeof(MlaSmem<NW>));
+  MlaSmem<NW, KV8>& sm = *reinterpret_cast<MlaSmem<NW, KV8>*>(smem_raw);
+  int32_t* sidx = reinterpret_cast<int32_t*>(smem_raw + sizeof(MlaSmem<NW, KV8>));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -104,15 +137,16 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
     for (int k = 0; k < nl; ++k) {
       const int u0 = (first + k) * 64;
       const int u = u0 + lane;
-      int r = u / ROW_STRIDE;
-      int c = u - r * ROW_STRIDE;
-      if (r >= TILE_ROWS || c >= ROW_UNITS) {  // padding slot: fetch a harmless valid unit
+      int r = u / RUNITS;
+      int c = u - r * RUNITS;
+      if (r >= TILE_ROWS || c >= (KV8 ? KV8_ROW_UNITS : ROW_UNITS)) {  // padding slot: a harmless valid unit
         r = min(r, TILE_ROWS - 1);
         c = 0;
       }
       int slot = sidx[ti * TILE_ROWS + r];
       slot = slot < 0 ? 0 : slot;
-      const uint16_t* g = p.kv + (int64_t)slot * LATENT + 8 * c;
+      const uint16_t* g = KV8 ? p.kv + (int64_t)slot * (KV8_ROW_UNITS * 8) + 8 * c
+                              : p.kv + (int64_t)slot * LATENT + 8 * c;
       const uint32_t lds_addr =
           (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)(st + 16 * u0);
       dma16_to_lds(g, uniform(lds_addr));
@@ -126,19 +160,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
     for (int nt = 0; nt < NW; ++nt) o[vt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;  // for head hq (logits role)
 
-  if (ntiles > 0) issue_tile(0);
-  if (ntiles > 1) issue_tile(1);
-
-  for (int ti = 0; ti < ntiles; ++ti) {
-    // this wave's loads of tile ti are done when at most one newer tile is in flight
-    if (ti + 1 < ntiles)
-      __builtin_amdgcn_s_waitcnt((LMIN & 15) | ((LMIN >> 4) << 14) | (7 << 4) | (15 << 8));
-    else
-      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
-    lds_barrier_keep_dma();
-    if (ti + 2 < ntiles) issue_tile(ti + 2);
-    const unsigned char* st = sm.stage[ti % STAGES];
-
+  // logits + online softmax of tile ti from the bf16 tile at st (writes P^T, alpha)
+  auto logits_softmax = [&](int ti, const unsigned char* st) {
     // ---- logits S^T[row, head] for heads 16w..16w+15
     const uint32_t vmask = (uint32_t)ballot(lane < 32 && sidx[ti * TILE_ROWS + (lane & 31)] >= 0);
     v4f acc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
@@ -183,8 +206,9 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
       *reinterpret_cast<v4i*>(&sm.pt[hq][8 * g4]) = __builtin_bit_cast(v4i, pv);
       if (g4 == 0) sm.alpha[hq] = a_;
     }
-    lds_barrier_keep_dma();
-
+  };
+  // O^T += C^T P^T for this wave's value slice, from the bf16 tile at st
+  auto pv = [&](const unsigned char* st) {
     // ---- PV: O^T[v, head] = alpha * O^T + C^T[v, row] P^T[row, head], v in this wave's slice
     {
       float al[NW];
@@ -217,6 +241,70 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
         for (int vt = 0; vt < VT; ++vt)
           o[vt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[vt], __builtin_bit_cast(v8bf, pb), o[vt][nt], 0, 0, 0);
       }
+    }
+  };
+
+  if constexpr (!KV8) {
+    if (ntiles > 0) issue_tile(0);
+    if (ntiles > 1) issue_tile(1);
+    for (int ti = 0; ti < ntiles; ++ti) {
+      // this wave's loads of tile ti are done when at most one newer tile is in flight
+      if (ti + 1 < ntiles)
+        __builtin_amdgcn_s_waitcnt((LMIN & 15) | ((LMIN >> 4) << 14) | (7 << 4) | (15 << 8));
+      else
+        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+      lds_barrier_keep_dma();
+      if (ti + 2 < ntiles) issue_tile(ti + 2);
+      const unsigned char* st = sm.stage[ti % STAGES];
+      logits_softmax(ti, st);
+      lds_barrier_keep_dma();
+      pv(st);
+    }
+  } else {
+    // FP8 rows: once a tile's rows have landed, all waves dequantize it into the
+    // bf16 tile, then the bf16 phases run on it (three barriers per tile).
+    // Dequantizing the next tile during this tile's PV instead (two bf16
+    // tiles) measured slower: the kernel is bound by LDS traffic, not by the
+    // gather, and the extra live registers spill.
+    auto dequant = [&](int ti) {
+      const unsigned char* src = sm.stage[ti % STAGES];
+      // keep the per-thread offsets out of the registers that live across the
+      // tile loop: the thread index is made opaque here, so they are recomputed
+      int tid_o = tid;
+      asm volatile("" : "+v"(tid_o));
+#pragma unroll 1
+      for (int i = tid_o; i < TILE_ROWS * 32; i += NT) {  // 32 units of 16 codes per row
+        const int r = i >> 5, k = i & 31;
+        const unsigned char* rowp = src + 16 * KV8_ROW_UNITS * r;
+        const v4i c16 = *reinterpret_cast<const v4i*>(rowp + 16 * k);
+        const float sc = *reinterpret_cast<const float*>(rowp + KV8_SCALE_OFF + 4 * (k >> 3));
+        v4i lo, hi;
+        dequant16(c16, sc, lo, hi);
+        unsigned char* d = sm.tile + 16 * (r * ROW_STRIDE + 2 * k);
+        *reinterpret_cast<v4i*>(d) = lo;
+        *reinterpret_cast<v4i*>(d + 16) = hi;
+      }
+#pragma unroll 1
+      for (int i = tid_o; i < TILE_ROWS * 8; i += NT) {  // rope: 8 units per row, copied
+        const int r = i >> 3, j = i & 7;
+        *reinterpret_cast<v4i*>(sm.tile + 16 * (r * ROW_STRIDE + 64 + j)) =
+            *reinterpret_cast<const v4i*>(src + 16 * KV8_ROW_UNITS * r + KV8_ROPE_OFF + 16 * j);
+      }
+    };
+    if (ntiles > 0) issue_tile(0);
+    if (ntiles > 1) issue_tile(1);
+    for (int ti = 0; ti < ntiles; ++ti) {
+      if (ti + 1 < ntiles)
+        __builtin_amdgcn_s_waitcnt((LMIN & 15) | ((LMIN >> 4) << 14) | (7 << 4) | (15 << 8));
+      else
+        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+      lds_barrier_keep_dma();  // tile ti landed; every wave has left tile ti-1's PV
+      if (ti + 2 < ntiles) issue_tile(ti + 2);
+      dequant(ti);
+      lds_barrier_keep_dma();
+      logits_softmax(ti, sm.tile);
+      lds_barrier_keep_dma();
+      pv(sm.tile);
     }
   }
 
@@ -293,18 +381,17 @@ __global__ __launch_bounds__(128) void dsa_mla_combine_kernel(MlaParams p) {
   *reinterpret_cast<uint2*>(p.out + (int64_t)th * VDIM + v) = __builtin_bit_cast(uint2, b4);
 }
 
-template <int NW>
+template <int NW, bool KV8>
 static size_t mla_smem_t(int rows_per_split) {
   const int tiles = (rows_per_split + TILE_ROWS - 1) / TILE_ROWS;
-  return sizeof(MlaSmem<NW>) + (size_t)tiles * TILE_ROWS * 4;
+  return sizeof(MlaSmem<NW, KV8>) + (size_t)tiles * TILE_ROWS * 4;
 }
 
-size_t mla_smem_bytes(int rows_per_split) { return mla_smem_t<8>(rows_per_split); }
 
-template <int NW>
+template <int NW, bool KV8>
 static hipError_t launch_mla_t(const MlaParams& p, hipStream_t st) {
-  auto kfn = dsa_mla_split_kernel<NW>;
-  const size_t smem = mla_smem_t<NW>(p.rows_per_split);
+  auto kfn = dsa_mla_split_kernel<NW, KV8>;
+  const size_t smem = mla_smem_t<NW, KV8>(p.rows_per_split);
   hipError_t e = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kfn, dim3(p.S, p.T), dim3(NW * 64), smem, st, p);
@@ -314,13 +401,18 @@ static hipError_t launch_mla_t(const MlaParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_mla(const MlaParams& p, hipStream_t st) {
+template <bool KV8>
+static hipError_t launch_mla_kv(const MlaParams& p, hipStream_t st) {
   switch (p.H) {
-    case 16: return launch_mla_t<1>(p, st);
-    case 32: return launch_mla_t<2>(p, st);
-    case 64: return launch_mla_t<4>(p, st);
-    default: return launch_mla_t<8>(p, st);
+    case 16: return launch_mla_t<1, KV8>(p, st);
+    case 32: return launch_mla_t<2, KV8>(p, st);
+    case 64: return launch_mla_t<4, KV8>(p, st);
+    default: return launch_mla_t<8, KV8>(p, st);
   }
+}
+
+hipError_t launch_mla(const MlaParams& p, hipStream_t st) {
+  return p.kv8 ? launch_mla_kv<true>(p, st) : launch_mla_kv<false>(p, st);
 }
 
 }  // namespace dsa

@@ -18,6 +18,9 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 IDX_BF16 = 0
 IDX_FP8_E4M3FN = 1
 IDX_MXFP8_E4M3 = 2
+KV_BF16 = 0
+KV_FP8_TILE128 = 1
+KV_FP8_ROW = 656
 PAGE = 64
 LATENT = 576
 VDIM = 512
@@ -49,7 +52,7 @@ class IndexerArgs(ctypes.Structure):
 class MlaArgs(ctypes.Structure):
     _fields_ = [
         ("T", ctypes.c_int32), ("H", ctypes.c_int32), ("q", ctypes.c_void_p), ("kv_pool", ctypes.c_void_p),
-        ("num_blocks", ctypes.c_int64),
+        ("num_blocks", ctypes.c_int64), ("kv_dtype", ctypes.c_int32),
     ]
 
 
@@ -121,10 +124,12 @@ def indexer_args(q_idx, w, k_idx_pool, block_table, seq_lens, *, q_idx_scale=Non
 
 
 def mla_args(q, kv_pool) -> MlaArgs:
+    """kv_pool: bf16 [slots, 576], or uint8 [slots, 656] FP8 latent rows."""
     m = MlaArgs()
     m.T, m.H = q.shape[0], q.shape[1]
     m.q, m.kv_pool = _ptr(q), _ptr(kv_pool)
     m.num_blocks = kv_pool.shape[0] // PAGE
+    m.kv_dtype = KV_FP8_TILE128 if kv_pool.dtype == torch.uint8 else KV_BF16
     return m
 
 

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     m = re.search(r"#define DSA_ABI_VERSION (\d+)", open(HEADER).read())
-    assert int(m.group(1)) == 3
+    assert int(m.group(1)) == 4
     assert dsa.LIB.dsa_abi_version() == int(m.group(1))
     assert dsa.status_str(0) == "ok"
     for s in range(1, 9):
@@ -59,6 +59,7 @@ int main(void) {
   F(dsa_indexer_args, seq_lens); F(dsa_indexer_args, q_seq); F(dsa_indexer_args, q_visible);
   F(dsa_indexer_args, max_q_per_seq);
   F(dsa_mla_args, T); F(dsa_mla_args, H); F(dsa_mla_args, q); F(dsa_mla_args, kv_pool); F(dsa_mla_args, num_blocks);
+  F(dsa_mla_args, kv_dtype);
   return 0;
 }
 ''')
@@ -140,7 +141,7 @@ def call_mla(m, K=2048, idx=_base, out=_base, ws=None, ws_bytes=0):
 @pytest.mark.parametrize("kw,expect", [
     (dict(H=48), E_SHAPE), (dict(H=256), E_SHAPE), (dict(T=0), E_SHAPE), (dict(num_blocks=0), E_SHAPE),
     (dict(q=None), E_NULL), (dict(kv_pool=None), E_NULL), (dict(q=_base + 8), E_ALIGN),
-    (dict(kv_pool=_base + 2), E_ALIGN),
+    (dict(kv_pool=_base + 2), E_ALIGN), (dict(kv_dtype=2), E_DTYPE), (dict(kv_dtype=-1), E_DTYPE),
 ])
 def test_mla_argument_errors(kw, expect):
     assert call_mla(good_mla(**kw)) == expect

@@ -64,6 +64,22 @@ def test_mxfp8_prefill_paired_queries():
              queries=[0, 1, 511, 512, 1000, 2047])
 
 
+def test_fp8_latent_decode_ragged_multisplit():
+    # FP8 latent rows (656 B) dequantized on chip; several splits per query, ragged tails, short sequences
+    run_case(spec("fp8kv_ragged", lens=[40000, 1000, 3, 9000, 2047], seed=43, kv_dtype="fp8"))
+
+
+@pytest.mark.parametrize("H", [16, 32, 64])
+def test_fp8_latent_fewer_heads(H):
+    run_case(spec(f"fp8kv_h{H}", lens=[5000, 300], seed=44 + H, kv_dtype="fp8", H=H, K=1024))
+
+
+def test_fp8_latent_prefill_chunk():
+    # one split per query: the kernel writes bf16 output straight from the dequantized tiles
+    sp = spec("fp8kv_prefill", prefill=(2048, 512), seed=47, kv_dtype="fp8", K=512)
+    run_case(sp, prefill_chunk=3, queries=[0, 1, 200, 511])
+
+
 def test_speculative_multi_query_groups():
     run_case(spec("spec_mix", lens=[3000, 9000, 20000, 130], queries_per_seq=[1, 4, 2, 3], seed=7))
 
@@ -107,6 +123,10 @@ def test_full_decode_b64_128k_fp8():
 
 def test_full_decode_b64_128k_mxfp8():
     run_case(synth.PRESETS["decode_b64_128k_mxfp8"], queries=[0, 21, 63])
+
+
+def test_full_decode_b64_128k_fp8_latent():
+    run_case(synth.PRESETS["decode_b64_128k_fp8kv"], queries=[0, 17, 40, 63])
 
 
 def test_full_prefill_16k_last_chunk():
