@@ -35,7 +35,10 @@ Readings where the pages are silent (each also listed in the design notes):
     position; outputs are physical pool slots, valid ones first, then -1;
   * a query with no visible position attends over nothing and outputs zeros;
   * FP8 latent KV: per token, 4 scales over the 512 nope dims (tiles of 128),
-    the 64 rope dims kept in bf16; attention runs over the dequantized rows.
+    the 64 rope dims kept in bf16; attention runs over the dequantized rows;
+  * residual + RMSNorm after the attention: over the token's H x 512 output
+    values (no output projection is part of the layer), with a given norm
+    weight and epsilon.
 
 Every function here is pinned by tests/test_oracle_pins.py against closed
 forms, hand-worked values, a library routine (torch's float8 decode and its
@@ -274,6 +277,21 @@ def mla_query(case: dict, t: int, slots) -> np.ndarray:
     slots = slots[slots >= 0]
     qh = bf16_to_f64(np.asarray(case["q"][t]))
     return sparse_mla(qh, latent_rows(case, slots), case["scale"])
+
+
+def residual_rmsnorm(attn: np.ndarray, residual: np.ndarray, gamma: np.ndarray, eps: float):
+    """The step after the attention ("Day-0 Inference Adaptation for LLMs",
+    operator section 2: the residual connection and normalization that follow
+    sparse attention, fused into its tail).  Per query token, over the token's
+    whole output vector (H heads x 512, flattened): y = attn + residual (the new
+    residual stream), out = y / sqrt(mean(y^2) + eps) * gamma.  Returns (y, out)
+    as float64, same shapes as attn."""
+    a = np.asarray(attn, dtype=np.float64)
+    T = a.shape[0]
+    y = a.reshape(T, -1) + np.asarray(residual, dtype=np.float64).reshape(T, -1)
+    ms = np.mean(y * y, axis=1, keepdims=True)
+    out = y / np.sqrt(ms + eps) * np.asarray(gamma, dtype=np.float64).reshape(1, -1)
+    return y.reshape(a.shape), out.reshape(a.shape)
 
 
 def layer_query(case: dict, t: int) -> dict:

@@ -515,3 +515,42 @@ def test_fp8_kv_rows_follow_slots_and_skip_padding():
     q = bf16_round_bits(rng.normal(0, 1, (1, 2, 576)))
     out = O.mla_query(dict(q=q, kv_pool=pool, kv_dtype="fp8", scale=0.1), 0, np.array([-1, 3, -1]))
     assert np.array_equal(out, np.tile(O.latent_rows(dict(kv_pool=pool, kv_dtype="fp8"), [3])[0, :512], (2, 1)))
+
+
+# --------------------------------------------------------------------------- residual + RMSNorm after the attention
+def test_residual_rmsnorm_matches_torch_rms_norm_float64():
+    # library routine: torch's RMSNorm over the last dim, in float64
+    rng = np.random.default_rng(31)
+    T, H = 3, 4
+    attn, res = rng.normal(0, 1, (T, H, 512)), rng.normal(0, 2, (T, H, 512))
+    gamma = rng.normal(1, 0.3, H * 512)
+    y, out = O.residual_rmsnorm(attn, res, gamma, 1e-6)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(attn + res).reshape(T, -1), (H * 512,),
+                                       torch.from_numpy(gamma), eps=1e-6).reshape(T, H, 512).numpy()
+    assert np.array_equal(y, attn + res)
+    assert np.allclose(out, ref, rtol=1e-13, atol=1e-13)
+
+
+def test_residual_rmsnorm_closed_forms():
+    H = 2
+    # a constant row c: mean(y^2) = c^2, so out = c / sqrt(c^2 + eps) * gamma
+    attn = np.full((1, H, 512), 1.5)
+    res = np.full((1, H, 512), -3.5)
+    gamma = np.linspace(-2, 2, H * 512)
+    y, out = O.residual_rmsnorm(attn, res, gamma, 0.25)
+    assert np.all(y == -2.0)
+    assert np.allclose(out.reshape(-1), -2.0 / np.sqrt(4.0 + 0.25) * gamma, rtol=1e-15, atol=0)
+    # one non-zero entry v in N values: mean = v^2/N, out there = v / sqrt(v^2/N) = sqrt(N) (eps = 0)
+    attn = np.zeros((1, H, 512))
+    attn[0, 1, 7] = 3.0
+    _, out = O.residual_rmsnorm(attn, np.zeros_like(attn), np.ones(H * 512), 0.0)
+    assert np.isclose(out[0, 1, 7], np.sqrt(H * 512)) and np.count_nonzero(out) == 1
+    # tokens are normalized separately, and scaling a token (eps = 0) changes nothing
+    rng = np.random.default_rng(32)
+    a = rng.normal(0, 1, (2, H, 512))
+    _, o1 = O.residual_rmsnorm(a, np.zeros_like(a), np.ones(H * 512), 0.0)
+    a2 = a.copy()
+    a2[1] *= 1000.0
+    _, o2 = O.residual_rmsnorm(a2, np.zeros_like(a2), np.ones(H * 512), 0.0)
+    assert np.allclose(o1, o2, rtol=1e-12, atol=1e-12)
+    assert np.allclose(np.mean(o1.reshape(2, -1) ** 2, axis=1), 1.0, rtol=1e-12)
