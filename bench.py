@@ -35,6 +35,9 @@ def parse():
     ap.add_argument("--op", choices=("layer", "quantize"), default="layer",
                     help="layer: the DSA layer step (default); quantize: the index-query quantization that "
                          "prepares the workload's q_idx from its bf16 projection")
+    ap.add_argument("--epilogue", action="store_true",
+                    help="layer: fuse residual + RMSNorm (synthetic bf16 residual and norm weight) into the "
+                         "attention's tail; the step then also writes the new residual stream")
     ap.add_argument("--quant-dtype", choices=("fp8", "mxfp8"), default=None,
                     help="--op quantize: the code format (default: the workload's index dtype)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -94,7 +97,7 @@ def copy_calibration(dev):
     print(json.dumps({"copy_calibration_bytes": 1 << 30, "launches": 3}), flush=True)
 
 
-def algorithmic_bytes(case, indices):
+def algorithmic_bytes(case, indices, epilogue=False):
     """Bytes the method itself must move per step: the index-K cache once per
     sequence (codes + scales), the tables, each query's indexer query, weights
     and index row, the gathered latent rows (the union over a sequence's
@@ -117,6 +120,8 @@ def algorithmic_bytes(case, indices):
         rows += int(torch.unique(sel[sel >= 0]).numel())
     row_b = 656 if s.kv_dtype == "fp8" else 1152  # FP8 latent: 512 codes + 4 fp32 scales + 64 bf16 rope
     mla_bytes = rows * row_b + T * (s.H * 576 * 2 + s.H * 512 * 2 + 4 * s.K)
+    if epilogue:  # residual read, new residual written, norm weight read
+        mla_bytes += T * s.H * 512 * 2 * 2 + s.H * 512 * 2
     return idx_bytes, idx_bytes + mla_bytes
 
 
@@ -250,19 +255,25 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     case = synth.build_case(spec, device=dev, prefill_chunk=prefill_chunk)
+    ep_kw = {}
+    if args.epilogue:
+        g = torch.Generator(device=dev).manual_seed(spec.seed + 7)
+        res = torch.randn(case.T, spec.H, 512, generator=g, device=dev).to(torch.bfloat16)
+        gam = (1.0 + 0.1 * torch.randn(spec.H * 512, generator=g, device=dev)).to(torch.bfloat16)
+        ep_kw = dict(residual=res, norm_weight=gam, residual_out=torch.empty_like(res), eps=1e-6)
     if args.op == "quantize":
         bench_quantize(args, spec, case)
         if args.copy_calibration:
             copy_calibration(dev)
         return
-    layers = [dsa.layer_from_case(case)]
+    layers = [dsa.layer_from_case(case, **ep_kw)]
     extra_cases = []
     for _ in range(max(0, args.copies - 1)):
         c2 = synth.Case(**{f: getattr(case, f) for f in case.__dataclass_fields__})
         c2.k_idx_pool = case.k_idx_pool.clone()
         c2.kv_pool = case.kv_pool.clone()
         extra_cases.append(c2)
-        layers.append(dsa.layer_from_case(c2))
+        layers.append(dsa.layer_from_case(c2, **ep_kw))
     torch.cuda.synchronize()
 
     for i in range(args.warmup):
@@ -298,7 +309,7 @@ def main():
     torch.cuda.synchronize()
     idx_ms = e0.elapsed_time(e1) / n_idx
 
-    idx_bytes, layer_bytes = algorithmic_bytes(case, layers[0].indices)
+    idx_bytes, layer_bytes = algorithmic_bytes(case, layers[0].indices, args.epilogue)
     achieved = idx_bytes / (idx_ms * 1e-3) / 1e9
     line = {
         "metric": METRIC,
@@ -320,6 +331,7 @@ def main():
             "top_k": spec.K, "mla_heads": spec.H, "latent_dim": 576, "latent_cache": spec.kv_dtype,
             "page_tokens": 64,
             "input_copies_rotated": len(layers), "parallelism": "single GPU",
+            "epilogue": "residual + RMSNorm" if args.epilogue else None,
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",

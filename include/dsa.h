@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 4
+#define DSA_ABI_VERSION 5
 #define DSA_PAGE_TOKENS 64
 #define DSA_LATENT_DIM 576
 #define DSA_VALUE_DIM 512
@@ -153,6 +153,23 @@ typedef struct dsa_indexer_args {
  *   num_blocks pages in the pool
  *   kv_dtype   dsa_kv_dtype of kv_pool.  FP8 rows are dequantized to bf16 on
  *              chip (one rounding of code * scale) and attended like bf16 rows.
+ *
+ * Optional epilogue: residual connection + RMSNorm fused into the attention's
+ * tail ("Day-0 Inference Adaptation for LLMs", operator section 2).  When
+ * `residual` is non-NULL, per query token t over its H*512 output values:
+ *   residual_out[t] = bf16(attn[t] + residual[t])            (the new residual)
+ *   out[t]          = bf16(r * residual_out[t] * norm_weight),
+ *   r = 1 / sqrt(mean(residual_out[t]^2) + norm_eps)
+ * (the norm reads the stored bf16 residual_out), and attn itself is never
+ * written.  With one split per query everything happens in the attention
+ * kernel; with several, the split combine adds the residual and a small
+ * kernel applies the norm.
+ *   residual      [T][H][512] bf16 or NULL (no epilogue; the fields below are
+ *                 then ignored)
+ *   norm_weight   [H*512] bf16, 16-byte aligned
+ *   residual_out  [T][H][512] bf16, 16-byte aligned; may be the residual
+ *                 buffer itself (residual: 8-byte aligned)
+ *   norm_eps      >= 0
  */
 typedef struct dsa_mla_args {
   int32_t T, H;
@@ -160,6 +177,10 @@ typedef struct dsa_mla_args {
   const void* kv_pool;
   int64_t num_blocks;
   int32_t kv_dtype;
+  const void* residual;
+  const void* norm_weight;
+  void* residual_out;
+  float norm_eps;
 } dsa_mla_args;
 
 /* Bytes of workspace the call needs.  Pass NULL for the struct a call does not

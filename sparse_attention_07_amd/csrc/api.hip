@@ -33,7 +33,7 @@ struct IdxPlan {
 
 struct MlaPlan {
   int S = 1, RPS = 0;
-  size_t off_o = 0, off_ml = 0, end = 0;
+  size_t off_o = 0, off_ml = 0, off_ss = 0, end = 0;
 };
 
 dsa_status check_indexer(const dsa_indexer_args* a, int K) {
@@ -65,6 +65,12 @@ dsa_status check_mla(const dsa_mla_args* m, int K) {
   if (m->T < 1 || m->num_blocks < 1) return DSA_ERR_SHAPE;
   if (m->H != 16 && m->H != 32 && m->H != 64 && m->H != 128) return DSA_ERR_SHAPE;
   if (m->kv_dtype != DSA_KV_BF16 && m->kv_dtype != DSA_KV_FP8_TILE128) return DSA_ERR_DTYPE;
+  if (m->residual) {
+    if (!m->norm_weight || !m->residual_out) return DSA_ERR_NULL;
+    if (!(m->norm_eps >= 0.f) || std::isinf(m->norm_eps)) return DSA_ERR_SHAPE;
+    if (!aligned(m->residual, 8) || !aligned(m->norm_weight, 16) || !aligned(m->residual_out, 16))
+      return DSA_ERR_ALIGN;
+  }
   if ((int64_t)m->num_blocks * DSA_PAGE_TOKENS > (int64_t)INT32_MAX) return DSA_ERR_SHAPE;
   if (!aligned(m->q, 16) || !aligned(m->kv_pool, 16)) return DSA_ERR_ALIGN;
   return DSA_OK;
@@ -132,6 +138,10 @@ MlaPlan plan_mla(const dsa_mla_args* m, int K, size_t base) {
     off = align_up(off + (size_t)m->T * S * m->H * DSA_VALUE_DIM * 2, 256);
     pl.off_ml = off;
     off = align_up(off + (size_t)m->T * S * m->H * 2 * 4, 256);
+    if (m->residual) {
+      pl.off_ss = off;
+      off = align_up(off + (size_t)m->T * m->H * 4, 256);
+    }
   }
   pl.end = off;
   return pl;
@@ -188,6 +198,11 @@ MlaParams make_mla_params(const dsa_mla_args* m, const int32_t* indices, int K, 
   p.out = (uint16_t*)out;
   p.part_o = pl.S > 1 ? (_Float16*)(ws + pl.off_o) : nullptr;
   p.part_ml = pl.S > 1 ? (float*)(ws + pl.off_ml) : nullptr;
+  p.residual = (const uint16_t*)m->residual;
+  p.gamma = (const uint16_t*)m->norm_weight;
+  p.res_out = (uint16_t*)m->residual_out;
+  p.eps = m->norm_eps;
+  p.ssq = (pl.S > 1 && m->residual) ? (float*)(ws + pl.off_ss) : nullptr;
   return p;
 }
 

@@ -43,6 +43,13 @@ __device__ __forceinline__ float sum_lane_groups(float v) {
   return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
+// Sum over all 64 lanes of a wave, returned to every lane (epilogue use only).
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) v += __shfl_xor(v, m);
+  return sum_lane_groups(v);
+}
+
 __device__ __forceinline__ float max_lane_groups(float v) {
   auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   float s = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));

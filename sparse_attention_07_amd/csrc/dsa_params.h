@@ -51,6 +51,12 @@ struct MlaParams {
   uint16_t* out;            // [T][H][512] bf16
   _Float16* part_o;         // [T][S][H][512] fp16, normalised O/l of each split (S > 1)
   float* part_ml;           // [T][S][H][2]   fp32 (S > 1)
+  // residual + RMSNorm epilogue (residual == nullptr: none)
+  const uint16_t* residual; // [T][H][512] bf16
+  const uint16_t* gamma;    // [H*512] bf16
+  uint16_t* res_out;        // [T][H][512] bf16
+  float eps;
+  float* ssq;               // [T][H] fp32 sums of squares of res_out (S > 1)
 };
 
 }  // namespace dsa

@@ -26,6 +26,10 @@
 //  * with several splits, each split stores its normalised partial output
 //    O/l as fp16 (|O/l| is bounded by the largest value entry) plus (m, l) in
 //    fp32, and a small kernel merges them with log-sum-exp weights;
+//  * optional residual + RMSNorm epilogue over the token's H x 512 values: with
+//    one split the workgroup holds the whole token and finishes it; with
+//    several, the combine adds the residual and stores per-head sums of
+//    squares, and a small kernel applies the norm;
 //  * FP8 latent rows (656 B: e4m3fn nope, one fp32 scale per 128 dims, bf16
 //    rope) are gathered the same way into their own 3-stage ring (41 units per
 //    row instead of 72), then all waves dequantize the tile once into the bf16
@@ -63,6 +67,7 @@ struct MlaSmem {
   float alpha[16 * NW];
   float mfin[16 * NW];
   float lfin[16 * NW];
+  float red[NW];  // per-wave partial sums (residual + RMSNorm epilogue)
   // followed by the slice's slots (int32)
 };
 
@@ -317,6 +322,58 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
     }
   }
   lds_barrier();
+  if (p.S == 1 && p.residual) {
+    // y = attn + residual (stored as bf16), then RMSNorm over the token with the
+    // stored values; this workgroup holds all H x 512 values of token t
+    float ssl = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < NW; ++nt) {
+      const int h = 16 * nt + n16;
+      const float l_tot = sm.lfin[h];
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      const int64_t rbase = ((int64_t)t * H + h) * VDIM;
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt) {
+        const int v = (wave * VT + vt) * 16 + 4 * g4;
+        const uint2 rr = *reinterpret_cast<const uint2*>(p.residual + rbase + v);
+        const float res[4] = {__uint_as_float(rr.x << 16), __uint_as_float(rr.x & 0xffff0000u),
+                              __uint_as_float(rr.y << 16), __uint_as_float(rr.y & 0xffff0000u)};
+        __bf16 b4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          b4[i] = (__bf16)(o[vt][nt][i] * inv + res[i]);
+          const float yb = (float)b4[i];
+          o[vt][nt][i] = yb;
+          ssl += yb * yb;
+        }
+        *reinterpret_cast<uint2*>(p.res_out + rbase + v) = __builtin_bit_cast(uint2, b4);
+      }
+    }
+    ssl = wave_sum_f32(ssl);
+    if (lane == 0) sm.red[wave] = ssl;
+    lds_barrier();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) tot += sm.red[w];
+    const float r = 1.f / sqrtf(tot / (float)(H * VDIM) + p.eps);
+#pragma unroll
+    for (int nt = 0; nt < NW; ++nt) {
+      const int h = 16 * nt + n16;
+      uint16_t* orow = p.out + ((int64_t)t * H + h) * VDIM;
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt) {
+        const int v = (wave * VT + vt) * 16 + 4 * g4;
+        const uint2 gg = *reinterpret_cast<const uint2*>(p.gamma + h * VDIM + v);
+        const float gm[4] = {__uint_as_float(gg.x << 16), __uint_as_float(gg.x & 0xffff0000u),
+                             __uint_as_float(gg.y << 16), __uint_as_float(gg.y & 0xffff0000u)};
+        __bf16 b4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b4[i] = (__bf16)(o[vt][nt][i] * r * gm[i]);
+        *reinterpret_cast<uint2*>(orow + v) = __builtin_bit_cast(uint2, b4);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int nt = 0; nt < NW; ++nt) {
     const int h = 16 * nt + n16;
@@ -376,9 +433,53 @@ __global__ __launch_bounds__(128) void dsa_mla_combine_kernel(MlaParams p) {
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   __bf16 b4[4];
+  if (!p.residual) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) b4[i] = (__bf16)(acc[i] * inv);
-  *reinterpret_cast<uint2*>(p.out + (int64_t)th * VDIM + v) = __builtin_bit_cast(uint2, b4);
+    for (int i = 0; i < 4; ++i) b4[i] = (__bf16)(acc[i] * inv);
+    *reinterpret_cast<uint2*>(p.out + (int64_t)th * VDIM + v) = __builtin_bit_cast(uint2, b4);
+    return;
+  }
+  // residual epilogue: store y = attn + residual (bf16) and this head's sum of
+  // squares of the stored values; the norm itself needs every head of the token
+  const uint2 rr = *reinterpret_cast<const uint2*>(p.residual + (int64_t)th * VDIM + v);
+  const float res[4] = {__uint_as_float(rr.x << 16), __uint_as_float(rr.x & 0xffff0000u),
+                        __uint_as_float(rr.y << 16), __uint_as_float(rr.y & 0xffff0000u)};
+  float ssl = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    b4[i] = (__bf16)(acc[i] * inv + res[i]);
+    const float yb = (float)b4[i];
+    ssl += yb * yb;
+  }
+  *reinterpret_cast<uint2*>(p.res_out + (int64_t)th * VDIM + v) = __builtin_bit_cast(uint2, b4);
+  __shared__ float red[2];
+  ssl = wave_sum_f32(ssl);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ssl;
+  __syncthreads();
+  if (threadIdx.x == 0) p.ssq[th] = red[0] + red[1];
+}
+
+// RMSNorm of the stored residual stream: a workgroup covers 4 (query, head)
+// rows of one query (H is a multiple of 4), 8 values per thread;
+// out = y / sqrt(mean over the token's H x 512 values of y^2 + eps) * gamma
+__global__ __launch_bounds__(256) void dsa_mla_norm_kernel(MlaParams p) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // t * H + h
+  const int t = (int)(row / p.H), h = (int)(row % p.H);
+  const int v = (threadIdx.x & 63) * 8;
+  float part = 0.f;
+  for (int i = threadIdx.x & 63; i < p.H; i += 64) part += p.ssq[(int64_t)t * p.H + i];
+  const float tot = wave_sum_f32(part);
+  const float r = 1.f / sqrtf(tot / (float)(p.H * VDIM) + p.eps);
+  const uint4 yy = *reinterpret_cast<const uint4*>(p.res_out + row * VDIM + v);
+  const uint4 gg = *reinterpret_cast<const uint4*>(p.gamma + h * VDIM + v);
+  const uint32_t yw[4] = {yy.x, yy.y, yy.z, yy.w}, gw[4] = {gg.x, gg.y, gg.z, gg.w};
+  __bf16 b8[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    b8[2 * j] = (__bf16)(__uint_as_float(yw[j] << 16) * r * __uint_as_float(gw[j] << 16));
+    b8[2 * j + 1] = (__bf16)(__uint_as_float(yw[j] & 0xffff0000u) * r * __uint_as_float(gw[j] & 0xffff0000u));
+  }
+  *reinterpret_cast<uint4*>(p.out + row * VDIM + v) = __builtin_bit_cast(uint4, b8);
 }
 
 template <int NW, bool KV8>
@@ -398,6 +499,9 @@ static hipError_t launch_mla_t(const MlaParams& p, hipStream_t st) {
   e = hipGetLastError();
   if (e != hipSuccess || p.S == 1) return e;
   hipLaunchKernelGGL(dsa_mla_combine_kernel, dim3(p.T * p.H), dim3(128), 0, st, p);
+  e = hipGetLastError();
+  if (e != hipSuccess || !p.residual) return e;
+  hipLaunchKernelGGL(dsa_mla_norm_kernel, dim3(p.T * p.H / 4), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

@@ -53,6 +53,8 @@ class MlaArgs(ctypes.Structure):
     _fields_ = [
         ("T", ctypes.c_int32), ("H", ctypes.c_int32), ("q", ctypes.c_void_p), ("kv_pool", ctypes.c_void_p),
         ("num_blocks", ctypes.c_int64), ("kv_dtype", ctypes.c_int32),
+        ("residual", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p), ("residual_out", ctypes.c_void_p),
+        ("norm_eps", ctypes.c_float),
     ]
 
 
@@ -123,13 +125,17 @@ def indexer_args(q_idx, w, k_idx_pool, block_table, seq_lens, *, q_idx_scale=Non
     return a
 
 
-def mla_args(q, kv_pool) -> MlaArgs:
-    """kv_pool: bf16 [slots, 576], or uint8 [slots, 656] FP8 latent rows."""
+def mla_args(q, kv_pool, *, residual=None, norm_weight=None, residual_out=None, eps: float = 1e-6) -> MlaArgs:
+    """kv_pool: bf16 [slots, 576], or uint8 [slots, 656] FP8 latent rows.  With
+    `residual` ([T, H, 512] bf16), the output becomes RMSNorm(attn + residual) *
+    norm_weight and residual_out receives attn + residual."""
     m = MlaArgs()
     m.T, m.H = q.shape[0], q.shape[1]
     m.q, m.kv_pool = _ptr(q), _ptr(kv_pool)
     m.num_blocks = kv_pool.shape[0] // PAGE
     m.kv_dtype = KV_FP8_TILE128 if kv_pool.dtype == torch.uint8 else KV_BF16
+    m.residual, m.norm_weight, m.residual_out = _ptr(residual), _ptr(norm_weight), _ptr(residual_out)
+    m.norm_eps = eps
     return m
 
 
@@ -159,9 +165,11 @@ def indexer_topk(q_idx, w, k_idx_pool, block_table, seq_lens, K: int, *, q_idx_s
 
 
 def sparse_mla_attn(q, kv_pool, indices, scale: float, *, out: Optional[torch.Tensor] = None,
-                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Sparse MLA: bf16 [T, H, 512] over the latent rows at `indices` (-1 skipped)."""
-    m = mla_args(q, kv_pool)
+                    workspace: Optional[torch.Tensor] = None, residual=None, norm_weight=None, residual_out=None,
+                    eps: float = 1e-6) -> torch.Tensor:
+    """Sparse MLA: bf16 [T, H, 512] over the latent rows at `indices` (-1 skipped);
+    with `residual`, RMSNorm(attn + residual) * norm_weight (see mla_args)."""
+    m = mla_args(q, kv_pool, residual=residual, norm_weight=norm_weight, residual_out=residual_out, eps=eps)
     K = indices.shape[1]
     if out is None:
         out = torch.empty(m.T, m.H, VDIM, dtype=torch.bfloat16, device=q.device)
@@ -199,11 +207,13 @@ class Layer:
 
     def __init__(self, q_idx, w, k_idx_pool, block_table, seq_lens, q, kv_pool, K: int, scale: float, *,
                  q_idx_scale=None, q_seq=None, q_visible=None, max_q_per_seq: int = 1,
-                 want_indices: bool = True):
-        self._keep = (q_idx, w, k_idx_pool, block_table, seq_lens, q, kv_pool, q_idx_scale, q_seq, q_visible)
+                 want_indices: bool = True, residual=None, norm_weight=None, residual_out=None, eps: float = 1e-6):
+        self._keep = (q_idx, w, k_idx_pool, block_table, seq_lens, q, kv_pool, q_idx_scale, q_seq, q_visible,
+                      residual, norm_weight, residual_out)
         self.idx = indexer_args(q_idx, w, k_idx_pool, block_table, seq_lens, q_idx_scale=q_idx_scale,
                                 q_seq=q_seq, q_visible=q_visible, max_q_per_seq=max_q_per_seq)
-        self.mla = mla_args(q, kv_pool)
+        self.mla = mla_args(q, kv_pool, residual=residual, norm_weight=norm_weight, residual_out=residual_out,
+                            eps=eps)
         self.K, self.scale = K, float(scale)
         dev = q.device
         self.out = torch.empty(self.mla.T, self.mla.H, VDIM, dtype=torch.bfloat16, device=dev)
@@ -220,9 +230,10 @@ class Layer:
         return self.out
 
 
-def layer_from_case(case, want_indices: bool = True) -> Layer:
-    """Layer over a synthetic case (see synth.py)."""
+def layer_from_case(case, want_indices: bool = True, **epilogue) -> Layer:
+    """Layer over a synthetic case (see synth.py); `epilogue` takes residual,
+    norm_weight, residual_out and eps."""
     s = case.spec
     return Layer(case.q_idx, case.w, case.k_idx_pool, case.block_table, case.seq_lens, case.q, case.kv_pool, s.K,
                  s.scale, q_idx_scale=case.q_idx_scale, q_seq=case.q_seq, q_visible=case.q_visible,
-                 max_q_per_seq=case.max_q_per_seq, want_indices=want_indices)
+                 max_q_per_seq=case.max_q_per_seq, want_indices=want_indices, **epilogue)

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     m = re.search(r"#define DSA_ABI_VERSION (\d+)", open(HEADER).read())
-    assert int(m.group(1)) == 4
+    assert int(m.group(1)) == 5
     assert dsa.LIB.dsa_abi_version() == int(m.group(1))
     assert dsa.status_str(0) == "ok"
     for s in range(1, 9):
@@ -59,7 +59,8 @@ int main(void) {
   F(dsa_indexer_args, seq_lens); F(dsa_indexer_args, q_seq); F(dsa_indexer_args, q_visible);
   F(dsa_indexer_args, max_q_per_seq);
   F(dsa_mla_args, T); F(dsa_mla_args, H); F(dsa_mla_args, q); F(dsa_mla_args, kv_pool); F(dsa_mla_args, num_blocks);
-  F(dsa_mla_args, kv_dtype);
+  F(dsa_mla_args, kv_dtype); F(dsa_mla_args, residual); F(dsa_mla_args, norm_weight);
+  F(dsa_mla_args, residual_out); F(dsa_mla_args, norm_eps);
   return 0;
 }
 ''')
@@ -142,6 +143,16 @@ def call_mla(m, K=2048, idx=_base, out=_base, ws=None, ws_bytes=0):
     (dict(H=48), E_SHAPE), (dict(H=256), E_SHAPE), (dict(T=0), E_SHAPE), (dict(num_blocks=0), E_SHAPE),
     (dict(q=None), E_NULL), (dict(kv_pool=None), E_NULL), (dict(q=_base + 8), E_ALIGN),
     (dict(kv_pool=_base + 2), E_ALIGN), (dict(kv_dtype=2), E_DTYPE), (dict(kv_dtype=-1), E_DTYPE),
+    # residual + RMSNorm epilogue
+    (dict(residual=_base), E_NULL), (dict(residual=_base, norm_weight=_base), E_NULL),
+    (dict(residual=_base, norm_weight=_base, residual_out=_base, norm_eps=-1.0), E_SHAPE),
+    (dict(residual=_base, norm_weight=_base, residual_out=_base, norm_eps=float("nan")), E_SHAPE),
+    (dict(residual=_base, norm_weight=_base, residual_out=_base, norm_eps=float("inf")), E_SHAPE),
+    (dict(residual=_base + 4, norm_weight=_base, residual_out=_base), E_ALIGN),
+    (dict(residual=_base, norm_weight=_base + 2, residual_out=_base), E_ALIGN),
+    (dict(residual=_base, norm_weight=_base, residual_out=_base + 4), E_ALIGN),
+    (dict(residual=_base, norm_weight=_base + 8, residual_out=_base), E_ALIGN),
+    (dict(residual=_base, norm_weight=_base, residual_out=_base + 8), E_ALIGN),
 ])
 def test_mla_argument_errors(kw, expect):
     assert call_mla(good_mla(**kw)) == expect
@@ -156,6 +167,10 @@ def test_mla_null_and_workspace():
     # 4 queries -> the rows are split and partial results need workspace
     assert dsa.workspace_bytes(None, good_mla(), 2048) > 0
     assert call_mla(good_mla()) == E_WS
+    # the residual epilogue adds one fp32 sum of squares per (query, head) when rows are split
+    ep = dict(residual=_base, norm_weight=_base, residual_out=_base, norm_eps=1e-6)
+    assert dsa.workspace_bytes(None, good_mla(**ep), 2048) >= dsa.workspace_bytes(None, good_mla(), 2048) + 4 * 128 * 4
+    assert dsa.workspace_bytes(None, good_mla(T=1000, **ep), 2048) == dsa.workspace_bytes(None, good_mla(T=1000), 2048)
 
 
 def test_layer_argument_errors():
