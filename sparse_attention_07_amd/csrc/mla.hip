@@ -408,14 +408,16 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
 }
 
 // Merge S partial results per (query, head), with O_s = l_s * (O/l)_s:
-// out = sum_s e^(m_s-M) l_s (O/l)_s / sum_s e^(m_s-M) l_s
-__global__ __launch_bounds__(128) void dsa_mla_combine_kernel(MlaParams p) {
-  const int th = blockIdx.x;  // t * H + h
-  const int t = th / p.H, h = th % p.H;
-  const int v = threadIdx.x * 4;
+// out = sum_s e^(m_s-M) l_s (O/l)_s / sum_s e^(m_s-M) l_s.
+// A workgroup covers 4 (query, head) rows (one wave each, 8 values per lane);
+// H is a multiple of 4.
+__global__ __launch_bounds__(256) void dsa_mla_combine_kernel(MlaParams p) {
+  const int64_t th = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // t * H + h
+  const int t = (int)(th / p.H), h = (int)(th % p.H);
+  const int v = (threadIdx.x & 63) * 8;
   float M = -INFINITY;
   for (int s = 0; s < p.S; ++s) M = fmaxf(M, p.part_ml[(((int64_t)t * p.S + s) * p.H + h) * 2]);
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
   if (M != -INFINITY) {
     for (int s = 0; s < p.S; ++s) {
@@ -424,39 +426,43 @@ __global__ __launch_bounds__(128) void dsa_mla_combine_kernel(MlaParams p) {
       if (ms == -INFINITY) continue;
       const float wgt = exp2f(ms - M) * ls;
       L += wgt;
-      const uint2 raw = *reinterpret_cast<const uint2*>(p.part_o + rowi * VDIM + v);
-      _Float16 h4[4];
-      __builtin_memcpy(h4, &raw, 8);
+      const uint4 raw = *reinterpret_cast<const uint4*>(p.part_o + rowi * VDIM + v);
+      _Float16 h8[8];
+      __builtin_memcpy(h8, &raw, 16);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] += wgt * (float)h4[i];
+      for (int i = 0; i < 8; ++i) acc[i] += wgt * (float)h8[i];
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  __bf16 b4[4];
+  __bf16 b8[8];
   if (!p.residual) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) b4[i] = (__bf16)(acc[i] * inv);
-    *reinterpret_cast<uint2*>(p.out + (int64_t)th * VDIM + v) = __builtin_bit_cast(uint2, b4);
+    for (int i = 0; i < 8; ++i) b8[i] = (__bf16)(acc[i] * inv);
+    uint2* o2 = reinterpret_cast<uint2*>(p.out + th * VDIM + v);  // the output is 8-byte aligned
+    const uint4 u = __builtin_bit_cast(uint4, b8);
+    o2[0] = make_uint2(u.x, u.y);
+    o2[1] = make_uint2(u.z, u.w);
     return;
   }
   // residual epilogue: store y = attn + residual (bf16) and this head's sum of
   // squares of the stored values; the norm itself needs every head of the token
-  const uint2 rr = *reinterpret_cast<const uint2*>(p.residual + (int64_t)th * VDIM + v);
-  const float res[4] = {__uint_as_float(rr.x << 16), __uint_as_float(rr.x & 0xffff0000u),
-                        __uint_as_float(rr.y << 16), __uint_as_float(rr.y & 0xffff0000u)};
+  const uint2* r2 = reinterpret_cast<const uint2*>(p.residual + th * VDIM + v);  // 8-byte aligned
+  const uint2 ra = r2[0], rb = r2[1];
+  const uint32_t rw[4] = {ra.x, ra.y, rb.x, rb.y};
   float ssl = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    b4[i] = (__bf16)(acc[i] * inv + res[i]);
-    const float yb = (float)b4[i];
+  for (int j = 0; j < 4; ++j) {
+    b8[2 * j] = (__bf16)(acc[2 * j] * inv + __uint_as_float(rw[j] << 16));
+    b8[2 * j + 1] = (__bf16)(acc[2 * j + 1] * inv + __uint_as_float(rw[j] & 0xffff0000u));
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float yb = (float)b8[i];
     ssl += yb * yb;
   }
-  *reinterpret_cast<uint2*>(p.res_out + (int64_t)th * VDIM + v) = __builtin_bit_cast(uint2, b4);
-  __shared__ float red[2];
+  *reinterpret_cast<uint4*>(p.res_out + th * VDIM + v) = __builtin_bit_cast(uint4, b8);
   ssl = wave_sum_f32(ssl);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ssl;
-  __syncthreads();
-  if (threadIdx.x == 0) p.ssq[th] = red[0] + red[1];
+  if ((threadIdx.x & 63) == 0) p.ssq[th] = ssl;
 }
 
 // RMSNorm of the stored residual stream: a workgroup covers 4 (query, head)
@@ -498,7 +504,7 @@ static hipError_t launch_mla_t(const MlaParams& p, hipStream_t st) {
   hipLaunchKernelGGL(kfn, dim3(p.S, p.T), dim3(NW * 64), smem, st, p);
   e = hipGetLastError();
   if (e != hipSuccess || p.S == 1) return e;
-  hipLaunchKernelGGL(dsa_mla_combine_kernel, dim3(p.T * p.H), dim3(128), 0, st, p);
+  hipLaunchKernelGGL(dsa_mla_combine_kernel, dim3(p.T * p.H / 4), dim3(256), 0, st, p);
   e = hipGetLastError();
   if (e != hipSuccess || !p.residual) return e;
   hipLaunchKernelGGL(dsa_mla_norm_kernel, dim3(p.T * p.H / 4), dim3(256), 0, st, p);
