@@ -43,12 +43,13 @@
 namespace dsa {
 
 // =============================================================================
-// Planning kernel: one workgroup of 1024 threads.
+// Planning kernel: one workgroup (1024 threads; 256 for at most 256 queries,
+// one wave for at most 64).
 // =============================================================================
 constexpr int PLAN_NT = 1024;
 
 __device__ __forceinline__ int block_scan_incl(int v, int* s_w, bool is_max) {
-  // inclusive scan (sum or max) over PLAN_NT threads; s_w: >= 16 ints of LDS
+  // inclusive scan (sum or max) over the workgroup (<= PLAN_NT threads); s_w: >= 16 ints of LDS
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   v = is_max ? wave_incl_max(v) : (int)wave_incl_scan((uint32_t)v);
   if (lane == 63) s_w[wave] = v;
@@ -73,17 +74,32 @@ __device__ __forceinline__ int plan_vis(const IdxParams& p, int t) {
   return min(max(v, 0), L);
 }
 
+// Up to PLAN_LDS_T queries, the per-query visible counts and the per-group
+// fields the later passes read are kept in LDS (dynamic, PLAN_LDS_BYTES), so
+// no pass waits on a global round trip for what an earlier pass produced.
+constexpr int PLAN_LDS_T = 4096;
+constexpr size_t PLAN_LDS_BYTES = (size_t)5 * PLAN_LDS_T * sizeof(int);
+
 __global__ __launch_bounds__(PLAN_NT) void dsa_plan_kernel(IdxParams p) {
   __shared__ int s_w[16];
   __shared__ int s_carry[4];
+  extern __shared__ int plan_lds[];
+  const bool in_lds = p.T <= PLAN_LDS_T;
+  int* s_vis = plan_lds;                    // [T] visible count of each query
+  int* s_t0 = plan_lds + PLAN_LDS_T;        // [groups] first query
+  int* s_nq = plan_lds + 2 * PLAN_LDS_T;    // [groups] queries
+  int* s_rng = plan_lds + 3 * PLAN_LDS_T;   // [groups] key range
+  int* s_off = plan_lds + 4 * PLAN_LDS_T;   // [groups] offset in the key space
   const int tid = threadIdx.x;
+  const int nt = blockDim.x;  // fewer waves per barrier for a short batch
   // ---- pass 1: group starts (runs of one sequence, cut every MQ queries)
   int carry_run = 0, carry_gid = 0;
-  for (int base = 0; base < p.T; base += PLAN_NT) {
+  for (int base = 0; base < p.T; base += nt) {
     const int t = base + tid;
     const bool valid = t < p.T;
     const int b = valid ? plan_seq(p, t) : -2;
     const int bprev = (valid && t > 0) ? plan_seq(p, t - 1) : -3;
+    if (in_lds && valid) s_vis[t] = plan_vis(p, t);
     const bool f = valid && (t == 0 || b != bprev);
     int run = block_scan_incl(f ? t : -1, s_w, true);
     run = max(run, carry_run);
@@ -94,8 +110,9 @@ __global__ __launch_bounds__(PLAN_NT) void dsa_plan_kernel(IdxParams p) {
       int* g = p.groups + (int64_t)gid * G_FIELDS;
       g[G_T0] = t;
       g[G_SEQ] = b;
+      if (in_lds) s_t0[gid] = t;
     }
-    if (tid == PLAN_NT - 1) {
+    if (tid == nt - 1) {
       s_carry[0] = run;
       s_carry[1] = carry_gid + gincl;
     }
@@ -108,25 +125,33 @@ __global__ __launch_bounds__(PLAN_NT) void dsa_plan_kernel(IdxParams p) {
   // ---- pass 2: per-group key ranges and their offsets in the concatenated
   // key space (each group padded to whole 16-key groups, at least one)
   int c_off = 0;
-  for (int base = 0; base < n_groups; base += PLAN_NT) {
+  for (int base = 0; base < n_groups; base += nt) {
     const int g = base + tid;
     int wgt = 0;
     int* gr = p.groups + (int64_t)g * G_FIELDS;
     if (g < n_groups) {
-      const int t0 = gr[G_T0];
-      const int t1 = (g + 1 < n_groups) ? p.groups[(int64_t)(g + 1) * G_FIELDS + G_T0] : p.T;
+      const int t0 = in_lds ? s_t0[g] : gr[G_T0];
+      const int t1 = (g + 1 < n_groups) ? (in_lds ? s_t0[g + 1] : p.groups[(int64_t)(g + 1) * G_FIELDS + G_T0])
+                                        : p.T;
       int range = 0;
       for (int t = t0; t < t1; ++t) {
-        range = max(range, plan_vis(p, t));
+        range = max(range, in_lds ? s_vis[t] : plan_vis(p, t));
         p.qgroup[t] = g;
       }
       gr[G_NQ] = t1 - t0;
       gr[G_RANGE] = range;
+      if (in_lds) {
+        s_nq[g] = t1 - t0;
+        s_rng[g] = range;
+      }
       wgt = max(16, (range + 15) & ~15) + SEG_COST;
     }
     const int so = block_scan_incl(wgt, s_w, false);
-    if (g < n_groups) gr[G_OFF] = c_off + so - wgt;
-    if (tid == PLAN_NT - 1) s_carry[0] = c_off + so;
+    if (g < n_groups) {
+      gr[G_OFF] = c_off + so - wgt;
+      if (in_lds) s_off[g] = c_off + so - wgt;
+    }
+    if (tid == nt - 1) s_carry[0] = c_off + so;
     __syncthreads();
     c_off = s_carry[0];
     __syncthreads();
@@ -135,26 +160,28 @@ __global__ __launch_bounds__(PLAN_NT) void dsa_plan_kernel(IdxParams p) {
   const int slice = max(MIN_SLICE, (((total + p.nwg - 1) / p.nwg) + 15) & ~15);
   // ---- pass 3: workgroups overlapping each group; list slots of split groups
   int c_list = 0;
-  for (int base = 0; base < n_groups; base += PLAN_NT) {
+  for (int base = 0; base < n_groups; base += nt) {
     const int g = base + tid;
     int lists = 0;
     int* gr = p.groups + (int64_t)g * G_FIELDS;
     if (g < n_groups) {
-      const int off = gr[G_OFF];
+      const int off = in_lds ? s_off[g] : gr[G_OFF];
+      const int range = in_lds ? s_rng[g] : gr[G_RANGE];
+      const int nq = in_lds ? s_nq[g] : gr[G_NQ];
       // workgroups holding the group's keys (the extra weight that stands
       // for the segment cost follows them and holds no keys)
-      const int wreal = max(16, (gr[G_RANGE] + 15) & ~15);
+      const int wreal = max(16, (range + 15) & ~15);
       const int w0 = off / slice, w1 = (off + wreal - 1) / slice;
       const int wlast = (off + wreal + SEG_COST - 1) / slice;
       gr[G_W0] = w0;
       gr[G_NL] = w1 - w0 + 1;
       // workgroups whose slice starts inside this group begin with it
       for (int w = (off + slice - 1) / slice; w <= wlast && w < p.nwg; ++w) p.wg_first[w] = g;
-      lists = w1 > w0 ? gr[G_NQ] * (w1 - w0 + 1) : 0;
+      lists = w1 > w0 ? nq * (w1 - w0 + 1) : 0;
     }
     const int sl = block_scan_incl(lists, s_w, false);
     if (g < n_groups) gr[G_LIST] = c_list + sl - lists;
-    if (tid == PLAN_NT - 1) s_carry[0] = c_list + sl;
+    if (tid == nt - 1) s_carry[0] = c_list + sl;
     __syncthreads();
     c_list = s_carry[0];
     __syncthreads();
@@ -1004,8 +1031,13 @@ static hipError_t launch_indexer_mq(const IdxParams& p, int grid, hipStream_t st
 }
 
 hipError_t launch_indexer(const IdxParams& p, int idx_dtype, int D, int grid, bool need_merge, hipStream_t st) {
-  hipLaunchKernelGGL(dsa_plan_kernel, dim3(1), dim3(PLAN_NT), 0, st, p);
-  hipError_t e = hipGetLastError();
+  const size_t plan_smem = p.T <= PLAN_LDS_T ? PLAN_LDS_BYTES : 0;
+  hipError_t e = hipFuncSetAttribute((const void*)dsa_plan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)PLAN_LDS_BYTES);
+  if (e != hipSuccess) return e;
+  const int plan_nt = p.T <= 64 ? 64 : (p.T <= 256 ? 256 : PLAN_NT);
+  hipLaunchKernelGGL(dsa_plan_kernel, dim3(1), dim3(plan_nt), plan_smem, st, p);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const bool small_heads = p.H_idx <= 16;
   if (idx_dtype == 1)

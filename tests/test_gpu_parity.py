@@ -96,6 +96,12 @@ def test_prefill_chunks_causal(chunk):
              queries=[0, 1, 511, 512, 513, 1000, 2047] if chunk < 2 else None)
 
 
+def test_prefill_chunk_above_4096_queries():
+    # more queries than the planning kernel keeps in LDS: its global-memory path
+    sp = spec("prefill_big_chunk", prefill=(5000, 5000), K=256, H=16, H_idx=16, seed=23)
+    run_case(sp, prefill_chunk=0, queries=[0, 255, 256, 4095, 4096, 4999])
+
+
 def test_edge_lengths_and_small_k():
     run_case(spec("edges_bf16", idx_dtype="bf16", H_idx=4, D_idx=64, K=4, H=16, lens=[0, 1, 63, 65, 4], seed=13))
     run_case(spec("edges_k1", H_idx=16, K=1, H=32, lens=[1, 2, 700], seed=17))
