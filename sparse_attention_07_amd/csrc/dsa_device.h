@@ -23,7 +23,9 @@ constexpr int MIN_SLICE = 4096;       // smallest key slice an indexer workgroup
 // slice: query setup, final selection, output), in keys streamed at full
 // bandwidth.  Each group is charged this many extra keys of weight in the
 // key-space partition, so slices that hold more segments get fewer keys.
-constexpr int SEG_COST = 2560;
+// (Measured: 2560, 3584, 4608 and 5632 gave 208, 205, 202 and 203 us for the
+// 128K-token decode batch; 4608 is also the best or near it for the others.)
+constexpr int SEG_COST = 4608;
 constexpr int SUB = 65536;            // keys whose page ids the indexer stages in LDS at once
 
 // Order-preserving map fp32 -> uint32 (a < b  <=>  key(a) < key(b)); -0 maps
