@@ -63,8 +63,8 @@ template <int NW, bool KV8>
 struct MlaSmem {
   unsigned char stage[STAGES][KV8 ? KV8_STAGE_BYTES : STAGE_BYTES];  // gather ring
   unsigned char tile[KV8 ? STAGE_BYTES : 16];  // FP8 only: the dequantized bf16 tile
-  uint16_t pt[16 * NW][TILE_ROWS];  // P^T as [head][row] bf16
-  float alpha[16 * NW];
+  uint16_t pt[2][16 * NW][TILE_ROWS];  // P^T as [head][row] bf16, two tiles
+  float alpha[2][16 * NW];             // per-head rescale factor, two tiles
   float mfin[16 * NW];
   float lfin[16 * NW];
   float red[NW];  // per-wave partial sums (residual + RMSNorm epilogue)
@@ -208,19 +208,19 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
       }
       l_run = l_run * a_ + lsum;
       m_run = m_new;
-      *reinterpret_cast<v4i*>(&sm.pt[hq][8 * g4]) = __builtin_bit_cast(v4i, pv);
-      if (g4 == 0) sm.alpha[hq] = a_;
+      *reinterpret_cast<v4i*>(&sm.pt[ti & 1][hq][8 * g4]) = __builtin_bit_cast(v4i, pv);
+      if (g4 == 0) sm.alpha[ti & 1][hq] = a_;
     }
   };
-  // O^T += C^T P^T for this wave's value slice, from the bf16 tile at st
-  auto pv = [&](const unsigned char* st) {
+  // O^T += C^T P^T of tile ti for this wave's value slice, from the bf16 tile at st
+  auto pv = [&](int ti, const unsigned char* st) {
     // ---- PV: O^T[v, head] = alpha * O^T + C^T[v, row] P^T[row, head], v in this wave's slice
     {
       float al[NW];
       bool any = false;
 #pragma unroll
       for (int nt = 0; nt < NW; ++nt) {
-        al[nt] = sm.alpha[16 * nt + n16];
+        al[nt] = sm.alpha[ti & 1][16 * nt + n16];
         any |= (al[nt] != 1.f);
       }
       if (__builtin_amdgcn_ballot_w64(any)) {
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
       }
 #pragma unroll
       for (int nt = 0; nt < NW; ++nt) {
-        const v4i pb = *reinterpret_cast<const v4i*>(&sm.pt[16 * nt + n16][8 * g4]);
+        const v4i pb = *reinterpret_cast<const v4i*>(&sm.pt[ti & 1][16 * nt + n16][8 * g4]);
 #pragma unroll
         for (int vt = 0; vt < VT; ++vt)
           o[vt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[vt], __builtin_bit_cast(v8bf, pb), o[vt][nt], 0, 0, 0);
@@ -250,20 +250,17 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
   };
 
   if constexpr (!KV8) {
+    // Software pipelined, one barrier per tile: iteration ti runs the PV of
+    // tile ti-1 and the logits and softmax of tile ti (P^T and the rescale
+    // factors are double-buffered).  The three gather stages hold tiles ti-1
+    // (PV), ti (logits) and ti+1 (in flight), so gathers run one tile ahead.
     if (ntiles > 0) issue_tile(0);
-    if (ntiles > 1) issue_tile(1);
-    for (int ti = 0; ti < ntiles; ++ti) {
-      // this wave's loads of tile ti are done when at most one newer tile is in flight
-      if (ti + 1 < ntiles)
-        __builtin_amdgcn_s_waitcnt((LMIN & 15) | ((LMIN >> 4) << 14) | (7 << 4) | (15 << 8));
-      else
-        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
-      lds_barrier_keep_dma();
-      if (ti + 2 < ntiles) issue_tile(ti + 2);
-      const unsigned char* st = sm.stage[ti % STAGES];
-      logits_softmax(ti, st);
-      lds_barrier_keep_dma();
-      pv(st);
+    for (int ti = 0; ti <= ntiles; ++ti) {
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // tile ti, the only one in flight, has landed
+      lds_barrier_keep_dma();  // and every wave has left iteration ti-1 (stage (ti+1)%3 is free)
+      if (ti + 1 < ntiles) issue_tile(ti + 1);
+      if (ti > 0) pv(ti - 1, sm.stage[(ti - 1) % STAGES]);
+      if (ti < ntiles) logits_softmax(ti, sm.stage[ti % STAGES]);
     }
   } else {
     // FP8 rows: once a tile's rows have landed, all waves dequantize it into the
@@ -309,7 +306,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
       lds_barrier_keep_dma();
       logits_softmax(ti, sm.tile);
       lds_barrier_keep_dma();
-      pv(sm.tile);
+      pv(ti, sm.tile);
     }
   }
 
