@@ -75,10 +75,19 @@ __device__ __forceinline__ void lds_barrier_keep_dma() { asm volatile("s_waitcnt
 
 // 16-byte global -> LDS copy per lane: lane i writes LDS[lds_base + 16 i].
 // Issued as asm so the compiler does not add its own (drain-everything) wait
-// before later LDS reads; callers wait with an explicit vmcnt.  The asm has no
-// output register, only the address input, and the m0 write is declared.
+// before later LDS reads; callers wait with an explicit vmcnt.  The load has no
+// output register (it writes LDS).  m0 is reserved to the compiler, so the asm
+// saves it in a scratch SGPR and restores it after the load has been issued.
 __device__ __forceinline__ void dma16_to_lds(const void* gaddr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(lds_base) : "memory", "m0");
+  uint32_t saved_m0;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved_m0)
+      : "v"(gaddr), "s"(lds_base)
+      : "memory");
 }
 
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
