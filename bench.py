@@ -242,8 +242,8 @@ def bench_quantize(args, spec, case):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
-              "(how the layer would shard is described in the design notes)", file=sys.stderr)
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported: the layer has no "
+              "multi-GPU path", file=sys.stderr)
         sys.exit(2)
     import torch
     from sparse_attention_07_amd import dsa, synth

@@ -20,7 +20,7 @@ The exact formula is S[p] = sum_h w_h * ReLU(q_h . k_p) over indexer heads h,
 MLA attention over the 576-wide latent rows (512 "nope" + 64 rope) with value =
 the first 512 dims and softmax scale 1/sqrt(576).
 
-Readings where the pages are silent (each also listed in the design notes):
+Readings where the pages are silent:
   * one index key per token, shared by all indexer heads; w is per query token;
   * FP8 data is OCP e4m3fn codes times an fp32 scale (per token for keys, per
     (token, head) for queries), dequantized before the dot product;

@@ -60,8 +60,8 @@ class MlaArgs(ctypes.Structure):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_attention_07_amd.build` "
-                          "(or __graft_entry__.build()); the DSA layer has no non-HIP path")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_attention_07_amd.build`; "
+                          "the DSA layer has no non-HIP path")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER
     lib.dsa_workspace_bytes.restype = ctypes.c_size_t
