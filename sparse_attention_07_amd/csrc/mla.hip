@@ -61,8 +61,9 @@ __device__ __forceinline__ int stage_off(int r, int col) { return 16 * (r * ROW_
 
 template <int NW, bool KV8>
 struct MlaSmem {
-  unsigned char stage[STAGES][KV8 ? KV8_STAGE_BYTES : STAGE_BYTES];  // gather ring
-  unsigned char tile[KV8 ? STAGE_BYTES : 16];  // FP8 only: the dequantized bf16 tile
+  static constexpr int NSTAGE = KV8 ? 2 : STAGES;
+  unsigned char stage[NSTAGE][KV8 ? KV8_STAGE_BYTES : STAGE_BYTES];  // gather ring
+  unsigned char tile[KV8 ? 2 : 1][KV8 ? STAGE_BYTES : 16];          // FP8 only: two dequantized bf16 tiles
   uint16_t pt[2][16 * NW][TILE_ROWS];  // P^T as [head][row] bf16, two tiles
   float alpha[2][16 * NW];             // per-head rescale factor, two tiles
   float mfin[16 * NW];
@@ -135,8 +136,9 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
   lds_barrier();
 
+  constexpr int NSTAGE = MlaSmem<NW, KV8>::NSTAGE;
   auto issue_tile = [&](int ti) {
-    unsigned char* st = sm.stage[ti % STAGES];
+    unsigned char* st = sm.stage[ti % NSTAGE];
     const int nl = LMIN + (wave < LEXTRA ? 1 : 0);
     const int first = wave * LMIN + min(wave, LEXTRA);
     for (int k = 0; k < nl; ++k) {
@@ -263,13 +265,14 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
       if (ti < ntiles) logits_softmax(ti, sm.stage[ti % STAGES]);
     }
   } else {
-    // FP8 rows: once a tile's rows have landed, all waves dequantize it into the
-    // bf16 tile, then the bf16 phases run on it (three barriers per tile).
-    // Dequantizing the next tile during this tile's PV instead (two bf16
-    // tiles) measured slower: the kernel is bound by LDS traffic, not by the
-    // gather, and the extra live registers spill.
+    // FP8 rows, pipelined like the bf16 loop with one more barrier: once tile
+    // ti has landed, all waves dequantize it into bf16 tile ti&1; after the
+    // second barrier iteration ti runs the PV of tile ti-1 (from the other
+    // bf16 tile) and the logits and softmax of tile ti.  Two FP8 gather
+    // stages: tile ti+1 is in flight while tile ti is dequantized.
     auto dequant = [&](int ti) {
-      const unsigned char* src = sm.stage[ti % STAGES];
+      const unsigned char* src = sm.stage[ti % NSTAGE];
+      unsigned char* dst = sm.tile[ti & 1];
       // keep the per-thread offsets out of the registers that live across the
       // tile loop: the thread index is made opaque here, so they are recomputed
       int tid_o = tid;
@@ -282,31 +285,26 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
         const float sc = *reinterpret_cast<const float*>(rowp + KV8_SCALE_OFF + 4 * (k >> 3));
         v4i lo, hi;
         dequant16(c16, sc, lo, hi);
-        unsigned char* d = sm.tile + 16 * (r * ROW_STRIDE + 2 * k);
+        unsigned char* d = dst + 16 * (r * ROW_STRIDE + 2 * k);
         *reinterpret_cast<v4i*>(d) = lo;
         *reinterpret_cast<v4i*>(d + 16) = hi;
       }
 #pragma unroll 1
       for (int i = tid_o; i < TILE_ROWS * 8; i += NT) {  // rope: 8 units per row, copied
         const int r = i >> 3, j = i & 7;
-        *reinterpret_cast<v4i*>(sm.tile + 16 * (r * ROW_STRIDE + 64 + j)) =
+        *reinterpret_cast<v4i*>(dst + 16 * (r * ROW_STRIDE + 64 + j)) =
             *reinterpret_cast<const v4i*>(src + 16 * KV8_ROW_UNITS * r + KV8_ROPE_OFF + 16 * j);
       }
     };
     if (ntiles > 0) issue_tile(0);
-    if (ntiles > 1) issue_tile(1);
-    for (int ti = 0; ti < ntiles; ++ti) {
-      if (ti + 1 < ntiles)
-        __builtin_amdgcn_s_waitcnt((LMIN & 15) | ((LMIN >> 4) << 14) | (7 << 4) | (15 << 8));
-      else
-        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
-      lds_barrier_keep_dma();  // tile ti landed; every wave has left tile ti-1's PV
-      if (ti + 2 < ntiles) issue_tile(ti + 2);
-      dequant(ti);
-      lds_barrier_keep_dma();
-      logits_softmax(ti, sm.tile);
-      lds_barrier_keep_dma();
-      pv(ti, sm.tile);
+    for (int ti = 0; ti <= ntiles; ++ti) {
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // tile ti, the only one in flight, has landed
+      lds_barrier_keep_dma();  // every wave has left iteration ti-1: bf16 tile ti&1 and stage (ti+1)%2 are free
+      if (ti + 1 < ntiles) issue_tile(ti + 1);
+      if (ti < ntiles) dequant(ti);
+      lds_barrier_keep_dma();  // bf16 tile ti is complete
+      if (ti > 0) pv(ti - 1, sm.tile[(ti - 1) & 1]);
+      if (ti < ntiles) logits_softmax(ti, sm.tile[ti & 1]);
     }
   }
 
