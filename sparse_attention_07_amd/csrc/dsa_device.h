@@ -19,6 +19,7 @@ constexpr int VDIM = 512;
 constexpr int KMAX = 2048;
 constexpr int ROUND = 1024;  // keys scored per streaming round of the indexer
 constexpr int MIN_SLICE = 4096;       // smallest key slice an indexer workgroup is given
+constexpr int MERGE_FAN = 8;          // candidate lists one merge workgroup takes at once
 // Fixed cost of one indexer segment (a group's keys inside one workgroup's
 // slice: query setup, final selection, output), in keys streamed at full
 // bandwidth.  Each group is charged this many extra keys of weight in the

@@ -36,6 +36,13 @@ struct IdxParams {
   uint32_t* list_mm;   //   [.][2] smallest and largest key of the list
   uint32_t* list_keys; //   [.][K] order keys, ascending position
   int32_t* list_pos;   //   [.][K] logical positions
+  // two-level merge of queries with many lists: intermediate lists (same
+  // layout and slots as above) and a per-query count of finished runs
+  int32_t* mlist_cnt;
+  uint32_t* mlist_mm;
+  uint32_t* mlist_keys;
+  int32_t* mlist_pos;
+  int32_t* merge_done;  // [T], cleared by the planning kernel
 };
 
 struct MlaParams {

@@ -186,6 +186,8 @@ __global__ __launch_bounds__(PLAN_NT) void dsa_plan_kernel(IdxParams p) {
     c_list = s_carry[0];
     __syncthreads();
   }
+  if (p.merge_done)
+    for (int t = tid; t < p.T; t += nt) p.merge_done[t] = 0;
   if (tid == 0) {
     p.hdr[0] = n_groups;
     p.hdr[1] = total;
@@ -864,22 +866,32 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
 }
 
 // =============================================================================
-// Merge kernel: one workgroup per query whose keys span several slices.
+// Merge kernel: the candidate lists of queries whose keys span several slices.
 //
 // Every full list (K entries) is itself the Top-K of its slice, so the largest
 // list minimum lb bounds the final K-th key from below and keys below lb are
-// out.  The lists' concatenation (already in position order; slots past a
-// list's count hold key 0) is read in chunks of MRG_RS entries per lane, wide
-// and all at once.  A chunk's entries above the running bound are appended in
-// order to an LDS buffer; when they would not fit, the buffer is first cut to
-// its Top-K, which raises the bound.  A query whose lists fit one chunk (the
-// common case) selects straight from registers.
+// out.  A run of lists (in position order; slots past a list's count hold key
+// 0) is read in chunks of MRG_RS entries per lane, wide and all at once.  A
+// chunk's entries above the running bound are appended in order to an LDS
+// buffer; when they would not fit, the buffer is first cut to its Top-K,
+// which raises the bound.  A run that fits one chunk (up to MRG_FAN lists)
+// selects straight from registers.
+//
+// A query with more than MRG_FAN lists merges in two levels within the same
+// launch: workgroup (t, j) merges lists [MRG_FAN j, MRG_FAN (j + 1)) of query t
+// into an intermediate list of the same layout (second list area, same slot
+// index unit0 + j), and the last of these to finish
+// (a per-query counter the planning kernel clears) merges the intermediate
+// lists.  A list's Top-K keeps every entry of the query's Top-K that it holds,
+// so the two levels select exactly what one would.
 // =============================================================================
 constexpr int MRG_NW = 8;
 constexpr int MRG_NT = MRG_NW * 64;
 constexpr int MRG_RS = 32;                  // entries per lane per chunk
 constexpr int MRG_CHUNK = MRG_RS * MRG_NT;  // 16384
 constexpr int MRG_CAP = 16384;              // LDS candidate buffer
+constexpr int MRG_FAN = MERGE_FAN;          // lists one single-chunk merge takes
+static_assert(MRG_FAN * KMAX <= MRG_CHUNK, "a run of MRG_FAN lists is one chunk");
 
 struct MergeSmem {
   uint32_t cand_key[MRG_CAP];
@@ -890,24 +902,32 @@ struct MergeSmem {
 };
 static_assert(MRG_CAP >= 2 * KMAX, "the buffer cut to K takes a chunk cut to K");
 
-__global__ __launch_bounds__(MRG_NT, 1) void dsa_merge_kernel(IdxParams p) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  MergeSmem& sm = *reinterpret_cast<MergeSmem*>(smem_raw);
+// Largest minimum over the full lists among n (counts cnt, [min, max] pairs
+// mm), at least 1.  Block-wide; ends with a barrier.
+__device__ __forceinline__ uint32_t lists_lb(const int32_t* cnt, const uint32_t* mm, int n, int K, MergeSmem& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t = blockIdx.x;
-  if (t >= p.T) return;
-  const int g = p.qgroup[t];
-  const int* gr = p.groups + (int64_t)g * G_FIELDS;
-  const int nl = gr[G_NL];  // lists of this query (one per overlapping indexer workgroup)
-  if (nl <= 1) return;
-  const int q = t - gr[G_T0];
-  const int seq = gr[G_SEQ];
-  const int64_t unit0 = (int64_t)gr[G_LIST] + (int64_t)q * nl;
-  const int K = p.K;
-  const int total = nl * K;
+  uint32_t lb = 1u;
+  for (int c = tid; c < n; c += MRG_NT) {
+    if (cnt[c] == K) lb = max(lb, mm[2 * c]);
+  }
+  lb = wave_max_u32(lb);
+  if (lane == 0) sm.red[wave] = lb;
+  lds_barrier();
+  lb = 1u;
+#pragma unroll
+  for (int w = 0; w < MRG_NW; ++w) lb = max(lb, sm.red[w]);
+  lds_barrier();
+  return lb;
+}
+
+// Top-K of the n lists at keys0/pos0 (list i at offset i K), keys below lb
+// excluded: the kept entries, in position order, go to sm.cand_key/cand_pos
+// [0, cnt); returns cnt.  Ends with a barrier.
+__device__ __forceinline__ int merge_lists(const uint32_t* keys0, const int32_t* pos0, int n, uint32_t lb, int K,
+                                           MergeSmem& sm) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int total = n * K;
   const int nchunks = (total + MRG_CHUNK - 1) / MRG_CHUNK;
-  const uint32_t* keys0 = p.list_keys + unit0 * K;
-  const int32_t* pos0 = p.list_pos + unit0 * K;
 
   // Chunk layout: wave w holds entries [w * wch, (w + 1) * wch) of the chunk,
   // 64 per slot; every load comes from a clamped index and out-of-range slots
@@ -927,22 +947,6 @@ __global__ __launch_bounds__(MRG_NT, 1) void dsa_merge_kernel(IdxParams p) {
     return wch;
   };
   int wch = load_chunk(0);
-
-  // ---- lb = largest minimum over full lists
-  uint32_t lb = 1u;
-  for (int c = tid; c < nl; c += MRG_NT) {
-    if (p.list_cnt[unit0 + c] == K) lb = max(lb, p.list_mm[2 * (unit0 + c)]);
-  }
-  lb = wave_max_u32(lb);
-  if (lane == 0) sm.red[wave] = lb;
-  lds_barrier();
-  lb = 1u;
-#pragma unroll
-  for (int w = 0; w < MRG_NW; ++w) lb = max(lb, sm.red[w]);
-  lds_barrier();
-
-  const int32_t* bt = p.block_table + (int64_t)max(seq, 0) * p.max_blocks;
-  int32_t* out = p.indices + (int64_t)t * K;
   uint32_t thr = lb - 1u;  // keep keys > thr
   int cnt = 0;
   for (int c = 0; c < nchunks; ++c) {
@@ -960,8 +964,10 @@ __global__ __launch_bounds__(MRG_NT, 1) void dsa_merge_kernel(IdxParams p) {
       // ---- single chunk: select straight from the registers
       const SelRule rule = select_rule<MRG_NW, MRG_RS>(rk, rp, K, sm.hist, sm.sel, sm.red);
       uint32_t kmin;
-      cnt = select_output<MRG_NW, MRG_RS>(rk, rp, rule, sm.red, kmin,
-                                          [&](int o, uint32_t, int32_t ps) { sm.cand_pos[o] = ps; });
+      cnt = select_output<MRG_NW, MRG_RS>(rk, rp, rule, sm.red, kmin, [&](int o, uint32_t k, int32_t ps) {
+        sm.cand_key[o] = k;
+        sm.cand_pos[o] = ps;
+      });
       break;
     }
     // survivors of this chunk (word 8w+7 of red is used by nothing else)
@@ -971,10 +977,10 @@ __global__ __launch_bounds__(MRG_NT, 1) void dsa_merge_kernel(IdxParams p) {
       for (int s = 0; s < MRG_RS; ++s) wc += (uint32_t)__builtin_popcountll(ballot(rk[s] != 0u));
       if (lane == 0) sm.red[8 * wave + 7] = wc;
       lds_barrier();
-      int n = 0;
+      int m = 0;
 #pragma unroll
-      for (int w = 0; w < MRG_NW; ++w) n += (int)sm.red[8 * w + 7];
-      return n;
+      for (int w = 0; w < MRG_NW; ++w) m += (int)sm.red[8 * w + 7];
+      return m;
     };
     int tot = count_valid();
     if (cnt + tot > MRG_CAP && cnt > K) {
@@ -1001,7 +1007,62 @@ __global__ __launch_bounds__(MRG_NT, 1) void dsa_merge_kernel(IdxParams p) {
     block_select<MRG_NW, MRG_CAP / MRG_NT>(sm.cand_key, sm.cand_pos, cnt, K, sm.hist, sm.sel, sm.red);
     cnt = K;
   }
+  return cnt;
+}
+
+__global__ __launch_bounds__(MRG_NT, 1) void dsa_merge_kernel(IdxParams p) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  MergeSmem& sm = *reinterpret_cast<MergeSmem*>(smem_raw);
+  const int tid = threadIdx.x;
+  const int t = blockIdx.x;
+  const int j = blockIdx.y;  // run of lists (second level: runs of MRG_FAN)
+  if (t >= p.T) return;
+  const int g = p.qgroup[t];
+  const int* gr = p.groups + (int64_t)g * G_FIELDS;
+  const int nl = gr[G_NL];  // lists of this query (one per overlapping indexer workgroup)
+  if (nl <= 1) return;
+  const int nrun = nl > MRG_FAN ? (nl + MRG_FAN - 1) / MRG_FAN : 1;
+  if (j >= nrun) return;
+  const int q = t - gr[G_T0];
+  const int seq = gr[G_SEQ];
+  const int64_t unit0 = (int64_t)gr[G_LIST] + (int64_t)q * nl;
+  const int K = p.K;
+  // lower bound from every list of the query
+  const uint32_t lb = lists_lb(p.list_cnt + unit0, p.list_mm + 2 * unit0, nl, K, sm);
+
+  int cnt;
+  if (nrun == 1) {
+    cnt = merge_lists(p.list_keys + unit0 * K, p.list_pos + unit0 * K, nl, lb, K, sm);
+  } else {
+    // ---- first level: this run's Top-K becomes intermediate list unit0 + j
+    const int c0 = j * MRG_FAN;
+    const int nj = min(MRG_FAN, nl - c0);
+    cnt = merge_lists(p.list_keys + (unit0 + c0) * K, p.list_pos + (unit0 + c0) * K, nj, lb, K, sm);
+    const int64_t u = unit0 + j;
+    for (int i = tid; i < K; i += MRG_NT) {
+      p.mlist_keys[u * K + i] = i < cnt ? sm.cand_key[i] : 0u;
+      if (i < cnt) p.mlist_pos[u * K + i] = sm.cand_pos[i];
+    }
+    uint32_t mn = 0u, mx = 0u;
+    if (cnt > 0) block_minmax<MRG_NW>(sm.cand_key, cnt, sm.red, mn, mx);
+    if (tid == 0) {
+      p.mlist_cnt[u] = cnt;
+      p.mlist_mm[2 * u] = mn;
+      p.mlist_mm[2 * u + 1] = mx;
+    }
+    // the last run to finish merges the intermediate lists
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) sm.sel[3] = atomicAdd(&p.merge_done[t], 1);
+    __syncthreads();
+    if (sm.sel[3] != nrun - 1) return;
+    __threadfence();
+    const uint32_t lb2 = max(lb, lists_lb(p.mlist_cnt + unit0, p.mlist_mm + 2 * unit0, nrun, K, sm));
+    cnt = merge_lists(p.mlist_keys + unit0 * K, p.mlist_pos + unit0 * K, nrun, lb2, K, sm);
+  }
   // ---- output: kept positions (in LDS, in order) to pool slots
+  const int32_t* bt = p.block_table + (int64_t)max(seq, 0) * p.max_blocks;
+  int32_t* out = p.indices + (int64_t)t * K;
   for (int i = tid; i < K; i += MRG_NT) {
     int v = -1;
     if (i < cnt) {
@@ -1030,7 +1091,8 @@ static hipError_t launch_indexer_mq(const IdxParams& p, int grid, hipStream_t st
   return p.MQ == 1 ? launch_indexer_t<DT, D, HT, 1, 8>(p, grid, st) : launch_indexer_t<DT, D, HT, 2, 8>(p, grid, st);
 }
 
-hipError_t launch_indexer(const IdxParams& p, int idx_dtype, int D, int grid, bool need_merge, hipStream_t st) {
+hipError_t launch_indexer(const IdxParams& p, int idx_dtype, int D, int grid, bool need_merge, int merge_runs,
+                          hipStream_t st) {
   const size_t plan_smem = p.T <= PLAN_LDS_T ? PLAN_LDS_BYTES : 0;
   hipError_t e = hipFuncSetAttribute((const void*)dsa_plan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)PLAN_LDS_BYTES);
@@ -1052,7 +1114,7 @@ hipError_t launch_indexer(const IdxParams& p, int idx_dtype, int D, int grid, bo
   const size_t smem = sizeof(MergeSmem);
   e = hipFuncSetAttribute((const void*)dsa_merge_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(dsa_merge_kernel, dim3(p.T), dim3(MRG_NT), smem, st, p);
+  hipLaunchKernelGGL(dsa_merge_kernel, dim3(p.T, merge_runs), dim3(MRG_NT), smem, st, p);
   return hipGetLastError();
 }
 
