@@ -336,7 +336,7 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": stored_traffic(f"indexer_traffic_{spec.name}"),
-            "kernel": "dsa_indexer_topk: planning + dsa_indexer_kernel + dsa_merge_kernel",
+            "kernel": "dsa_indexer_topk: planning + dsa_indexer_kernel (Top-K and list merge)",
             "launch_ms": round(idx_ms, 5), "algorithmic_bytes": idx_bytes,
         },
         "layer": {

@@ -10,8 +10,7 @@
 #include "dsa_params.h"
 
 namespace dsa {
-hipError_t launch_indexer(const IdxParams& p, int idx_dtype, int D, int grid, bool need_merge, int merge_runs,
-                          hipStream_t st);
+hipError_t launch_indexer(const IdxParams& p, int idx_dtype, int D, int grid, hipStream_t st);
 hipError_t launch_mla(const MlaParams& p, hipStream_t st);
 hipError_t launch_quantize_q(const void* q, int64_t rows, int D, int idx_dtype, void* codes, void* scales,
                              hipStream_t st);
@@ -29,7 +28,7 @@ struct IdxPlan {
   bool need_merge = false;
   int merge_runs = 1;  // runs of MERGE_FAN lists a query may need (second merge level when > 1)
   int64_t lists = 0;  // candidate lists the workspace holds
-  size_t off_mcnt = 0, off_mmin = 0, off_mkeys = 0, off_mpos = 0, off_mdone = 0;
+  size_t off_run = 0, off_mcnt = 0, off_mmin = 0, off_mkeys = 0, off_mpos = 0, off_mdone = 0;
   size_t off_hdr = 0, off_groups = 0, off_qgroup = 0, off_wgfirst = 0, off_lcnt = 0, off_lmin = 0, off_lkeys = 0, off_lpos = 0,
          end = 0;
 };
@@ -122,6 +121,8 @@ IdxPlan plan_indexer(const dsa_indexer_args* a, int K, size_t base, int nwg) {
   off = align_up(off + (size_t)pl.lists * K * 4, 256);
   pl.off_lpos = off;
   off = align_up(off + (size_t)pl.lists * K * 4, 256);
+  pl.off_run = off;
+  off = align_up(off + (size_t)pl.lists * 4, 256);
   // a query's lists: at most one per workgroup, and its keys cover at most
   // maxlen / MIN_SLICE + 2 slices
   const int64_t nl_max = std::min<int64_t>(nwg, maxlen / MIN_SLICE + 2);
@@ -197,6 +198,7 @@ IdxParams make_idx_params(const dsa_indexer_args* a, int K, int32_t* indices, un
   p.list_mm = (uint32_t*)(ws + pl.off_lmin);
   p.list_keys = (uint32_t*)(ws + pl.off_lkeys);
   p.list_pos = (int32_t*)(ws + pl.off_lpos);
+  p.run_done = pl.need_merge ? (int32_t*)(ws + pl.off_run) : nullptr;
   const bool two = pl.merge_runs > 1;
   p.mlist_cnt = two ? (int32_t*)(ws + pl.off_mcnt) : nullptr;
   p.mlist_mm = two ? (uint32_t*)(ws + pl.off_mmin) : nullptr;
@@ -280,8 +282,7 @@ dsa_status dsa_indexer_topk(const dsa_indexer_args* a, int K, int32_t* indices_o
   const IdxPlan pl = plan_indexer(a, K, 0, device_cus());
   if (!ws || ws_bytes < pl.end || !aligned(ws, 256)) return DSA_ERR_WORKSPACE;
   IdxParams p = make_idx_params(a, K, indices_out, (unsigned char*)ws, pl);
-  return hip_status(launch_indexer(p, a->idx_dtype, a->D_idx, pl.nwg, pl.need_merge, pl.merge_runs,
-                                   (hipStream_t)stream));
+  return hip_status(launch_indexer(p, a->idx_dtype, a->D_idx, pl.nwg, (hipStream_t)stream));
 }
 
 dsa_status dsa_sparse_mla_attn(const dsa_mla_args* m, const int32_t* indices, int K, float scale, void* out, void* ws,
@@ -314,7 +315,7 @@ dsa_status dsa_layer(const dsa_indexer_args* idx, const dsa_mla_args* mla, int K
   int32_t* indices = indices_out ? indices_out : (int32_t*)(w + off_idx);
   hipStream_t s = (hipStream_t)stream;
   IdxParams p = make_idx_params(idx, K, indices, w, ip);
-  st = hip_status(launch_indexer(p, idx->idx_dtype, idx->D_idx, ip.nwg, ip.need_merge, ip.merge_runs, s));
+  st = hip_status(launch_indexer(p, idx->idx_dtype, idx->D_idx, ip.nwg, s));
   if (st != DSA_OK) return st;
   MlaParams q = make_mla_params(mla, indices, K, scale, out, w, mp);
   return hip_status(launch_mla(q, s));

@@ -91,6 +91,23 @@ __device__ __forceinline__ void dma16_to_lds(const void* gaddr, uint32_t lds_bas
       : "memory");
 }
 
+// Device-coherent (agent-scope) loads and stores for data that one workgroup
+// hands to another inside a launch.  They bypass the per-XCD cache levels a
+// plain access may find stale, so no device-scope fence (a writeback and an
+// invalidation of the whole L2 of the XCD) is needed: the writer waits for its
+// stores to complete before it moves the arrival counter, and the reader
+// issues its loads after it has read the counter.
+template <typename T>
+__device__ __forceinline__ T ld_dev(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ void st_dev(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this wave's global loads and stores have completed.
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 
 // Number of set bits of `mask` below this lane.

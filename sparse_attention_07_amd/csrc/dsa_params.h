@@ -36,6 +36,7 @@ struct IdxParams {
   uint32_t* list_mm;   //   [.][2] smallest and largest key of the list
   uint32_t* list_keys; //   [.][K] order keys, ascending position
   int32_t* list_pos;   //   [.][K] logical positions
+  int32_t* run_done;   //   [.] lists written of the run starting at each slot (cleared by the planning kernel)
   // two-level merge of queries with many lists: intermediate lists (same
   // layout and slots as above) and a per-query count of finished runs
   int32_t* mlist_cnt;

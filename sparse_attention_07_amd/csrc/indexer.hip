@@ -32,11 +32,14 @@
 //    the count of the waves before it); only when a round would not fit is
 //    the buffer cut back to K by a block radix select, which raises the
 //    bound;
-//  * a query whose keys span several slices gets one list per slice; a merge
-//    kernel (after a kernel boundary, so no cross-workgroup fences) starts from
-//    the largest minimum key of any full list -- that list alone already holds
-//    K entries at or above it -- and selects the final K from the lists held
-//    in registers.
+//  * a query whose keys span several slices gets one list per slice; the
+//    workgroup that writes the last of them (an arrival counter; lists are
+//    written and read device-coherent) merges them in the same launch: from the
+//    largest minimum key of any full list -- that list alone already holds K
+//    entries at or above it -- it selects the final K from the lists held in
+//    registers, while other workgroups are still streaming.
+#include <algorithm>
+
 #include "dsa_device.h"
 #include "dsa_params.h"
 
@@ -186,6 +189,8 @@ __global__ __launch_bounds__(PLAN_NT) void dsa_plan_kernel(IdxParams p) {
     c_list = s_carry[0];
     __syncthreads();
   }
+  if (p.run_done)
+    for (int u = tid; u < c_list; u += nt) p.run_done[u] = 0;
   if (p.merge_done)
     for (int t = tid; t < p.T; t += nt) p.merge_done[t] = 0;
   if (tid == 0) {
@@ -489,6 +494,213 @@ __device__ __forceinline__ void block_minmax(const uint32_t* keys, int n, uint32
 }
 
 // =============================================================================
+// Merge: the candidate lists of queries whose keys span several slices.
+//
+// Every full list (K entries) is itself the Top-K of its slice, so the largest
+// list minimum lb bounds the final K-th key from below and keys below lb are
+// out.  A run of lists (in position order; slots past a list's count hold key
+// 0) is read in chunks of MRG_RS entries per lane, wide and all at once.  A
+// chunk's entries above the running bound are appended in order to an LDS
+// buffer; when they would not fit, the buffer is first cut to its Top-K,
+// which raises the bound.  A run that fits one chunk (up to MRG_FAN lists)
+// selects straight from registers.
+//
+// The merge runs inside the indexer kernel, in the workgroup that writes the
+// last list of a run: a per-run arrival counter (cleared by the planning
+// kernel), moved once the workgroup's list stores have completed; lists are
+// written and read with device-coherent accesses, so no fence is needed.  A
+// query with up to MRG_FAN lists is one run.  A longer query merges in two
+// levels: run j (lists MRG_FAN j ... MRG_FAN j + MRG_FAN - 1) goes to an
+// intermediate list of the same layout (second list area, slot unit0 + j), and
+// the workgroup that finishes the query's last run (a per-query counter)
+// merges the intermediate lists.  A run's Top-K keeps every entry of the
+// query's Top-K that the run holds, so the two levels select what one would.
+// A split group is the last group a workgroup streams or its first (whose
+// other lists are written later, at the end of earlier slices), so the merge
+// usually starts when its workgroup has nothing left to stream and overlaps
+// the other workgroups' streaming.
+// =============================================================================
+constexpr int MRG_NW = 8;
+constexpr int MRG_NT = MRG_NW * 64;
+constexpr int MRG_RS = 32;                  // entries per lane per chunk
+constexpr int MRG_CHUNK = MRG_RS * MRG_NT;  // 16384
+constexpr int MRG_CAP = 16384;              // LDS candidate buffer
+constexpr int MRG_FAN = MERGE_FAN;          // lists one single-chunk merge takes
+static_assert(MRG_FAN * KMAX <= MRG_CHUNK, "a run of MRG_FAN lists is one chunk");
+
+struct MergeSmem {
+  uint32_t cand_key[MRG_CAP];
+  int32_t cand_pos[MRG_CAP];
+  uint32_t hist[2 * MRG_NW * 256];
+  uint32_t red[8 * MRG_NW];
+  int32_t sel[4];
+};
+static_assert(MRG_CAP >= 2 * KMAX, "the buffer cut to K takes a chunk cut to K");
+
+// Largest minimum over the full lists among n (counts cnt, [min, max] pairs
+// mm), at least 1.  Block-wide; ends with a barrier.
+__device__ __forceinline__ uint32_t lists_lb(const int32_t* cnt, const uint32_t* mm, int n, int K, MergeSmem& sm) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t lb = 1u;
+  for (int c = tid; c < n; c += MRG_NT) {
+    if (ld_dev(cnt + c) == K) lb = max(lb, ld_dev(mm + 2 * c));
+  }
+  lb = wave_max_u32(lb);
+  if (lane == 0) sm.red[wave] = lb;
+  lds_barrier();
+  lb = 1u;
+#pragma unroll
+  for (int w = 0; w < MRG_NW; ++w) lb = max(lb, sm.red[w]);
+  lds_barrier();
+  return lb;
+}
+
+// Top-K of the n lists at keys0/pos0 (list i at offset i K), keys below lb
+// excluded: the kept entries, in position order, go to sm.cand_key/cand_pos
+// [0, cnt); returns cnt.  Ends with a barrier.
+__device__ __forceinline__ int merge_lists(const uint32_t* keys0, const int32_t* pos0, int n, uint32_t lb, int K,
+                                           MergeSmem& sm) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int total = n * K;
+  const int nchunks = (total + MRG_CHUNK - 1) / MRG_CHUNK;
+
+  // Chunk layout: wave w holds entries [w * wch, (w + 1) * wch) of the chunk,
+  // 64 per slot; every load comes from a clamped index and out-of-range slots
+  // are dropped afterwards.
+  uint32_t rk[MRG_RS];
+  int32_t rp[MRG_RS];
+  auto load_chunk = [&](int c) {
+    const int cb = c * MRG_CHUNK;
+    const int cn = min(MRG_CHUNK, total - cb);
+    const int wch = (((cn + MRG_NW - 1) / MRG_NW) + 63) & ~63;
+#pragma unroll
+    for (int s = 0; s < MRG_RS; ++s) {
+      const int e = cb + min(wave * wch + s * 64 + lane, cn - 1);
+      rk[s] = ld_dev(keys0 + e);
+      rp[s] = ld_dev(pos0 + e);
+    }
+    return wch;
+  };
+  int wch = load_chunk(0);
+  uint32_t thr = lb - 1u;  // keep keys > thr
+  int cnt = 0;
+  for (int c = 0; c < nchunks; ++c) {
+    if (c > 0) wch = load_chunk(c);
+    const int cn = min(MRG_CHUNK, total - c * MRG_CHUNK);
+    auto mask = [&]() {
+#pragma unroll
+      for (int s = 0; s < MRG_RS; ++s) {
+        const int e = wave * wch + s * 64 + lane;
+        if (s * 64 >= wch || e >= cn || rk[s] <= thr) rk[s] = 0u;
+      }
+    };
+    mask();
+    if (nchunks == 1) {
+      // ---- single chunk: select straight from the registers
+      const SelRule rule = select_rule<MRG_NW, MRG_RS>(rk, rp, K, sm.hist, sm.sel, sm.red);
+      uint32_t kmin;
+      cnt = select_output<MRG_NW, MRG_RS>(rk, rp, rule, sm.red, kmin, [&](int o, uint32_t k, int32_t ps) {
+        sm.cand_key[o] = k;
+        sm.cand_pos[o] = ps;
+      });
+      break;
+    }
+    // survivors of this chunk (word 8w+7 of red is used by nothing else)
+    auto count_valid = [&]() {
+      uint32_t wc = 0;
+#pragma unroll
+      for (int s = 0; s < MRG_RS; ++s) wc += (uint32_t)__builtin_popcountll(ballot(rk[s] != 0u));
+      if (lane == 0) sm.red[8 * wave + 7] = wc;
+      lds_barrier();
+      int m = 0;
+#pragma unroll
+      for (int w = 0; w < MRG_NW; ++w) m += (int)sm.red[8 * w + 7];
+      return m;
+    };
+    int tot = count_valid();
+    if (cnt + tot > MRG_CAP && cnt > K) {
+      // cut the buffer to its Top-K (raising the bound), then drop the chunk's
+      // entries that no longer pass
+      thr = max(thr, block_select<MRG_NW, MRG_CAP / MRG_NT>(sm.cand_key, sm.cand_pos, cnt, K, sm.hist, sm.sel,
+                                                             sm.red));
+      cnt = K;
+      mask();
+      tot = count_valid();
+    }
+    // append in order: every valid entry, or only the chunk's own Top-K when
+    // that does not fit (cnt <= K then, and cnt + K <= MRG_CAP)
+    const SelRule rule = cnt + tot > MRG_CAP ? select_rule<MRG_NW, MRG_RS>(rk, rp, K, sm.hist, sm.sel, sm.red)
+                                             : SelRule{0u, 0xffffffffu, 0u, 0u};
+    uint32_t kmin;
+    cnt += select_output<MRG_NW, MRG_RS>(rk, rp, rule, sm.red, kmin,
+                                         [&](int o, uint32_t k, int32_t ps) {
+                                           sm.cand_key[cnt + o] = k;
+                                           sm.cand_pos[cnt + o] = ps;
+                                         });
+  }
+  if (nchunks > 1 && cnt > K) {
+    block_select<MRG_NW, MRG_CAP / MRG_NT>(sm.cand_key, sm.cand_pos, cnt, K, sm.hist, sm.sel, sm.red);
+    cnt = K;
+  }
+  return cnt;
+}
+
+// One merge step for query t, run j, in the workgroup that wrote the run's
+// last list (every list of the run is complete and visible).  Block-wide;
+// ends with a barrier, after which the caller may reuse the LDS.
+__device__ __forceinline__ void merge_query(const IdxParams& p, int t, int j, MergeSmem& sm) {
+  const int tid = threadIdx.x;
+  const int* gr = p.groups + (int64_t)p.qgroup[t] * G_FIELDS;
+  const int nl = gr[G_NL];  // lists of this query (one per overlapping indexer workgroup)
+  const int nrun = nl > MRG_FAN ? (nl + MRG_FAN - 1) / MRG_FAN : 1;
+  const int seq = gr[G_SEQ];
+  const int64_t unit0 = (int64_t)gr[G_LIST] + (int64_t)(t - gr[G_T0]) * nl;
+  const int K = p.K;
+  // this run's lists (the other runs may still be streaming)
+  const int c0 = j * MRG_FAN;
+  const int nj = nrun == 1 ? nl : min(MRG_FAN, nl - c0);
+  const uint32_t lb = lists_lb(p.list_cnt + unit0 + c0, p.list_mm + 2 * (unit0 + c0), nj, K, sm);
+  int cnt = merge_lists(p.list_keys + (unit0 + c0) * K, p.list_pos + (unit0 + c0) * K, nj, lb, K, sm);
+  if (nrun > 1) {
+    // ---- first level: the run's Top-K becomes intermediate list unit0 + j
+    const int64_t u = unit0 + j;
+    for (int i = tid; i < K; i += MRG_NT) {
+      st_dev(p.mlist_keys + u * K + i, i < cnt ? sm.cand_key[i] : 0u);
+      if (i < cnt) st_dev(p.mlist_pos + u * K + i, sm.cand_pos[i]);
+    }
+    uint32_t mn = 0u, mx = 0u;
+    if (cnt > 0) block_minmax<MRG_NW>(sm.cand_key, cnt, sm.red, mn, mx);
+    if (tid == 0) {
+      st_dev(p.mlist_cnt + u, cnt);
+      st_dev(p.mlist_mm + 2 * u, mn);
+      st_dev(p.mlist_mm + 2 * u + 1, mx);
+    }
+    // the workgroup that finishes the last run merges the intermediate lists
+    wait_vm();
+    __syncthreads();
+    if (tid == 0) sm.sel[3] = atomicAdd(&p.merge_done[t], 1);
+    __syncthreads();
+    const bool last = uniform(sm.sel[3]) == nrun - 1;
+    lds_barrier();
+    if (!last) return;
+    const uint32_t lb2 = max(lb, lists_lb(p.mlist_cnt + unit0, p.mlist_mm + 2 * unit0, nrun, K, sm));
+    cnt = merge_lists(p.mlist_keys + unit0 * K, p.mlist_pos + unit0 * K, nrun, lb2, K, sm);
+  }
+  // ---- output: kept positions (in LDS, in order) to pool slots
+  const int32_t* bt = p.block_table + (int64_t)max(seq, 0) * p.max_blocks;
+  int32_t* out = p.indices + (int64_t)t * K;
+  for (int i = tid; i < K; i += MRG_NT) {
+    int v = -1;
+    if (i < cnt) {
+      const int ps = sm.cand_pos[i];
+      v = bt[ps >> 6] * PAGE + (ps & 63);
+    }
+    out[i] = v;
+  }
+  lds_barrier();
+}
+
+// =============================================================================
 // Main indexer kernel.
 // =============================================================================
 template <int MQ>
@@ -541,8 +753,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
   static_assert(GPW % PF == 0, "prefetch ring must divide the round");
   static_assert(DT == 0 || D == 128, "fp8 path is 128-wide");
 
+  static_assert(NW == MRG_NW, "the merge runs in the indexer's workgroup");
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Sm& sm = *reinterpret_cast<Sm*>(smem_raw);
+  MergeSmem& msm = *reinterpret_cast<MergeSmem*>(smem_raw);  // same LDS, between segments
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -559,6 +773,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
 
   // first group overlapping [a0, a1), found by the planning kernel
   int g = uniform(p.wg_first[blockIdx.x]);
+  // runs this workgroup completes, merged once its slice is streamed: at most
+  // two split groups overlap a slice (the one across each end), each entry
+  // (group << 8) | (run << 2) | query mask
+  int pend0 = -1, pend1 = -1;
 
   for (; g < n_groups; ++g) {
     const int* gr = p.groups + (int64_t)g * G_FIELDS;
@@ -823,6 +1041,13 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
     }
 
     // ---- final selection and output
+    // split group: this workgroup's list is list il of each query; run jr
+    // (of runs with rs lists) is the one it belongs to
+    const int il = (int)blockIdx.x - w0;
+    const int nrun = nl > MERGE_FAN ? (nl + MERGE_FAN - 1) / MERGE_FAN : 1;
+    const int jr = nrun > 1 ? il / MERGE_FAN : 0;
+    const int rs = nrun > 1 ? min(MERGE_FAN, nl - jr * MERGE_FAN) : nl;
+    int pend = 0;  // queries of the group whose run this workgroup completes
 #pragma unroll
     for (int q = 0; q < MQ; ++q) {
       if (q < nq) {
@@ -848,228 +1073,44 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
           // slots past the count get key 0 (no candidate), so a reader may
           // take all K slots without looking at the count
           for (int i = tid; i < p.K; i += NT) {
-            p.list_keys[unit * p.K + i] = i < c ? sm.cand_key[q][i] : 0u;
-            if (i < c) p.list_pos[unit * p.K + i] = sm.cand_pos[q][i];
+            st_dev(p.list_keys + unit * p.K + i, i < c ? sm.cand_key[q][i] : 0u);
+            if (i < c) st_dev(p.list_pos + unit * p.K + i, sm.cand_pos[q][i]);
           }
           uint32_t mn = 0u, mx = 0u;
           if (c > 0) block_minmax<NW>(sm.cand_key[q], c, sm.red, mn, mx);
           if (tid == 0) {
-            p.list_cnt[unit] = c;
-            p.list_mm[2 * unit] = mn;
-            p.list_mm[2 * unit + 1] = mx;
+            st_dev(p.list_cnt + unit, c);
+            st_dev(p.list_mm + 2 * unit, mn);
+            st_dev(p.list_mm + 2 * unit + 1, mx);
           }
+          // arrival: the list is complete before the run's counter moves
+          wait_vm();
+          __syncthreads();
+          if (tid == 0) sm.sel[3] = atomicAdd(&p.run_done[unit - il + jr], 1);
+          __syncthreads();
+          if (uniform(sm.sel[3]) == rs - 1) pend |= 1 << q;
         }
         lds_barrier();
       }
     }
+    if (pend) {
+      const int e = (g << 8) | (jr << 2) | pend;
+      if (pend0 < 0) pend0 = e;
+      else pend1 = e;
+    }
   }
-}
 
-// =============================================================================
-// Merge kernel: the candidate lists of queries whose keys span several slices.
-//
-// Every full list (K entries) is itself the Top-K of its slice, so the largest
-// list minimum lb bounds the final K-th key from below and keys below lb are
-// out.  A run of lists (in position order; slots past a list's count hold key
-// 0) is read in chunks of MRG_RS entries per lane, wide and all at once.  A
-// chunk's entries above the running bound are appended in order to an LDS
-// buffer; when they would not fit, the buffer is first cut to its Top-K,
-// which raises the bound.  A run that fits one chunk (up to MRG_FAN lists)
-// selects straight from registers.
-//
-// A query with more than MRG_FAN lists merges in two levels within the same
-// launch: workgroup (t, j) merges lists [MRG_FAN j, MRG_FAN (j + 1)) of query t
-// into an intermediate list of the same layout (second list area, same slot
-// index unit0 + j), and the last of these to finish
-// (a per-query counter the planning kernel clears) merges the intermediate
-// lists.  A list's Top-K keeps every entry of the query's Top-K that it holds,
-// so the two levels select exactly what one would.
-// =============================================================================
-constexpr int MRG_NW = 8;
-constexpr int MRG_NT = MRG_NW * 64;
-constexpr int MRG_RS = 32;                  // entries per lane per chunk
-constexpr int MRG_CHUNK = MRG_RS * MRG_NT;  // 16384
-constexpr int MRG_CAP = 16384;              // LDS candidate buffer
-constexpr int MRG_FAN = MERGE_FAN;          // lists one single-chunk merge takes
-static_assert(MRG_FAN * KMAX <= MRG_CHUNK, "a run of MRG_FAN lists is one chunk");
-
-struct MergeSmem {
-  uint32_t cand_key[MRG_CAP];
-  int32_t cand_pos[MRG_CAP];
-  uint32_t hist[2 * MRG_NW * 256];
-  uint32_t red[8 * MRG_NW];
-  int32_t sel[4];
-};
-static_assert(MRG_CAP >= 2 * KMAX, "the buffer cut to K takes a chunk cut to K");
-
-// Largest minimum over the full lists among n (counts cnt, [min, max] pairs
-// mm), at least 1.  Block-wide; ends with a barrier.
-__device__ __forceinline__ uint32_t lists_lb(const int32_t* cnt, const uint32_t* mm, int n, int K, MergeSmem& sm) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t lb = 1u;
-  for (int c = tid; c < n; c += MRG_NT) {
-    if (cnt[c] == K) lb = max(lb, mm[2 * c]);
-  }
-  lb = wave_max_u32(lb);
-  if (lane == 0) sm.red[wave] = lb;
-  lds_barrier();
-  lb = 1u;
-#pragma unroll
-  for (int w = 0; w < MRG_NW; ++w) lb = max(lb, sm.red[w]);
-  lds_barrier();
-  return lb;
-}
-
-// Top-K of the n lists at keys0/pos0 (list i at offset i K), keys below lb
-// excluded: the kept entries, in position order, go to sm.cand_key/cand_pos
-// [0, cnt); returns cnt.  Ends with a barrier.
-__device__ __forceinline__ int merge_lists(const uint32_t* keys0, const int32_t* pos0, int n, uint32_t lb, int K,
-                                           MergeSmem& sm) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int total = n * K;
-  const int nchunks = (total + MRG_CHUNK - 1) / MRG_CHUNK;
-
-  // Chunk layout: wave w holds entries [w * wch, (w + 1) * wch) of the chunk,
-  // 64 per slot; every load comes from a clamped index and out-of-range slots
-  // are dropped afterwards.
-  uint32_t rk[MRG_RS];
-  int32_t rp[MRG_RS];
-  auto load_chunk = [&](int c) {
-    const int cb = c * MRG_CHUNK;
-    const int cn = min(MRG_CHUNK, total - cb);
-    const int wch = (((cn + MRG_NW - 1) / MRG_NW) + 63) & ~63;
-#pragma unroll
-    for (int s = 0; s < MRG_RS; ++s) {
-      const int e = cb + min(wave * wch + s * 64 + lane, cn - 1);
-      rk[s] = keys0[e];
-      rp[s] = pos0[e];
-    }
-    return wch;
-  };
-  int wch = load_chunk(0);
-  uint32_t thr = lb - 1u;  // keep keys > thr
-  int cnt = 0;
-  for (int c = 0; c < nchunks; ++c) {
-    if (c > 0) wch = load_chunk(c);
-    const int cn = min(MRG_CHUNK, total - c * MRG_CHUNK);
-    auto mask = [&]() {
-#pragma unroll
-      for (int s = 0; s < MRG_RS; ++s) {
-        const int e = wave * wch + s * 64 + lane;
-        if (s * 64 >= wch || e >= cn || rk[s] <= thr) rk[s] = 0u;
-      }
-    };
-    mask();
-    if (nchunks == 1) {
-      // ---- single chunk: select straight from the registers
-      const SelRule rule = select_rule<MRG_NW, MRG_RS>(rk, rp, K, sm.hist, sm.sel, sm.red);
-      uint32_t kmin;
-      cnt = select_output<MRG_NW, MRG_RS>(rk, rp, rule, sm.red, kmin, [&](int o, uint32_t k, int32_t ps) {
-        sm.cand_key[o] = k;
-        sm.cand_pos[o] = ps;
-      });
-      break;
-    }
-    // survivors of this chunk (word 8w+7 of red is used by nothing else)
-    auto count_valid = [&]() {
-      uint32_t wc = 0;
-#pragma unroll
-      for (int s = 0; s < MRG_RS; ++s) wc += (uint32_t)__builtin_popcountll(ballot(rk[s] != 0u));
-      if (lane == 0) sm.red[8 * wave + 7] = wc;
-      lds_barrier();
-      int m = 0;
-#pragma unroll
-      for (int w = 0; w < MRG_NW; ++w) m += (int)sm.red[8 * w + 7];
-      return m;
-    };
-    int tot = count_valid();
-    if (cnt + tot > MRG_CAP && cnt > K) {
-      // cut the buffer to its Top-K (raising the bound), then drop the chunk's
-      // entries that no longer pass
-      thr = max(thr, block_select<MRG_NW, MRG_CAP / MRG_NT>(sm.cand_key, sm.cand_pos, cnt, K, sm.hist, sm.sel,
-                                                             sm.red));
-      cnt = K;
-      mask();
-      tot = count_valid();
-    }
-    // append in order: every valid entry, or only the chunk's own Top-K when
-    // that does not fit (cnt <= K then, and cnt + K <= MRG_CAP)
-    const SelRule rule = cnt + tot > MRG_CAP ? select_rule<MRG_NW, MRG_RS>(rk, rp, K, sm.hist, sm.sel, sm.red)
-                                             : SelRule{0u, 0xffffffffu, 0u, 0u};
-    uint32_t kmin;
-    cnt += select_output<MRG_NW, MRG_RS>(rk, rp, rule, sm.red, kmin,
-                                         [&](int o, uint32_t k, int32_t ps) {
-                                           sm.cand_key[cnt + o] = k;
-                                           sm.cand_pos[cnt + o] = ps;
-                                         });
-  }
-  if (nchunks > 1 && cnt > K) {
-    block_select<MRG_NW, MRG_CAP / MRG_NT>(sm.cand_key, sm.cand_pos, cnt, K, sm.hist, sm.sel, sm.red);
-    cnt = K;
-  }
-  return cnt;
-}
-
-__global__ __launch_bounds__(MRG_NT, 1) void dsa_merge_kernel(IdxParams p) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  MergeSmem& sm = *reinterpret_cast<MergeSmem*>(smem_raw);
-  const int tid = threadIdx.x;
-  const int t = blockIdx.x;
-  const int j = blockIdx.y;  // run of lists (second level: runs of MRG_FAN)
-  if (t >= p.T) return;
-  const int g = p.qgroup[t];
-  const int* gr = p.groups + (int64_t)g * G_FIELDS;
-  const int nl = gr[G_NL];  // lists of this query (one per overlapping indexer workgroup)
-  if (nl <= 1) return;
-  const int nrun = nl > MRG_FAN ? (nl + MRG_FAN - 1) / MRG_FAN : 1;
-  if (j >= nrun) return;
-  const int q = t - gr[G_T0];
-  const int seq = gr[G_SEQ];
-  const int64_t unit0 = (int64_t)gr[G_LIST] + (int64_t)q * nl;
-  const int K = p.K;
-  // lower bound from every list of the query
-  const uint32_t lb = lists_lb(p.list_cnt + unit0, p.list_mm + 2 * unit0, nl, K, sm);
-
-  int cnt;
-  if (nrun == 1) {
-    cnt = merge_lists(p.list_keys + unit0 * K, p.list_pos + unit0 * K, nl, lb, K, sm);
-  } else {
-    // ---- first level: this run's Top-K becomes intermediate list unit0 + j
-    const int c0 = j * MRG_FAN;
-    const int nj = min(MRG_FAN, nl - c0);
-    cnt = merge_lists(p.list_keys + (unit0 + c0) * K, p.list_pos + (unit0 + c0) * K, nj, lb, K, sm);
-    const int64_t u = unit0 + j;
-    for (int i = tid; i < K; i += MRG_NT) {
-      p.mlist_keys[u * K + i] = i < cnt ? sm.cand_key[i] : 0u;
-      if (i < cnt) p.mlist_pos[u * K + i] = sm.cand_pos[i];
-    }
-    uint32_t mn = 0u, mx = 0u;
-    if (cnt > 0) block_minmax<MRG_NW>(sm.cand_key, cnt, sm.red, mn, mx);
-    if (tid == 0) {
-      p.mlist_cnt[u] = cnt;
-      p.mlist_mm[2 * u] = mn;
-      p.mlist_mm[2 * u + 1] = mx;
-    }
-    // the last run to finish merges the intermediate lists
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) sm.sel[3] = atomicAdd(&p.merge_done[t], 1);
-    __syncthreads();
-    if (sm.sel[3] != nrun - 1) return;
-    __threadfence();
-    const uint32_t lb2 = max(lb, lists_lb(p.mlist_cnt + unit0, p.mlist_mm + 2 * unit0, nrun, K, sm));
-    cnt = merge_lists(p.mlist_keys + unit0 * K, p.mlist_pos + unit0 * K, nrun, lb2, K, sm);
-  }
-  // ---- output: kept positions (in LDS, in order) to pool slots
-  const int32_t* bt = p.block_table + (int64_t)max(seq, 0) * p.max_blocks;
-  int32_t* out = p.indices + (int64_t)t * K;
-  for (int i = tid; i < K; i += MRG_NT) {
-    int v = -1;
-    if (i < cnt) {
-      const int ps = sm.cand_pos[i];
-      v = bt[ps >> 6] * PAGE + (ps & 63);
-    }
-    out[i] = v;
+  // ---- merge the runs this workgroup completed (every list of them is
+  // complete; they are read with device-coherent loads)
+  if (pend0 < 0) return;
+#pragma unroll 1
+  for (int k = 0; k < 2; ++k) {
+    const int e = uniform(k == 0 ? pend0 : pend1);
+    if (e < 0) break;
+    const int t0 = p.groups[(int64_t)(e >> 8) * G_FIELDS + G_T0];
+#pragma unroll 1
+    for (int q = 0; q < MQ; ++q)
+      if ((e >> q) & 1) merge_query(p, t0 + q, (e >> 2) & 63, msm);
   }
 }
 
@@ -1079,7 +1120,8 @@ __global__ __launch_bounds__(MRG_NT, 1) void dsa_merge_kernel(IdxParams p) {
 template <int DT, int D, int HT, int MQ, int NW>
 static hipError_t launch_indexer_t(const IdxParams& p, int grid, hipStream_t st) {
   auto kfn = dsa_indexer_kernel<DT, D, HT, MQ, NW>;
-  const size_t smem = sizeof(IdxSmem<NW, MQ>);
+  // the merge reuses the workgroup's LDS when lists exist
+  const size_t smem = p.run_done ? std::max(sizeof(IdxSmem<NW, MQ>), sizeof(MergeSmem)) : sizeof(IdxSmem<NW, MQ>);
   hipError_t e = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kfn, dim3(grid), dim3(NW * 64), smem, st, p);
@@ -1091,8 +1133,7 @@ static hipError_t launch_indexer_mq(const IdxParams& p, int grid, hipStream_t st
   return p.MQ == 1 ? launch_indexer_t<DT, D, HT, 1, 8>(p, grid, st) : launch_indexer_t<DT, D, HT, 2, 8>(p, grid, st);
 }
 
-hipError_t launch_indexer(const IdxParams& p, int idx_dtype, int D, int grid, bool need_merge, int merge_runs,
-                          hipStream_t st) {
+hipError_t launch_indexer(const IdxParams& p, int idx_dtype, int D, int grid, hipStream_t st) {
   const size_t plan_smem = p.T <= PLAN_LDS_T ? PLAN_LDS_BYTES : 0;
   hipError_t e = hipFuncSetAttribute((const void*)dsa_plan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)PLAN_LDS_BYTES);
@@ -1110,12 +1151,7 @@ hipError_t launch_indexer(const IdxParams& p, int idx_dtype, int D, int grid, bo
     e = small_heads ? launch_indexer_mq<0, 64, 1>(p, grid, st) : launch_indexer_mq<0, 64, 4>(p, grid, st);
   else
     e = small_heads ? launch_indexer_mq<0, 128, 1>(p, grid, st) : launch_indexer_mq<0, 128, 4>(p, grid, st);
-  if (e != hipSuccess || !need_merge) return e;
-  const size_t smem = sizeof(MergeSmem);
-  e = hipFuncSetAttribute((const void*)dsa_merge_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(dsa_merge_kernel, dim3(p.T, merge_runs), dim3(MRG_NT), smem, st, p);
-  return hipGetLastError();
+  return e;
 }
 
 }  // namespace dsa
