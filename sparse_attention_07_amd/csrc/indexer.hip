@@ -227,7 +227,7 @@ struct SelRule {
 };
 
 // Finds the rule that keeps exactly min(K, candidates) entries (all of them
-// when there are at most K).  hist: 2 * NW * 256 words; wtmp: 8 * NW words;
+// when there are at most K).  hist: 2 * NW * 256 words, 16-byte aligned; wtmp: 8 * NW words;
 // sel: 4 words.  Ends with every wave past its last LDS read of wtmp.
 template <int NW, int R>
 __device__ __forceinline__ SelRule select_rule(const uint32_t (&rk)[R], const int32_t (&rp)[R], int K,
@@ -308,15 +308,17 @@ __device__ __forceinline__ SelRule select_rule(const uint32_t (&rk)[R], const in
     lds_barrier();
     if (tid < 64) {
       // lane L owns bins 255-4L .. 252-4L (descending), summed over the waves
-      uint32_t c[4], sum = 0;
+      // (one 16-byte read per wave histogram)
+      uint32_t c[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint32_t v = 0;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) v += hb[w * 256 + 255 - 4 * lane - j];
-        c[j] = v;
-        sum += v;
+      for (int w = 0; w < NW; ++w) {
+        const v4u v = *reinterpret_cast<const v4u*>(hb + w * 256 + 252 - 4 * lane);
+        c[0] += v.w;
+        c[1] += v.z;
+        c[2] += v.y;
+        c[3] += v.x;
       }
+      const uint32_t sum = c[0] + c[1] + c[2] + c[3];
       const uint32_t incl = wave_incl_scan(sum);
       const uint32_t excl = incl - sum;
       if (excl < (uint32_t)need && (uint32_t)need <= incl) {
@@ -526,6 +528,9 @@ constexpr int MRG_RS = 32;                  // entries per lane per chunk
 constexpr int MRG_CHUNK = MRG_RS * MRG_NT;  // 16384
 constexpr int MRG_CAP = 16384;              // LDS candidate buffer
 constexpr int MRG_FAN = MERGE_FAN;          // lists one single-chunk merge takes
+constexpr int MRG_BT = 2048;                // block-table entries a final merge stages in LDS
+static_assert(KMAX + MRG_BT <= MRG_CAP, "staged block table after the kept entries");
+static_assert(MRG_BT == 4 * MRG_NT, "block-table staging: one 16-byte piece per lane");
 static_assert(MRG_FAN * KMAX <= MRG_CHUNK, "a run of MRG_FAN lists is one chunk");
 
 struct MergeSmem {
@@ -656,6 +661,22 @@ __device__ __forceinline__ void merge_query(const IdxParams& p, int t, int j, Me
   const int seq = gr[G_SEQ];
   const int64_t unit0 = (int64_t)gr[G_LIST] + (int64_t)(t - gr[G_T0]) * nl;
   const int K = p.K;
+  const int32_t* bt = p.block_table + (int64_t)max(seq, 0) * p.max_blocks;
+  // The final step of a single-chunk merge copies the block-table slice
+  // into LDS (cand_key[KMAX ..] is unused then) with direct-to-LDS loads
+  // that fly while the lists load: 16 bytes (4 pages) per lane, so the row
+  // must be 16-byte aligned and a whole number of such pieces.
+  const int npg = (uniform(gr[G_RANGE]) + PAGE - 1) / PAGE;  // pages holding the group's keys
+  const bool stage = nrun == 1 && nl * K <= MRG_CHUNK && npg <= MRG_BT && (p.max_blocks & 3) == 0 &&
+                     ((uintptr_t)bt & 15) == 0;
+  int32_t* sbt = reinterpret_cast<int32_t*>(sm.cand_key + KMAX);
+  if (stage) {
+    const int wave = tid >> 6, lane = tid & 63;
+    const int c = wave * 64 + lane;      // pages 4c .. 4c + 3
+    const int cc = 4 * c < npg ? c : 0;  // past the slice: a harmless valid piece (its LDS slot is unused)
+    const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int32_t*)(sbt + 256 * wave);
+    dma16_to_lds(bt + 4 * cc, uniform(lds_addr));
+  }
   // this run's lists (the other runs may still be streaming)
   const int c0 = j * MRG_FAN;
   const int nj = nrun == 1 ? nl : min(MRG_FAN, nl - c0);
@@ -687,13 +708,16 @@ __device__ __forceinline__ void merge_query(const IdxParams& p, int t, int j, Me
     cnt = merge_lists(p.mlist_keys + unit0 * K, p.mlist_pos + unit0 * K, nrun, lb2, K, sm);
   }
   // ---- output: kept positions (in LDS, in order) to pool slots
-  const int32_t* bt = p.block_table + (int64_t)max(seq, 0) * p.max_blocks;
+  if (stage) {
+    wait_vm();  // this wave's block-table piece has landed
+    lds_barrier();
+  }
   int32_t* out = p.indices + (int64_t)t * K;
   for (int i = tid; i < K; i += MRG_NT) {
     int v = -1;
     if (i < cnt) {
       const int ps = sm.cand_pos[i];
-      v = bt[ps >> 6] * PAGE + (ps & 63);
+      v = (stage ? sbt[ps >> 6] : bt[ps >> 6]) * PAGE + (ps & 63);
     }
     out[i] = v;
   }
