@@ -106,24 +106,41 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
   const int wave = uniform(tid >> 6);
   const int g4 = lane >> 4;
   const int n16 = lane & 15;
-  const int t = blockIdx.y;
-  const int s = blockIdx.x;
+  // ---- workgroup -> (query, split).  Workgroups go to the 8 XCDs round-robin
+  // by linear id; with T a multiple of 8 the splits of a query are given ids of
+  // one XCD, so the query's q rows, which every split reads, come from that
+  // XCD's L2 after the first read instead of from HBM once per split.
+  int t, s;
+  {
+    const int id = blockIdx.y * gridDim.x + blockIdx.x;
+    if ((p.T & 7) == 0) {
+      const int k = id >> 3;
+      t = (k / p.S) * 8 + (id & 7);
+      s = k % p.S;
+    } else {
+      t = blockIdx.y;
+      s = blockIdx.x;
+    }
+    t = uniform(t);
+    s = uniform(s);
+  }
   const int r_begin = s * p.rows_per_split;
   const int r_end = min(p.K, r_begin + p.rows_per_split);
   const int nrows = max(0, r_end - r_begin);
   const int ntiles = (nrows + TILE_ROWS - 1) / TILE_ROWS;
 
-  // ---- the slice's pool slots (invalid -> -1)
-  for (int i = tid; i < ntiles * TILE_ROWS; i += NT) {
+  // ---- the slice's pool slots (invalid -> -1), and q of this wave's 16 heads
+  // as the logits B operand (k = latent dim).  The first NT slots are loaded
+  // before q, so the first tile's gather can start while q is in flight.
+  auto slot_of = [&](int i) {
     int v = -1;
     if (i < nrows) {
       v = p.indices[(int64_t)t * p.K + r_begin + i];
       if (v < 0 || (int64_t)v >= p.num_slots) v = -1;
     }
-    sidx[i] = v;
-  }
-
-  // ---- q of this wave's 16 heads as the logits B operand (k = latent dim)
+    return v;
+  };
+  const int v0 = slot_of(tid);
   const int hq = wave * 16 + n16;
   v4i qb[18];
   {
@@ -131,9 +148,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) qb[ks] = *reinterpret_cast<const v4i*>(qrow + 32 * ks + 8 * g4);
   }
-  // retire every plain global load here, so no compiler-inserted wait inside the
-  // tile loop can count (and drain) the row DMA queue
-  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+  if (tid < ntiles * TILE_ROWS) sidx[tid] = v0;
+  for (int i = tid + NT; i < ntiles * TILE_ROWS; i += NT) sidx[i] = slot_of(i);
   lds_barrier();
 
   constexpr int NSTAGE = MlaSmem<NW, KV8>::NSTAGE;
@@ -159,6 +175,14 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
       dma16_to_lds(g, uniform(lds_addr));
     }
   };
+
+  if (ntiles > 0) issue_tile(0);
+  // retire every plain global load here (tile 0 lands too), so no
+  // compiler-inserted wait inside the tile loop can count (and drain) the row
+  // DMA queue
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+  lds_barrier();
+
 
   v4f o[VT][NW];  // O^T[v tile][head tile]
 #pragma unroll
@@ -256,7 +280,6 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
     // tile ti-1 and the logits and softmax of tile ti (P^T and the rescale
     // factors are double-buffered).  The three gather stages hold tiles ti-1
     // (PV), ti (logits) and ti+1 (in flight), so gathers run one tile ahead.
-    if (ntiles > 0) issue_tile(0);
     for (int ti = 0; ti <= ntiles; ++ti) {
       __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // tile ti, the only one in flight, has landed
       lds_barrier_keep_dma();  // and every wave has left iteration ti-1 (stage (ti+1)%3 is free)
@@ -296,7 +319,6 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
             *reinterpret_cast<const v4i*>(src + 16 * KV8_ROW_UNITS * r + KV8_ROPE_OFF + 16 * j);
       }
     };
-    if (ntiles > 0) issue_tile(0);
     for (int ti = 0; ti <= ntiles; ++ti) {
       __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // tile ti, the only one in flight, has landed
       lds_barrier_keep_dma();  // every wave has left iteration ti-1: bf16 tile ti&1 and stage (ti+1)%2 are free
