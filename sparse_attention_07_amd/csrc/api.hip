@@ -19,6 +19,7 @@ namespace {
 
 constexpr int MLA_TARGET_WGS = 256;
 constexpr int MLA_MIN_ROWS = 256;
+constexpr int MLA_MAX_SPLITS = 8;
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -147,6 +148,7 @@ MlaPlan plan_mla(const dsa_mla_args* m, int K, size_t base) {
   MlaPlan pl;
   int S = (MLA_TARGET_WGS + m->T - 1) / m->T;
   S = std::max(1, std::min(S, std::max(1, K / MLA_MIN_ROWS)));
+  S = std::min(S, MLA_MAX_SPLITS);  // the combine kernel merges at most this many
   int rps = (K + S - 1) / S;
   rps = (rps + 31) / 32 * 32;
   S = (K + rps - 1) / rps;

@@ -43,6 +43,7 @@
 namespace dsa {
 
 constexpr int TILE_ROWS = 32;
+constexpr int MLA_SMAX = 8;  // most splits of a query's index list (K / 256 for K <= 2048)
 constexpr int ROW_UNITS = LATENT * 2 / 16;                         // 72 sixteen-byte units per row
 constexpr int ROW_STRIDE = ROW_UNITS + 1;                          // padded row stride (units)
 constexpr int TILE_LOADS = (TILE_ROWS * ROW_STRIDE + 63) / 64;     // 37 wave-loads of 64 units
@@ -432,20 +433,29 @@ __global__ __launch_bounds__(256) void dsa_mla_combine_kernel(MlaParams p) {
   const int64_t th = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // t * H + h
   const int t = (int)(th / p.H), h = (int)(th % p.H);
   const int v = (threadIdx.x & 63) * 8;
+  // every split's (m, l) and partial row in one round of loads (splits past S
+  // repeat the last one and get weight 0), then the weights
+  float ms[MLA_SMAX], ls[MLA_SMAX];
+  uint4 raw[MLA_SMAX];
+#pragma unroll
+  for (int s = 0; s < MLA_SMAX; ++s) {
+    const int64_t rowi = ((int64_t)t * p.S + min(s, p.S - 1)) * p.H + h;
+    ms[s] = p.part_ml[rowi * 2];
+    ls[s] = p.part_ml[rowi * 2 + 1];
+    raw[s] = *reinterpret_cast<const uint4*>(p.part_o + rowi * VDIM + v);
+  }
   float M = -INFINITY;
-  for (int s = 0; s < p.S; ++s) M = fmaxf(M, p.part_ml[(((int64_t)t * p.S + s) * p.H + h) * 2]);
+#pragma unroll
+  for (int s = 0; s < MLA_SMAX; ++s) M = s < p.S ? fmaxf(M, ms[s]) : M;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
   if (M != -INFINITY) {
-    for (int s = 0; s < p.S; ++s) {
-      const int64_t rowi = ((int64_t)t * p.S + s) * p.H + h;
-      const float ms = p.part_ml[rowi * 2], ls = p.part_ml[rowi * 2 + 1];
-      if (ms == -INFINITY) continue;
-      const float wgt = exp2f(ms - M) * ls;
+#pragma unroll
+    for (int s = 0; s < MLA_SMAX; ++s) {
+      const float wgt = (s < p.S && ms[s] != -INFINITY) ? exp2f(ms[s] - M) * ls[s] : 0.f;
       L += wgt;
-      const uint4 raw = *reinterpret_cast<const uint4*>(p.part_o + rowi * VDIM + v);
       _Float16 h8[8];
-      __builtin_memcpy(h8, &raw, 16);
+      __builtin_memcpy(h8, &raw[s], 16);
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] += wgt * (float)h8[i];
     }
