@@ -12,8 +12,9 @@
 //    index list and all H heads, so every gathered row leaves HBM once;
 //  * rows are gathered 32 at a time with direct-to-LDS 16-byte loads
 //    (global_load_lds_dwordx4) into a 3-stage ring; rows sit at a padded
-//    stride of 73 sixteen-byte units (1168 B = 292 dwords, so consecutive rows
-//    start 36 banks apart) and operand addresses stay base + immediate;
+//    stride of 74 sixteen-byte units in a permuted slot order that makes the
+//    operand reads of both phases free of bank conflicts (see row_slot), and
+//    operand addresses stay base + immediate;
 //  * H/16 waves.  Logits: wave w owns heads 16w..16w+15, keeps their q in
 //    registers as the MFMA B operand and computes S^T = C q^T (bf16 16x16x32;
 //    rows on M in an order that makes the probabilities come out as 8
@@ -45,8 +46,9 @@ namespace dsa {
 constexpr int TILE_ROWS = 32;
 constexpr int MLA_SMAX = 8;  // most splits of a query's index list (K / 256 for K <= 2048)
 constexpr int ROW_UNITS = LATENT * 2 / 16;                         // 72 sixteen-byte units per row
-constexpr int ROW_STRIDE = ROW_UNITS + 1;                          // padded row stride (units)
+constexpr int ROW_STRIDE = ROW_UNITS + 2;                          // padded row stride (units)
 constexpr int TILE_LOADS = (TILE_ROWS * ROW_STRIDE + 63) / 64;     // 37 wave-loads of 64 units
+constexpr int PT_STRIDE = TILE_ROWS + 16;                          // P^T row (bf16): 6 sixteen-byte units
 constexpr int STAGES = 3;
 constexpr int STAGE_BYTES = TILE_LOADS * 64 * 16;
 
@@ -58,14 +60,27 @@ constexpr int KV8_TILE_LOADS = (TILE_ROWS * KV8_ROW_UNITS + 63) / 64;  // 21 wav
 constexpr int KV8_STAGE_BYTES = KV8_TILE_LOADS * 64 * 16;
 
 // byte offset, inside a stage, of bf16 element (row r, column col)
-__device__ __forceinline__ int stage_off(int r, int col) { return 16 * (r * ROW_STRIDE + (col >> 3)) + 2 * (col & 7); }
+// LDS layout of a tile (bank conflicts measured with the LDS counters on
+// gfx950): a wave's 16-byte reads that put 16 lanes on 16 rows, the 4 lane
+// groups one unit apart, are conflict-free when the rows lie 2 mod 4 units
+// apart (74 here) and take 2-4 cycles more otherwise.  The logits A operand
+// of M-tile mt reads tile rows 8*(n/4) + n%4 + 4*mt for lanes n = 0..15, so
+// tile row r is stored in slot p(r) = 4*(r/8) + r%4 + 16*((r/4)%2): each
+// M-tile reads 16 consecutive slots.  The PV transpose reads (rows 8*g + j
+// and 8*g + 4 + j) then also fall on consecutive slots.
+__device__ __forceinline__ int row_slot(int r) { return 4 * (r >> 3) + (r & 3) + 16 * ((r >> 2) & 1); }
+__device__ __forceinline__ int slot_row(int p) { return 8 * ((p & 15) >> 2) + (p & 3) + 4 * (p >> 4); }
+__device__ __forceinline__ int row_unit(int r) { return ROW_STRIDE * row_slot(r); }
+
+// byte offset, inside a stage, of bf16 element (row r, column col)
+__device__ __forceinline__ int stage_off(int r, int col) { return 16 * (row_unit(r) + (col >> 3)) + 2 * (col & 7); }
 
 template <int NW, bool KV8>
 struct MlaSmem {
   static constexpr int NSTAGE = KV8 ? 2 : STAGES;
   unsigned char stage[NSTAGE][KV8 ? KV8_STAGE_BYTES : STAGE_BYTES];  // gather ring
   unsigned char tile[KV8 ? 2 : 1][KV8 ? STAGE_BYTES : 16];          // FP8 only: two dequantized bf16 tiles
-  uint16_t pt[2][16 * NW][TILE_ROWS];  // P^T as [head][row] bf16, two tiles
+  uint16_t pt[2][16 * NW][PT_STRIDE];  // P^T as [head][row] bf16, two tiles (rows padded: no bank conflicts)
   float alpha[2][16 * NW];             // per-head rescale factor, two tiles
   float mfin[16 * NW];
   float lfin[16 * NW];
@@ -161,12 +176,13 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
     for (int k = 0; k < nl; ++k) {
       const int u0 = (first + k) * 64;
       const int u = u0 + lane;
-      int r = u / RUNITS;
+      int r = u / RUNITS;  // FP8: row; bf16: slot
       int c = u - r * RUNITS;
       if (r >= TILE_ROWS || c >= (KV8 ? KV8_ROW_UNITS : ROW_UNITS)) {  // padding slot: a harmless valid unit
         r = min(r, TILE_ROWS - 1);
         c = 0;
       }
+      if constexpr (!KV8) r = slot_row(r);
       int slot = sidx[ti * TILE_ROWS + r];
       slot = slot < 0 ? 0 : slot;
       const uint16_t* g = KV8 ? p.kv + (int64_t)slot * (KV8_ROW_UNITS * 8) + 8 * c
@@ -198,8 +214,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
     const uint32_t vmask = (uint32_t)ballot(lane < 32 && sidx[ti * TILE_ROWS + (lane & 31)] >= 0);
     v4f acc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
     // M-tile row n16 holds tile row 8*(n16/4) + 4*mt + n16%4; k-step ks adds 64 bytes
-    const unsigned char* la0 = st + 16 * ((8 * (n16 >> 2) + (n16 & 3)) * ROW_STRIDE + g4);
-    const unsigned char* la1 = la0 + 16 * 4 * ROW_STRIDE;
+    const unsigned char* la0 = st + 16 * (row_unit(8 * (n16 >> 2) + (n16 & 3)) + g4);  // slot n16
+    const unsigned char* la1 = la0 + 16 * 16 * ROW_STRIDE;                              // slot 16 + n16
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) {
       const v4i a0 = *reinterpret_cast<const v4i*>(la0 + 64 * ks);
@@ -263,7 +279,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
       for (int vt = 0; vt < VT; ++vt) {
         const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(tb + 32 * vt));
         const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4s*)(tb + 16 * 4 * ROW_STRIDE + 32 * vt));
+            (__attribute__((address_space(3))) v4s*)(tb + 16 * 16 * ROW_STRIDE + 32 * vt));  // row + 4: slot + 16
         av[vt] = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
 #pragma unroll
@@ -309,14 +325,14 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
         const float sc = *reinterpret_cast<const float*>(rowp + KV8_SCALE_OFF + 4 * (k >> 3));
         v4i lo, hi;
         dequant16(c16, sc, lo, hi);
-        unsigned char* d = dst + 16 * (r * ROW_STRIDE + 2 * k);
+        unsigned char* d = dst + 16 * (row_unit(r) + 2 * k);
         *reinterpret_cast<v4i*>(d) = lo;
         *reinterpret_cast<v4i*>(d + 16) = hi;
       }
 #pragma unroll 1
       for (int i = tid_o; i < TILE_ROWS * 8; i += NT) {  // rope: 8 units per row, copied
         const int r = i >> 3, j = i & 7;
-        *reinterpret_cast<v4i*>(dst + 16 * (r * ROW_STRIDE + 64 + j)) =
+        *reinterpret_cast<v4i*>(dst + 16 * (row_unit(r) + 64 + j)) =
             *reinterpret_cast<const v4i*>(src + 16 * KV8_ROW_UNITS * r + KV8_ROPE_OFF + 16 * j);
       }
     };
