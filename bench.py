@@ -8,8 +8,10 @@ default workload is 64 decoding sequences with cached lengths uniform in
 
 Prints one JSON line.  `value` is decode query tokens per second of the whole
 layer; `roofline` reports the indexer kernel's algorithmic HBM bytes per launch
-over its event-timed launch duration; `cpu_baseline` is the CPU oracle timed on
-a bounded sample of the same workload.
+over its event-timed launch duration (or, where the indexer's algorithmic flops
+per byte exceed the MFMA ridge, as in chunked prefill, its FP8 / bf16 MFMA
+flops against the dense MFMA peak); `cpu_baseline` is the CPU oracle timed on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -23,6 +25,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+# dense MFMA peaks of the chip (TFLOP/s): FP8 for an FP8 / MXFP8 index, bf16 otherwise
+MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "mxfp8": 5000.0, "bf16": 2500.0}
 METRIC = "DSA decode tokens/s + % HBM roofline (indexer+top-k+sparse MLA, 128K ctx)"
 
 
@@ -123,6 +127,24 @@ def algorithmic_bytes(case, indices, epilogue=False):
     if epilogue:  # residual read, new residual written, norm weight read
         mla_bytes += T * s.H * 512 * 2 * 2 + s.H * 512 * 2
     return idx_bytes, idx_bytes + mla_bytes
+
+
+def algorithmic_flops(case, indices):
+    """Multiply-adds (x2) the method itself must do per step: the indexer's
+    H_i x D_i dot product for every visible key of every query, and the sparse
+    MLA's logits (576 dims) and PV (512 dims) over every selected row and head."""
+    s = case.spec
+    lens = case.seq_lens.tolist()
+    seqs = case.q_seq.tolist()
+    maxlen = case.block_table.shape[1] * 64
+    if case.q_visible is not None:
+        vis = [min(max(v, 0), min(lens[b], maxlen)) for v, b in zip(case.q_visible.tolist(), seqs)]
+    else:
+        vis = [min(lens[b], maxlen) for b in seqs]
+    idx_flops = 2 * s.H_idx * s.D_idx * sum(vis)
+    rows = int((indices >= 0).sum().item())
+    mla_flops = 2 * s.H * (576 + 512) * rows
+    return idx_flops, mla_flops
 
 
 def cpu_baseline(case, n_sample):
@@ -310,7 +332,27 @@ def main():
     idx_ms = e0.elapsed_time(e1) / n_idx
 
     idx_bytes, layer_bytes = algorithmic_bytes(case, layers[0].indices, args.epilogue)
+    idx_flops, mla_flops = algorithmic_flops(case, layers[0].indices)
     achieved = idx_bytes / (idx_ms * 1e-3) / 1e9
+    # the indexer's bound: MFMA when its flops per algorithmic byte exceed the
+    # chip's ridge (prefill: each key serves thousands of queries), else HBM
+    mfma_peak = MFMA_PEAK_TFLOPS[spec.idx_dtype]
+    if idx_flops / idx_bytes > mfma_peak * 1e12 / (HBM_PEAK_GBPS * 1e9):
+        tflops = idx_flops / (idx_ms * 1e-3) / 1e12
+        roofline = {
+            "bound": "mfma", "achieved": round(tflops, 1), "peak": mfma_peak, "unit": "TFLOP/s",
+            "frac": round(tflops / mfma_peak, 4), "traffic": stored_traffic(f"indexer_traffic_{spec.name}"),
+            "kernel": "dsa_indexer_topk: planning + dsa_indexer_kernel (Top-K and list merge)",
+            "launch_ms": round(idx_ms, 5), "algorithmic_flops": idx_flops, "algorithmic_bytes": idx_bytes,
+            "dtype": "fp8" if spec.idx_dtype != "bf16" else "bf16",
+        }
+    else:
+        roofline = {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": stored_traffic(f"indexer_traffic_{spec.name}"),
+            "kernel": "dsa_indexer_topk: planning + dsa_indexer_kernel (Top-K and list merge)",
+            "launch_ms": round(idx_ms, 5), "algorithmic_bytes": idx_bytes,
+        }
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -333,15 +375,13 @@ def main():
             "input_copies_rotated": len(layers), "parallelism": "single GPU",
             "epilogue": "residual + RMSNorm" if args.epilogue else None,
         },
-        "roofline": {
-            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": stored_traffic(f"indexer_traffic_{spec.name}"),
-            "kernel": "dsa_indexer_topk: planning + dsa_indexer_kernel (Top-K and list merge)",
-            "launch_ms": round(idx_ms, 5), "algorithmic_bytes": idx_bytes,
-        },
+        "roofline": roofline,
         "layer": {
             "algorithmic_bytes": layer_bytes, "GBps": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
             "frac_hbm": round(layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "algorithmic_flops": idx_flops + mla_flops,
+            "TFLOPs": round((idx_flops + mla_flops) / (ms * 1e-3) / 1e12, 1),
+            "mla_flops_bf16": mla_flops,
         },
     }
     if not args.no_cpu_baseline:
