@@ -47,6 +47,22 @@ __device__ __forceinline__ float sum_lane_groups(float v) {
   return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
+// Four such sums at once: x[r] holds one 16-wide column set in each of the
+// four lane groups; afterwards lane group r holds the column sums of x[r]
+// (column = lane & 15).  x0 and x2 are folded across the two halves of the
+// wave, x1 and x3 likewise, then the two results across odd and even rows:
+// three swaps and three adds instead of eight of each.
+__device__ __forceinline__ float sum_lane_groups4(float x0, float x1, float x2, float x3) {
+  // permlane32_swap(a, b) -> {[a lanes 0-31, b lanes 0-31], [a lanes 32-63, b lanes 32-63]}
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x0), __float_as_uint(x2), false, false);
+  const float u = __uint_as_float(a[0]) + __uint_as_float(a[1]);  // rows: x0 (r0+r2, r1+r3), x2 (r0+r2, r1+r3)
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x1), __float_as_uint(x3), false, false);
+  const float v = __uint_as_float(b[0]) + __uint_as_float(b[1]);  // rows: x1 (..), x1 (..), x3 (..), x3 (..)
+  // permlane16_swap(a, b) -> {[a r0, b r0, a r2, b r2], [a r1, b r1, a r3, b r3]}
+  auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(u), __float_as_uint(v), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);  // rows: x0, x1, x2, x3
+}
+
 // Sum over all 64 lanes of a wave, returned to every lane (epilogue use only).
 __device__ __forceinline__ float wave_sum_f32(float v) {
 #pragma unroll

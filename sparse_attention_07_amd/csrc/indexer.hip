@@ -782,6 +782,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
   // register prefetch depth (16-key groups): up to about 17 KB of loads in flight per wave
   constexpr int PF = (MQ == 1 && ROWB <= 128) ? 8 : 4;
   static_assert(GPW % PF == 0, "prefetch ring must divide the round");
+  static_assert(GPW % 4 == 0, "groups are scored four at a time");
+  constexpr int NQD = GPW / 4;  // quads of groups per wave per round
   static_assert(DT == 0 || D == 128, "fp8 path is 128-wide");
 
   static_assert(NW == MRG_NW, "the merge runs in the indexer's workgroup");
@@ -936,50 +938,73 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
         bf.ok = ok;
       };
 
-      auto score_group = [&](const BFrag<DT, D>& bf, int p0, uint32_t (&kk)[MQ][GPW], int s) {
+      // One 16-key group: each lane sums w * ReLU(q . k) over its 4 rows of
+      // every head tile (16 of the 64 heads) for key n16; the four lane groups
+      // are summed later, four groups at once.  Every query's MFMAs go first
+      // (independent accumulators), then the VALU.  Queries past the group's
+      // count have zero operands and no visible keys, so they need no branch.
+      auto partial_group = [&](const BFrag<DT, D>& bf, float (&part)[MQ][4], int u) {
+        v4f acc[MQ][HT];
+#pragma unroll
+        for (int q = 0; q < MQ; ++q)
+#pragma unroll
+          for (int mt = 0; mt < HT; ++mt) {
+            acc[q][mt] = v4f{0.f, 0.f, 0.f, 0.f};
+            if constexpr (DT == 1) {
+              const v8i av = __builtin_shufflevector(a[q][mt].d[0], a[q][mt].d[1], 0, 1, 2, 3, 4, 5, 6, 7);
+              const v8i bv = __builtin_shufflevector(bf.f.d[0], bf.f.d[1], 0, 1, 2, 3, 4, 5, 6, 7);
+              acc[q][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[q][mt], 0, 0, 0, 0, 0, 0);
+            } else if constexpr (DT == 2) {
+              // group scales applied by the MFMA: A = q (E8M0 in qsx), B = keys
+              const v8i av = __builtin_shufflevector(a[q][mt].d[0], a[q][mt].d[1], 0, 1, 2, 3, 4, 5, 6, 7);
+              const v8i bv = __builtin_shufflevector(bf.f.d[0], bf.f.d[1], 0, 1, 2, 3, 4, 5, 6, 7);
+              acc[q][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[q][mt], 0, 0, 0, qsx[q][mt],
+                                                                            0, __float_as_int(bf.sc));
+            } else {
+#pragma unroll
+              for (int j = 0; j < Frag<DT, D>::NP; ++j)
+                acc[q][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[q][mt].d[j]),
+                                                                     __builtin_bit_cast(v8bf, bf.f.d[j]), acc[q][mt],
+                                                                     0, 0, 0);
+            }
+          }
 #pragma unroll
         for (int q = 0; q < MQ; ++q) {
-          if (q < nq) {
-            // all head tiles' MFMAs first (independent accumulators), then the VALU
-            v4f acc[HT];
+          float sum = 0.f;
 #pragma unroll
-            for (int mt = 0; mt < HT; ++mt) {
-              acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
-              if constexpr (DT == 1) {
-                const v8i av = __builtin_shufflevector(a[q][mt].d[0], a[q][mt].d[1], 0, 1, 2, 3, 4, 5, 6, 7);
-                const v8i bv = __builtin_shufflevector(bf.f.d[0], bf.f.d[1], 0, 1, 2, 3, 4, 5, 6, 7);
-                acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[mt], 0, 0, 0, 0, 0, 0);
-              } else if constexpr (DT == 2) {
-                // group scales applied by the MFMA: A = q (E8M0 in qsx), B = keys
-                const v8i av = __builtin_shufflevector(a[q][mt].d[0], a[q][mt].d[1], 0, 1, 2, 3, 4, 5, 6, 7);
-                const v8i bv = __builtin_shufflevector(bf.f.d[0], bf.f.d[1], 0, 1, 2, 3, 4, 5, 6, 7);
-                acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[mt], 0, 0, 0, qsx[q][mt], 0,
-                                                                           __float_as_int(bf.sc));
-              } else {
+          for (int mt = 0; mt < HT; ++mt)
 #pragma unroll
-                for (int j = 0; j < Frag<DT, D>::NP; ++j)
-                  acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[q][mt].d[j]),
-                                                                    __builtin_bit_cast(v8bf, bf.f.d[j]), acc[mt], 0,
-                                                                    0, 0);
-              }
+            for (int i = 0; i < 4; ++i) {
+              // ReLU as an integer max on the bit pattern: negative floats
+              // (sign bit set) become +0, everything else is unchanged
+              const float d = __int_as_float(max(__float_as_int(acc[q][mt][i]), 0));
+              sum = fmaf(wv[q][mt][i], d, sum);
             }
-            float part = 0.f;
+          // pinned here: sinking the sum to the quad's end would keep every
+          // group's accumulators alive at once
+          asm volatile("" : "+v"(sum));
+          part[q][u] = sum;
+        }
+        // the group's MFMAs back to back, then its VALU: interleaving them
+        // would make each MFMA wait for the previous tile's ReLU
+        __builtin_amdgcn_sched_group_barrier(0x008, MQ * HT * (DT == 0 ? Frag<DT, D>::NP : 1), 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 1000, 0);
+      };
+
+      // Four consecutive groups (64 keys from p0): after the cross-lane sum,
+      // lane l holds the score of key p0 + l, whose group is lane group g4.
+      // sc4 / ok4: the key scale and page validity each group's load gave.
+      auto finish_quad = [&](const float (&part)[MQ][4], const float (&sc4)[4], const int (&ok4)[4], int p0,
+                             uint32_t (&kk)[MQ]) {
+        float ksc = 1.f;
+        if (DT == 1) ksc = g4 == 0 ? sc4[0] : g4 == 1 ? sc4[1] : g4 == 2 ? sc4[2] : sc4[3];
+        const int okl = g4 == 0 ? ok4[0] : g4 == 1 ? ok4[1] : g4 == 2 ? ok4[2] : ok4[3];
+        const int pos = p0 + lane;
 #pragma unroll
-            for (int mt = 0; mt < HT; ++mt)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                // ReLU as an integer max on the bit pattern: negative floats
-                // (sign bit set) become +0, everything else is unchanged
-                const float d = __int_as_float(max(__float_as_int(acc[mt][i]), 0));
-                part = fmaf(wv[q][mt][i], d, part);
-              }
-            float sc = sum_lane_groups(part);
-            if (DT == 1) sc *= bf.sc;
-            const bool valid = bf.ok && p0 + n16 < lim[q];
-            kk[q][s] = valid ? order_key(sc) : 0u;
-          } else {
-            kk[q][s] = 0u;
-          }
+        for (int q = 0; q < MQ; ++q) {
+          float sc = sum_lane_groups4(part[q][0], part[q][1], part[q][2], part[q][3]);
+          if (DT == 1) sc *= ksc;
+          kk[q] = (okl && pos < lim[q]) ? order_key(sc) : 0u;
         }
       };
 
@@ -998,19 +1023,29 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
       for (int r = 0; r < nrounds; ++r) {
-        // score this wave's GPW groups (keys stay in lanes 0..15 of each)
-        uint32_t kk[MQ][GPW];
+        // score this wave's GPW groups, four at a time (one key per lane);
+        // keys past the sub-chunk end fail the visibility test
+        uint32_t kk[MQ][NQD];
 #pragma unroll
-        for (int s = 0; s < GPW; ++s) {
-          const int j = r * GPW + s;
-          const int p0 = group_p0(j);
-          if (p0 < ke) {
-            score_group(buf[s % PF], p0, kk, s);
-          } else {
+        for (int qd = 0; qd < NQD; ++qd) {
+          float part[MQ][4];
+          float sc4[4];
+          int ok4[4];
 #pragma unroll
-            for (int q = 0; q < MQ; ++q) kk[q][s] = 0u;
+          for (int u = 0; u < 4; ++u) {
+            const int s = 4 * qd + u;
+            partial_group(buf[s % PF], part, u);
+            sc4[u] = buf[s % PF].sc;
+            ok4[u] = buf[s % PF].ok;
+            load_b(buf[s % PF], load_p0(r * GPW + s + PF));
+            // one group at a time: hoisting the next group's MFMAs would need
+            // a second accumulator set
+            __builtin_amdgcn_sched_barrier(0);
           }
-          load_b(buf[s % PF], load_p0(j + PF));
+          uint32_t kq[MQ];
+          finish_quad(part, sc4, ok4, group_p0(r * GPW + 4 * qd), kq);
+#pragma unroll
+          for (int q = 0; q < MQ; ++q) kk[q][qd] = kq[q];
         }
         // append the keys above each query's bound: a wave's groups are
         // consecutive positions and waves follow each other, so a wave's
@@ -1020,7 +1055,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
         auto count_round = [&](int q) {
           uint32_t wc = 0;
 #pragma unroll
-          for (int s = 0; s < GPW; ++s) wc += (uint32_t)__builtin_popcountll(ballot(lane < 16 && kk[q][s] > thr[q]));
+          for (int qd = 0; qd < NQD; ++qd) wc += (uint32_t)__builtin_popcountll(ballot(kk[q][qd] > thr[q]));
           if (lane == 0) sm.wcnt[rpar][q][wave] = wc;
         };
 #pragma unroll
@@ -1054,13 +1089,13 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
             }
             int o = cnt[q] + pre;
 #pragma unroll
-            for (int s = 0; s < GPW; ++s) {
-              const bool t = lane < 16 && kk[q][s] > thr[q];
+            for (int qd = 0; qd < NQD; ++qd) {
+              const bool t = kk[q][qd] > thr[q];
               const uint64_t m = ballot(t);
               if (t) {
                 const int oo = o + lanes_below(m);
-                sm.cand_key[q][oo] = kk[q][s];
-                sm.cand_pos[q][oo] = group_p0(r * GPW + s) + lane;
+                sm.cand_key[q][oo] = kk[q][qd];
+                sm.cand_pos[q][oo] = group_p0(r * GPW + 4 * qd) + lane;
               }
               o += (int)__builtin_popcountll(m);
             }
