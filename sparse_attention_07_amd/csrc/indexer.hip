@@ -752,7 +752,11 @@ struct IdxSmem {
   uint32_t wcnt[2][MQ][NW];  // per-round candidate counts of each wave (rounds alternate)
   uint32_t red[8 * NW];
   int32_t sel[4];
-  int32_t pages[SUB / PAGE + 1];  // the sub-chunk's block-table slice (-1 = invalid page); +1 when unaligned
+  // the sub-chunk's block-table slice as byte offsets of the pages in the
+  // pool, in 256-byte units (every page layout is a multiple of 256 bytes,
+  // and with at most 2^25 pages of at most 16 KB the offsets fit 32 bits);
+  // ~0 marks an invalid page.  +1 entry when the slice is unaligned.
+  uint32_t pages[SUB / PAGE + 1];
   float wq[MQ][64];               // head weight x query scale of the group's queries
 };
 
@@ -899,7 +903,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
       }
       for (int i = tid; i <= ((ke - 1) >> 6) - pg0; i += NT) {
         const int pg = bt[pg0 + i];
-        sm.pages[i] = (pg >= 0 && (int64_t)pg < p.num_blocks) ? pg : -1;
+        sm.pages[i] = (pg >= 0 && (int64_t)pg < p.num_blocks) ? (uint32_t)pg * (uint32_t)(p.page_bytes >> 8) : ~0u;
       }
       lds_barrier();
       if (kb == seg_lo) {
@@ -918,22 +922,24 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
       const int nrounds = (nkeys + ROUND - 1) / ROUND;
       auto group_p0 = [&](int j) { return kb + (j / GPW) * ROUND + (wave * GPW + (j % GPW)) * 16; };
 
-      auto load_b = [&](BFrag<DT, D>& bf, int p0) {
-        int page = sm.pages[(p0 >> 6) - pg0];
-        const bool ok = page >= 0;
-        page = ok ? page : 0;
-        const int r = (p0 & 63) + n16;
-        const uint8_t* pgp = p.k_pool + (int64_t)page * p.page_bytes;
-        const uint8_t* rowp = pgp + r * ROWB;
+      // Page entry of the group at p0 (read one group ahead of its load, so
+      // the LDS latency is spent under the current group's MFMAs).
+      auto page_of = [&](int p0) { return sm.pages[(p0 >> 6) - pg0]; };
+      // The group's rows: a uniform base (page and first row) plus a 32-bit
+      // per-lane offset, so the loads take the scalar-base form.
+      auto load_b = [&](BFrag<DT, D>& bf, int p0, uint32_t pu) {
+        const bool ok = pu != ~0u;
+        const uint8_t* rowp = p.k_pool + ((uint64_t)(ok ? pu : 0u) << 8) + (p0 & 63) * ROWB;
 #pragma unroll
         for (int j = 0; j < Frag<DT, D>::NP; ++j) {
-          const int off_b = DT == 0 ? 2 * (32 * j + 8 * g4) : (64 * j + 16 * g4);
+          const uint32_t off_b = n16 * ROWB + (DT == 0 ? 2 * (32 * j + 8 * g4) : (64 * j + 16 * g4));
           bf.f.d[j] = *reinterpret_cast<const v4i*>(rowp + off_b);
         }
         // FP8: the key's fp32 scale; MXFP8: the E8M0 byte of group g4 of key r
-        // (carried in sc's bits)
-        if (DT == 1) bf.sc = *reinterpret_cast<const float*>(pgp + PAGE * ROWB + 4 * r);
-        else if (DT == 2) bf.sc = __int_as_float((int)pgp[PAGE * ROWB + (D / 32) * r + g4]);
+        // (carried in sc's bits); the scales follow the page's 64 rows
+        const uint8_t* scp = p.k_pool + ((uint64_t)(ok ? pu : 0u) << 8) + PAGE * ROWB;
+        if (DT == 1) bf.sc = *reinterpret_cast<const float*>(scp + 4 * ((p0 & 63) + n16));
+        else if (DT == 2) bf.sc = __int_as_float((int)scp[(D / 32) * ((p0 & 63) + n16) + g4]);
         else bf.sc = 1.f;
         bf.ok = ok;
       };
@@ -985,8 +991,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
           asm volatile("" : "+v"(sum));
           part[q][u] = sum;
         }
-        // the group's MFMAs back to back, then its VALU: interleaving them
-        // would make each MFMA wait for the previous tile's ReLU
+        // the next page entry's LDS read, the group's MFMAs back to back, then
+        // its VALU: interleaving MFMAs and VALU would make each MFMA wait for
+        // the previous tile's ReLU
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, MQ * HT * (DT == 0 ? Frag<DT, D>::NP : 1), 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 1000, 0);
       };
@@ -1019,9 +1027,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
       BFrag<DT, D> buf[PF];
 #pragma unroll
       for (int s = 0; s < PF; ++s) {
-        load_b(buf[s], load_p0(s));
+        load_b(buf[s], load_p0(s), page_of(load_p0(s)));
         __builtin_amdgcn_sched_barrier(0);
       }
+      uint32_t pu_next = page_of(load_p0(PF));  // page of the next load
       for (int r = 0; r < nrounds; ++r) {
         // score this wave's GPW groups, four at a time (one key per lane);
         // keys past the sub-chunk end fail the visibility test
@@ -1034,10 +1043,12 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int s = 4 * qd + u;
+            const uint32_t pu = pu_next;
+            pu_next = page_of(load_p0(r * GPW + s + PF + 1));
             partial_group(buf[s % PF], part, u);
             sc4[u] = buf[s % PF].sc;
             ok4[u] = buf[s % PF].ok;
-            load_b(buf[s % PF], load_p0(r * GPW + s + PF));
+            load_b(buf[s % PF], load_p0(r * GPW + s + PF), pu);
             // one group at a time: hoisting the next group's MFMAs would need
             // a second accumulator set
             __builtin_amdgcn_sched_barrier(0);
