@@ -227,11 +227,15 @@ struct SelRule {
 };
 
 // Finds the rule that keeps exactly min(K, candidates) entries (all of them
-// when there are at most K).  hist: 2 * NW * 256 words, 16-byte aligned; wtmp: 8 * NW words;
-// sel: 4 words.  Ends with every wave past its last LDS read of wtmp.
+// when there are at most K).  With keep_max > K it may stop early, as soon as
+// the keys at or above the bin holding the K-th largest number at most
+// keep_max: the rule then keeps that whole bin (at least K entries, every one
+// of the Top-K among them), which is all a bound for later keys needs.
+// hist: 2 * NW * 256 words, 16-byte aligned; wtmp: 8 * NW words; sel: 4 words.
+// Ends with every wave past its last LDS read of wtmp.
 template <int NW, int R>
 __device__ __forceinline__ SelRule select_rule(const uint32_t (&rk)[R], const int32_t (&rp)[R], int K,
-                                               uint32_t* hist, int32_t* sel, uint32_t* wtmp) {
+                                               uint32_t* hist, int32_t* sel, uint32_t* wtmp, int keep_max = 0) {
   constexpr int NT = NW * 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t mn = 0xffffffffu, mx = 0u, pmn = 0xffffffffu, pmx = 0u, cnt = 0u;
@@ -344,6 +348,8 @@ __device__ __forceinline__ SelRule select_rule(const uint32_t (&rk)[R], const in
     ++pass;
     if (cb == need || (phase == 1 && sb == 0)) {
       done = true;
+    } else if (phase == 0 && K - need + cb <= keep_max) {
+      done = true;  // keys >= lo: the Top-K and the rest of their bin
     } else if (sb == 0) {
       // phase 0 resolved the key exactly; phase 1 cannot get here (positions
       // are distinct, so a resolved bin holds one entry)
@@ -400,12 +406,14 @@ __device__ __forceinline__ int select_output(const uint32_t (&rk)[R], const int3
 }
 
 // Top-K of keys/pos[0..n) in LDS (K < n <= R * NW * 64), in place: exactly K
-// entries remain at [0..K), in their original (position) order.  Returns the
-// smallest kept key: an entry at a later position whose key is <= it can
-// never enter.  hist: 2 * NW * 256 words; wtmp: 8 * NW words.
+// entries remain at [0..K), in their original (position) order (with
+// keep_max > K, between K and keep_max entries that include the Top-K; their
+// count goes to *kept).  Returns the smallest kept key: an entry at a later
+// position whose key is <= it can never enter.  hist: 2 * NW * 256 words;
+// wtmp: 8 * NW words.
 template <int NW, int R>
 __device__ __forceinline__ uint32_t block_select(uint32_t* keys, int32_t* pos, int n, int K, uint32_t* hist, int32_t* sel,
-                                                 uint32_t* wtmp) {
+                                                 uint32_t* wtmp, int keep_max = 0, int* kept = nullptr) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   lds_barrier();  // entries appended by other waves are visible
   const int chunk = (((n + NW - 1) / NW) + 63) & ~63;
@@ -422,12 +430,13 @@ __device__ __forceinline__ uint32_t block_select(uint32_t* keys, int32_t* pos, i
     rp[s] = pos[ic];
     rk[s] = (s * 64 < chunk && i < n) ? k : 0u;
   }
-  const SelRule rule = select_rule<NW, R>(rk, rp, K, hist, sel, wtmp);
+  const SelRule rule = select_rule<NW, R>(rk, rp, K, hist, sel, wtmp, keep_max);
   uint32_t kmin;
-  select_output<NW, R>(rk, rp, rule, wtmp, kmin, [&](int o, uint32_t k, int32_t ps) {
+  const int total = select_output<NW, R>(rk, rp, rule, wtmp, kmin, [&](int o, uint32_t k, int32_t ps) {
     keys[o] = k;
     pos[o] = ps;
   });
+  if (kept) *kept = total;
   return kmin;
 }
 
@@ -1083,10 +1092,12 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
               tot += c;
             }
             if (cnt[q] + tot > CAP) {
-              // cnt[q] > CAP - ROUND >= K, so the select has work to do
+              // cnt[q] > CAP - ROUND >= K, so the select has work to do; it
+              // leaves at most CAP - ROUND entries, so the round then fits
+              int kept;
               thr[q] = max(thr[q], block_select<NW, R>(sm.cand_key[q], sm.cand_pos[q], cnt[q], p.K, sm.hist,
-                                                       sm.sel, sm.red));
-              cnt[q] = p.K;
+                                                       sm.sel, sm.red, CAP - ROUND, &kept));
+              cnt[q] = kept;
               count_round(q);  // every wave read the old counts before the select's first barrier
               lds_barrier();
               pre = 0;
@@ -1136,14 +1147,22 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
           lds_barrier();  // other waves' appends are visible
         }
         if (nl == 1) {
+          // all block-table reads go out before the first store (clamped
+          // indices, masked afterwards), so their latencies overlap
           int32_t* out = p.indices + (int64_t)(t0 + q) * p.K;
-          for (int i = tid; i < p.K; i += NT) {
-            int v = -1;
-            if (i < c) {
-              const int ps = sm.cand_pos[q][i];
-              v = bt[ps >> 6] * PAGE + (ps & 63);
-            }
-            out[i] = v;
+          constexpr int OPT = (KMAX + NT - 1) / NT;  // output slots per thread
+          int ps[OPT], pg[OPT];
+#pragma unroll
+          for (int u = 0; u < OPT; ++u) {
+            const int i = tid + u * NT;
+            ps[u] = i < c ? sm.cand_pos[q][i] : -1;
+          }
+#pragma unroll
+          for (int u = 0; u < OPT; ++u) pg[u] = bt[max(ps[u], 0) >> 6];
+#pragma unroll
+          for (int u = 0; u < OPT; ++u) {
+            const int i = tid + u * NT;
+            if (i < p.K) out[i] = ps[u] >= 0 ? pg[u] * PAGE + (ps[u] & 63) : -1;
           }
         } else {
           const int64_t unit = (int64_t)list_base + (int64_t)q * nl + (blockIdx.x - w0);
