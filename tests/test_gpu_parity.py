@@ -4,11 +4,14 @@ Small cases are checked on every query; they span several key chunks, merge
 tree levels, 1024-key rounds and 32-row attention tiles, with ragged tails.
 The five named workloads run at full size in the launch configuration the
 benchmark times, with sampled queries checked one by one."""
+import dataclasses
+
+import numpy as np
 import pytest
 import torch
 
-from dsa_check import check_outputs
-from gpu_cases import bits16, check_queries, say
+from dsa_check import check_index_row, check_outputs
+from gpu_cases import bits16, check_queries, query_case, say
 from oracle import dsa_oracle as O
 from sparse_attention_07_amd import synth
 
@@ -161,6 +164,38 @@ def test_all_scores_tied_picks_lowest_positions():
         expect = (bt[t, pos // 64] * 64 + pos % 64).to(torch.int32)
         assert torch.equal(idx[t, :k], expect)
         assert (idx[t, k:] == -1).all()
+
+
+def test_absent_pages_are_skipped():
+    # block-table entries outside [0, num_blocks) (negative, or past the pool)
+    # mark pages as absent: their positions are never returned; the rest are
+    # ranked as if the absent ones did not exist (the first sequence spans
+    # several slices, so lists and the merge see the holes too)
+    sp = spec("absent_pages", lens=[9000, 3000], K=512, H=16, H_idx=16, seed=43)
+    case = synth.build_case(sp, device=DEV)
+    nb = case.num_blocks
+    bad = {0: {5: -1, 40: nb, 100: -7, 140: -1}, 1: {2: nb + 100}}
+    orig = dataclasses.replace(case, block_table=case.block_table.clone())
+    for b, m in bad.items():
+        for i, v in m.items():
+            case.block_table[b, i] = v
+    layer = dsa.layer_from_case(case)
+    layer()
+    torch.cuda.synchronize()
+    idx = layer.indices.cpu().numpy()
+    out = layer.out.float().cpu().numpy()
+    for t in range(case.T):
+        b = int(case.q_seq[t])
+        d, phys = query_case(orig, t)
+        S, _ = O.query_scores(d, 0)
+        keep = ~np.isin(np.arange(S.shape[0]) // 64, list(bad[b]))
+        ok, msg = check_index_row(idx[t], S[keep], phys[keep], sp.K)
+        say(f"  query {t}: {int(keep.sum())} of {S.shape[0]} positions present; index set: {msg}")
+        assert ok, msg
+        pos_of = {int(s): p for p, s in enumerate(phys)}
+        gpos = np.array([pos_of[int(s)] for s in idx[t] if s >= 0], dtype=np.int64)
+        ok, msg = check_outputs(out[t], O.mla_query(d, 0, gpos))
+        assert ok, msg
 
 
 def test_mla_score_outrun_takes_exact_max_path():
