@@ -18,20 +18,23 @@
 //    streams the same amount, whatever the sequence lengths;
 //  * each wave streams 16-key slices of 64-token pages straight into MFMA
 //    operand registers (per lane 64 contiguous bytes per key per load pair)
-//    through an 8-deep register prefetch ring; page ids come from an LDS copy
-//    of the segment's block-table slice, so no load in the ring depends on
-//    another;
+//    through a 4-deep register prefetch ring; page offsets come from an LDS
+//    copy of the segment's block-table slice, read one group ahead, so no
+//    load in the ring depends on another;
 //  * MFMA M = 16 indexer heads per tile, N = 16 keys, K = head dim
 //    (FP8: one 16x16x128 e4m3 MFMA per head tile; BF16: 16x16x32 steps);
+//    each group's MFMAs issue back to back into separate accumulators, then
 //    ReLU (an integer max on the bit pattern) and the head-weighted reduction
-//    run on the accumulators, then a 2-step permlane butterfly sums the four
-//    head groups of the tile;
+//    run on them; one permlane butterfly then sums the four head groups of
+//    four consecutive groups at once, leaving one key per lane (64 keys) for
+//    the key scale, the bound test and the candidate ballots;
 //  * selection streams: after each 1024-key round the keys above the current
 //    bound (a lower bound of the K-th score) are appended, in position order,
 //    to an LDS candidate buffer (one barrier per round: a wave's offset is
 //    the count of the waves before it); only when a round would not fit is
-//    the buffer cut back to K by a block radix select, which raises the
-//    bound;
+//    the buffer cut back by a block radix select, which raises the bound
+//    (it stops at the bin holding the K-th largest key once that bin fits:
+//    a bound needs no exact K; the final selection is exact);
 //  * a query whose keys span several slices gets one list per slice; the
 //    workgroup that writes the last of them (an arrival counter; lists are
 //    written and read device-coherent) merges them in the same launch: from the
