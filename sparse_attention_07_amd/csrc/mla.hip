@@ -444,17 +444,19 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
 // Merge S partial results per (query, head), with O_s = l_s * (O/l)_s:
 // out = sum_s e^(m_s-M) l_s (O/l)_s / sum_s e^(m_s-M) l_s.
 // A workgroup covers 4 (query, head) rows (one wave each, 8 values per lane);
-// H is a multiple of 4.
+// H is a multiple of 4.  SM >= S: the splits loaded per row (4 when S <= 4,
+// so no load repeats a split).
+template <int SM>
 __global__ __launch_bounds__(256) void dsa_mla_combine_kernel(MlaParams p) {
   const int64_t th = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // t * H + h
   const int t = (int)(th / p.H), h = (int)(th % p.H);
   const int v = (threadIdx.x & 63) * 8;
   // every split's (m, l) and partial row in one round of loads (splits past S
   // repeat the last one and get weight 0), then the weights
-  float ms[MLA_SMAX], ls[MLA_SMAX];
-  uint4 raw[MLA_SMAX];
+  float ms[SM], ls[SM];
+  uint4 raw[SM];
 #pragma unroll
-  for (int s = 0; s < MLA_SMAX; ++s) {
+  for (int s = 0; s < SM; ++s) {
     const int64_t rowi = ((int64_t)t * p.S + min(s, p.S - 1)) * p.H + h;
     ms[s] = p.part_ml[rowi * 2];
     ls[s] = p.part_ml[rowi * 2 + 1];
@@ -462,12 +464,12 @@ __global__ __launch_bounds__(256) void dsa_mla_combine_kernel(MlaParams p) {
   }
   float M = -INFINITY;
 #pragma unroll
-  for (int s = 0; s < MLA_SMAX; ++s) M = s < p.S ? fmaxf(M, ms[s]) : M;
+  for (int s = 0; s < SM; ++s) M = s < p.S ? fmaxf(M, ms[s]) : M;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
   if (M != -INFINITY) {
 #pragma unroll
-    for (int s = 0; s < MLA_SMAX; ++s) {
+    for (int s = 0; s < SM; ++s) {
       const float wgt = (s < p.S && ms[s] != -INFINITY) ? exp2f(ms[s] - M) * ls[s] : 0.f;
       L += wgt;
       _Float16 h8[8];
@@ -547,7 +549,10 @@ static hipError_t launch_mla_t(const MlaParams& p, hipStream_t st) {
   hipLaunchKernelGGL(kfn, dim3(p.S, p.T), dim3(NW * 64), smem, st, p);
   e = hipGetLastError();
   if (e != hipSuccess || p.S == 1) return e;
-  hipLaunchKernelGGL(dsa_mla_combine_kernel, dim3(p.T * p.H / 4), dim3(256), 0, st, p);
+  if (p.S <= 4)
+    hipLaunchKernelGGL(dsa_mla_combine_kernel<4>, dim3(p.T * p.H / 4), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL(dsa_mla_combine_kernel<MLA_SMAX>, dim3(p.T * p.H / 4), dim3(256), 0, st, p);
   e = hipGetLastError();
   if (e != hipSuccess || !p.residual) return e;
   hipLaunchKernelGGL(dsa_mla_norm_kernel, dim3(p.T * p.H / 4), dim3(256), 0, st, p);
