@@ -129,7 +129,9 @@ __global__ __launch_bounds__(PLAN_NT) void dsa_plan_kernel(IdxParams p) {
   }
   const int n_groups = carry_gid;
   // ---- pass 2: per-group key ranges and their offsets in the concatenated
-  // key space (each group padded to whole 16-key groups, at least one)
+  // key space (each group padded to whole 64-key pages, at least one, so
+  // every slice and segment starts on a page: four consecutive 16-key groups
+  // of the indexer are one page)
   int c_off = 0;
   for (int base = 0; base < n_groups; base += nt) {
     const int g = base + tid;
@@ -150,7 +152,7 @@ __global__ __launch_bounds__(PLAN_NT) void dsa_plan_kernel(IdxParams p) {
         s_nq[g] = t1 - t0;
         s_rng[g] = range;
       }
-      wgt = max(16, (range + 15) & ~15) + SEG_COST;
+      wgt = max(64, (range + 63) & ~63) + SEG_COST;
     }
     const int so = block_scan_incl(wgt, s_w, false);
     if (g < n_groups) {
@@ -163,7 +165,7 @@ __global__ __launch_bounds__(PLAN_NT) void dsa_plan_kernel(IdxParams p) {
     __syncthreads();
   }
   const int total = c_off;
-  const int slice = max(MIN_SLICE, (((total + p.nwg - 1) / p.nwg) + 15) & ~15);
+  const int slice = max(MIN_SLICE, (((total + p.nwg - 1) / p.nwg) + 63) & ~63);
   // ---- pass 3: workgroups overlapping each group; list slots of split groups
   int c_list = 0;
   for (int base = 0; base < n_groups; base += nt) {
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(PLAN_NT) void dsa_plan_kernel(IdxParams p) {
       const int nq = in_lds ? s_nq[g] : gr[G_NQ];
       // workgroups holding the group's keys (the extra weight that stands
       // for the segment cost follows them and holds no keys)
-      const int wreal = max(16, (range + 15) & ~15);
+      const int wreal = max(64, (range + 63) & ~63);
       const int w0 = off / slice, w1 = (off + wreal - 1) / slice;
       const int wlast = (off + wreal + SEG_COST - 1) / slice;
       gr[G_W0] = w0;
@@ -782,8 +784,7 @@ struct Frag {
 template <int DT, int D>
 struct BFrag {
   Frag<DT, D> f;
-  float sc;  // FP8: key scale; MXFP8: E8M0 group byte (as bits)
-  int ok;
+  float sc;  // MXFP8: E8M0 group byte (as bits); unused otherwise
 };
 
 template <int DT, int D, int HT, int MQ, int NW>
@@ -799,6 +800,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
   // loads in flight per wave (8 groups measured 0.3-0.45 % slower on the decode
   // batches once keys are scored four groups at a time)
   constexpr int PF = 4;
+  static_assert(PF == 4, "quad key scales are loaded one quad ahead, with the ring");
   static_assert(GPW % PF == 0, "prefetch ring must divide the round");
   static_assert(GPW % 4 == 0, "groups are scored four at a time");
   constexpr int NQD = GPW / 4;  // quads of groups per wave per round
@@ -840,7 +842,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
     const int nl = uniform(gr[G_NL]);
     const int list_base = uniform(gr[G_LIST]);
     const int w0 = uniform(gr[G_W0]);
-    const int wreal = max(16, (range + 15) & ~15);
+    const int wreal = max(64, (range + 63) & ~63);
     if ((int)blockIdx.x >= w0 + nl) continue;  // only the group's cost weight lies in this slice
     // this workgroup's keys of the group: [seg_lo, seg_hi), multiples of 16
     const int seg_lo = max(a0, off) - off;
@@ -949,13 +951,12 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
           const uint32_t off_b = n16 * ROWB + (DT == 0 ? 2 * (32 * j + 8 * g4) : (64 * j + 16 * g4));
           bf.f.d[j] = *reinterpret_cast<const v4i*>(rowp + off_b);
         }
-        // FP8: the key's fp32 scale; MXFP8: the E8M0 byte of group g4 of key r
-        // (carried in sc's bits); the scales follow the page's 64 rows
+        // MXFP8: the E8M0 byte of group g4 of key r (carried in sc's bits), for
+        // the MFMA; the scales follow the page's 64 rows (FP8 key scales are
+        // read once per quad instead)
         const uint8_t* scp = p.k_pool + ((uint64_t)(ok ? pu : 0u) << 8) + PAGE * ROWB;
-        if (DT == 1) bf.sc = *reinterpret_cast<const float*>(scp + 4 * ((p0 & 63) + n16));
-        else if (DT == 2) bf.sc = __int_as_float((int)scp[(D / 32) * ((p0 & 63) + n16) + g4]);
+        if (DT == 2) bf.sc = __int_as_float((int)scp[(D / 32) * ((p0 & 63) + n16) + g4]);
         else bf.sc = 1.f;
-        bf.ok = ok;
       };
 
       // One 16-key group: each lane sums w * ReLU(q . k) over its 4 rows of
@@ -1013,21 +1014,24 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
         __builtin_amdgcn_sched_group_barrier(0x002, 1000, 0);
       };
 
-      // Four consecutive groups (64 keys from p0): after the cross-lane sum,
-      // lane l holds the score of key p0 + l, whose group is lane group g4.
-      // sc4 / ok4: the key scale and page validity each group's load gave.
-      auto finish_quad = [&](const float (&part)[MQ][4], const float (&sc4)[4], const int (&ok4)[4], int p0,
-                             uint32_t (&kk)[MQ]) {
-        float ksc = 1.f;
-        if (DT == 1) ksc = g4 == 0 ? sc4[0] : g4 == 1 ? sc4[1] : g4 == 2 ? sc4[2] : sc4[3];
-        const int okl = g4 == 0 ? ok4[0] : g4 == 1 ? ok4[1] : g4 == 2 ? ok4[2] : ok4[3];
+      // Four consecutive groups: 64 keys from p0, one page (segments start on
+      // pages).  After the cross-lane sum, lane l holds the score of key
+      // p0 + l; ksc is that key's scale (one load per lane and quad), ok the
+      // page's validity.
+      auto finish_quad = [&](const float (&part)[MQ][4], float ksc, bool ok, int p0, uint32_t (&kk)[MQ]) {
         const int pos = p0 + lane;
 #pragma unroll
         for (int q = 0; q < MQ; ++q) {
           float sc = sum_lane_groups4(part[q][0], part[q][1], part[q][2], part[q][3]);
           if (DT == 1) sc *= ksc;
-          kk[q] = (okl && pos < lim[q]) ? order_key(sc) : 0u;
+          kk[q] = (ok && pos < lim[q]) ? order_key(sc) : 0u;
         }
+      };
+      // the quad's key scales (FP8): lane l reads the scale of row l of the page
+      auto load_qscale = [&](uint32_t pu) {
+        if (DT != 1) return 1.f;
+        const uint8_t* scp = p.k_pool + ((uint64_t)(pu != ~0u ? pu : 0u) << 8) + PAGE * ROWB;
+        return *reinterpret_cast<const float*>(scp + 4 * lane);
       };
 
       // Loads are unconditional so the prefetch queue depth stays static: slots
@@ -1045,6 +1049,15 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
       uint32_t pu_next = page_of(load_p0(PF));  // page of the next load
+      // key scales and page validity of the current and the next quad (the
+      // ring runs one quad ahead), indexed by quad parity
+      float qsc[2];
+      bool qok[2];
+      {
+        const uint32_t pu0 = page_of(load_p0(0));
+        qsc[0] = load_qscale(pu0);
+        qok[0] = pu0 != ~0u;
+      }
       for (int r = 0; r < nrounds; ++r) {
         // score this wave's GPW groups, four at a time (one key per lane);
         // keys past the sub-chunk end fail the visibility test
@@ -1052,23 +1065,23 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
 #pragma unroll
         for (int qd = 0; qd < NQD; ++qd) {
           float part[MQ][4];
-          float sc4[4];
-          int ok4[4];
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int s = 4 * qd + u;
             const uint32_t pu = pu_next;
             pu_next = page_of(load_p0(r * GPW + s + PF + 1));
             partial_group(buf[s % PF], part, u);
-            sc4[u] = buf[s % PF].sc;
-            ok4[u] = buf[s % PF].ok;
             load_b(buf[s % PF], load_p0(r * GPW + s + PF), pu);
+            if (u == 0) {  // the next quad's first group: its page is the quad's
+              qsc[(qd + 1) & 1] = load_qscale(pu);
+              qok[(qd + 1) & 1] = pu != ~0u;
+            }
             // one group at a time: hoisting the next group's MFMAs would need
             // a second accumulator set
             __builtin_amdgcn_sched_barrier(0);
           }
           uint32_t kq[MQ];
-          finish_quad(part, sc4, ok4, group_p0(r * GPW + 4 * qd), kq);
+          finish_quad(part, qsc[qd & 1], qok[qd & 1], group_p0(r * GPW + 4 * qd), kq);
 #pragma unroll
           for (int q = 0; q < MQ; ++q) kk[q][qd] = kq[q];
         }
