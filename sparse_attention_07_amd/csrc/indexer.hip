@@ -1048,7 +1048,12 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
         load_b(buf[s], load_p0(s), page_of(load_p0(s)));
         __builtin_amdgcn_sched_barrier(0);
       }
-      uint32_t pu_next = page_of(load_p0(PF));  // page of the next load
+      // Page entries of the loads.  One query per group: read one group ahead
+      // (pu_next).  Two: once per quad (a quad is one page, and clamped groups
+      // past the end stay on the last group's page), at the quad's start; the
+      // per-quad read measured 1.8 % faster for two queries and 0.3 % slower
+      // for one.
+      uint32_t pu_next = MQ == 1 ? page_of(load_p0(PF)) : 0u, pu_q = 0u;
       // key scales and page validity of the current and the next quad (the
       // ring runs one quad ahead), indexed by quad parity
       float qsc[2];
@@ -1068,8 +1073,14 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int s = 4 * qd + u;
-            const uint32_t pu = pu_next;
-            pu_next = page_of(load_p0(r * GPW + s + PF + 1));
+            uint32_t pu;
+            if constexpr (MQ == 2) {
+              if (u == 0) pu_q = page_of(load_p0(r * GPW + s + PF));
+              pu = pu_q;
+            } else {
+              pu = pu_next;
+              pu_next = page_of(load_p0(r * GPW + s + PF + 1));
+            }
             partial_group(buf[s % PF], part, u);
             load_b(buf[s % PF], load_p0(r * GPW + s + PF), pu);
             if (u == 0) {  // the next quad's first group: its page is the quad's
