@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 5
+#define DSA_ABI_VERSION 6
 #define DSA_PAGE_TOKENS 64
 #define DSA_LATENT_DIM 576
 #define DSA_VALUE_DIM 512
@@ -124,6 +124,10 @@ typedef enum dsa_idx_dtype {
  *                0..n_t-1), or NULL (then n_t = seq_lens[q_seq[t]])
  *   max_q_per_seq host-side upper bound on adjacent queries of one sequence
  *                (1 for plain decode); it only selects the kernel variant.
+ * Size limits (DSA_ERR_SHAPE otherwise): 64 * max_blocks <= 2^30 - 1,
+ * 64 * num_blocks <= 2^31 - 1, and T * (max_blocks + 72) <= 2^30 (the indexer
+ * lays all query groups' key ranges end to end in one page-counted space;
+ * e.g. a 4096-query chunk may see up to about 2^24 pages = 2^30 tokens).
  */
 typedef struct dsa_indexer_args {
   int32_t T, B, H_idx, D_idx;
@@ -196,6 +200,23 @@ size_t dsa_workspace_bytes(const dsa_indexer_args* idx, const dsa_mla_args* mla,
  */
 dsa_status dsa_indexer_topk(const dsa_indexer_args* a, int K, int32_t* indices_out,
                             void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Debugging aid for step 1 (the pages' alignment checklist, "Day 0 Inference
+ * Adaptation and Performance Optimization for Hybrid Attention LLMs", section
+ * "Engineering Execution", item 2: align the sparse index selection results
+ * module by module).  Runs the indexer kernel of dsa_indexer_topk with the
+ * same arguments, but instead of selecting it writes each fused score, exactly
+ * as the selection compares it, as fp32:
+ *   scores[t * ld + p] = S[t,p] for every position p < n_t whose page is
+ *   present; every other entry is left untouched (callers pre-fill it).
+ *   scores  float device, [T][ld]; ld >= 64 * max_blocks (else DSA_ERR_SHAPE)
+ *   ws      workspace of dsa_workspace_bytes(a, NULL, 1) bytes
+ * Argument errors are those of dsa_indexer_topk.  Meant for tests and
+ * debugging: it writes T * n_t floats, unlike the fused call.
+ */
+dsa_status dsa_indexer_scores(const dsa_indexer_args* a, float* scores, int64_t ld, void* ws, size_t ws_bytes,
+                              void* stream);
 
 /*
  * Step 3.  indices [T][K] int32 device pool slots; entries < 0 (or outside the

@@ -20,6 +20,7 @@ namespace {
 constexpr int MLA_TARGET_WGS = 256;
 constexpr int MLA_MIN_ROWS = 256;
 constexpr int MLA_MAX_SPLITS = 8;
+constexpr int64_t KEYSPACE_MAX_PAGES = (int64_t)1 << 30;
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -54,6 +55,10 @@ dsa_status check_indexer(const dsa_indexer_args* a, int K) {
   if (!a->q_seq && a->T != a->B) return DSA_ERR_SHAPE;
   if ((int64_t)a->max_blocks * DSA_PAGE_TOKENS > (int64_t)INT32_MAX / 2) return DSA_ERR_SHAPE;
   if ((int64_t)a->num_blocks * DSA_PAGE_TOKENS > (int64_t)INT32_MAX) return DSA_ERR_SHAPE;
+  // The stream-K key space (every query group's visible range padded to whole
+  // pages, plus a fixed per-segment weight) is counted in pages in 32 bits;
+  // bound its largest possible total: at most T groups of max_blocks pages.
+  if ((int64_t)a->T * ((int64_t)a->max_blocks + SEG_COST_PG) > KEYSPACE_MAX_PAGES) return DSA_ERR_SHAPE;
   if (!aligned(a->q_idx, 16) || !aligned(a->k_idx_pool, 16) || !aligned(a->w, 4) || !aligned(a->block_table, 4) ||
       !aligned(a->seq_lens, 4) || !aligned(a->q_idx_scale, 4) || !aligned(a->q_seq, 4) ||
       !aligned(a->q_visible, 4))
@@ -225,7 +230,7 @@ MlaParams make_mla_params(const dsa_mla_args* m, const int32_t* indices, int K, 
   p.rows_per_split = pl.RPS;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.out = (uint16_t*)out;
-  p.part_o = pl.S > 1 ? (_Float16*)(ws + pl.off_o) : nullptr;
+  p.part_o = pl.S > 1 ? (uint16_t*)(ws + pl.off_o) : nullptr;
   p.part_ml = pl.S > 1 ? (float*)(ws + pl.off_ml) : nullptr;
   p.residual = (const uint16_t*)m->residual;
   p.gamma = (const uint16_t*)m->norm_weight;
@@ -284,6 +289,21 @@ dsa_status dsa_indexer_topk(const dsa_indexer_args* a, int K, int32_t* indices_o
   const IdxPlan pl = plan_indexer(a, K, 0, device_cus());
   if (!ws || ws_bytes < pl.end || !aligned(ws, 256)) return DSA_ERR_WORKSPACE;
   IdxParams p = make_idx_params(a, K, indices_out, (unsigned char*)ws, pl);
+  return hip_status(launch_indexer(p, a->idx_dtype, a->D_idx, pl.nwg, (hipStream_t)stream));
+}
+
+dsa_status dsa_indexer_scores(const dsa_indexer_args* a, float* scores, int64_t ld, void* ws, size_t ws_bytes,
+                              void* stream) {
+  dsa_status st = check_indexer(a, 1);
+  if (st != DSA_OK) return st;
+  if (!scores) return DSA_ERR_NULL;
+  if (!aligned(scores, 4)) return DSA_ERR_ALIGN;
+  if (ld < (int64_t)a->max_blocks * DSA_PAGE_TOKENS) return DSA_ERR_SHAPE;
+  const IdxPlan pl = plan_indexer(a, 1, 0, device_cus());
+  if (!ws || ws_bytes < pl.end || !aligned(ws, 256)) return DSA_ERR_WORKSPACE;
+  IdxParams p = make_idx_params(a, 1, nullptr, (unsigned char*)ws, pl);
+  p.scores = scores;
+  p.scores_ld = ld;
   return hip_status(launch_indexer(p, a->idx_dtype, a->D_idx, pl.nwg, (hipStream_t)stream));
 }
 

@@ -28,6 +28,12 @@ constexpr int MERGE_FAN = 8;          // candidate lists one merge workgroup tak
 // (Measured: 2560, 3584, 4608 and 5632 gave 208, 205, 202 and 203 us for the
 // 128K-token decode batch; 4608 is also the best or near it for the others.)
 constexpr int SEG_COST = 4608;
+// The concatenated key space of the stream-K partition is counted in 64-key
+// pages (every group's range is padded to whole pages), so offsets of calls
+// with billions of keys in total still fit 32 bits; the host bounds the total.
+constexpr int MIN_SLICE_PG = MIN_SLICE / PAGE;
+constexpr int SEG_COST_PG = SEG_COST / PAGE;
+static_assert(MIN_SLICE % PAGE == 0 && SEG_COST % PAGE == 0, "page-unit key space");
 constexpr int SUB = 65536;            // keys whose page ids the indexer stages in LDS at once
 
 // Order-preserving map fp32 -> uint32 (a < b  <=>  key(a) < key(b)); -0 maps
@@ -36,6 +42,11 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   uint32_t u = __float_as_uint(x);
   if (u == 0x80000000u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inverse of order_key for keys of finite values (key 0 is no value).
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
 // Sum over the four lanes l, l^16, l^32, l^48 (the four k-groups of a 16x16

@@ -7,8 +7,9 @@ namespace dsa {
 
 // Per-group record written by the planning kernel (int32 fields): first query,
 // query count, sequence, visible key range, offset of the group in the
-// concatenated (16-key padded) key space, number of indexer workgroups whose
-// slice overlaps the group, first candidate-list slot, first workgroup.
+// concatenated (page-padded) key space in 64-key pages, number of indexer
+// workgroups whose slice overlaps the group, first candidate-list slot, first
+// workgroup.
 enum GroupField { G_T0 = 0, G_NQ, G_SEQ, G_RANGE, G_OFF, G_NL, G_LIST, G_W0, G_FIELDS };
 
 struct IdxParams {
@@ -27,8 +28,10 @@ struct IdxParams {
   int32_t nwg;  // indexer workgroups (each scans one equal slice of the key space)
   int32_t MQ;   // max queries per group
   int32_t* indices;  // [T][K] output
+  float* scores;      // score dump instead of selection (null: select): [T][scores_ld] fp32
+  int64_t scores_ld;
   // workspace
-  int32_t* hdr;        // [0] groups, [1] padded keys in total, [2] keys per workgroup slice
+  int32_t* hdr;        // [0] groups, [1] pages in the padded key space, [2] pages per workgroup slice
   int32_t* groups;     // [T][G_FIELDS]
   int32_t* qgroup;     // [T] group of each query
   int32_t* wg_first;   // [nwg] first group of each indexer workgroup
@@ -57,7 +60,7 @@ struct MlaParams {
   int32_t rows_per_split;   // multiple of 32
   float scale_log2;         // softmax scale * log2(e)
   uint16_t* out;            // [T][H][512] bf16
-  _Float16* part_o;         // [T][S][H][512] fp16, normalised O/l of each split (S > 1)
+  uint16_t* part_o;         // [T][S][H][512] bf16, normalised O/l of each split (S > 1)
   float* part_ml;           // [T][S][H][2]   fp32 (S > 1)
   // residual + RMSNorm epilogue (residual == nullptr: none)
   const uint16_t* residual; // [T][H][512] bf16

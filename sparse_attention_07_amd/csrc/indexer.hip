@@ -48,6 +48,14 @@
 
 namespace dsa {
 
+// The file is compiled once per part (DSA_IDX_PART): part 0 holds the
+// planning kernel and the launch dispatcher, parts 1-4 the indexer kernels of
+// one index format each, so the instantiations build in parallel.
+#ifndef DSA_IDX_PART
+#define DSA_IDX_PART 0
+#endif
+
+#if DSA_IDX_PART == 0
 // =============================================================================
 // Planning kernel: one workgroup (1024 threads; 256 for at most 256 queries,
 // one wave for at most 64).
@@ -129,9 +137,9 @@ __global__ __launch_bounds__(PLAN_NT) void dsa_plan_kernel(IdxParams p) {
   }
   const int n_groups = carry_gid;
   // ---- pass 2: per-group key ranges and their offsets in the concatenated
-  // key space (each group padded to whole 64-key pages, at least one, so
-  // every slice and segment starts on a page: four consecutive 16-key groups
-  // of the indexer are one page)
+  // key space, counted in 64-key pages (each group padded to whole pages, at
+  // least one, so every slice and segment starts on a page: four consecutive
+  // 16-key groups of the indexer are one page)
   int c_off = 0;
   for (int base = 0; base < n_groups; base += nt) {
     const int g = base + tid;
@@ -152,7 +160,7 @@ __global__ __launch_bounds__(PLAN_NT) void dsa_plan_kernel(IdxParams p) {
         s_nq[g] = t1 - t0;
         s_rng[g] = range;
       }
-      wgt = max(64, (range + 63) & ~63) + SEG_COST;
+      wgt = max(1, (range + PAGE - 1) / PAGE) + SEG_COST_PG;
     }
     const int so = block_scan_incl(wgt, s_w, false);
     if (g < n_groups) {
@@ -164,8 +172,8 @@ __global__ __launch_bounds__(PLAN_NT) void dsa_plan_kernel(IdxParams p) {
     c_off = s_carry[0];
     __syncthreads();
   }
-  const int total = c_off;
-  const int slice = max(MIN_SLICE, (((total + p.nwg - 1) / p.nwg) + 63) & ~63);
+  const int total = c_off;  // pages (the host keeps it below 2^30)
+  const int slice = max(MIN_SLICE_PG, (total + p.nwg - 1) / p.nwg);
   // ---- pass 3: workgroups overlapping each group; list slots of split groups
   int c_list = 0;
   for (int base = 0; base < n_groups; base += nt) {
@@ -178,9 +186,9 @@ __global__ __launch_bounds__(PLAN_NT) void dsa_plan_kernel(IdxParams p) {
       const int nq = in_lds ? s_nq[g] : gr[G_NQ];
       // workgroups holding the group's keys (the extra weight that stands
       // for the segment cost follows them and holds no keys)
-      const int wreal = max(64, (range + 63) & ~63);
+      const int wreal = max(1, (range + PAGE - 1) / PAGE);
       const int w0 = off / slice, w1 = (off + wreal - 1) / slice;
-      const int wlast = (off + wreal + SEG_COST - 1) / slice;
+      const int wlast = (off + wreal + SEG_COST_PG - 1) / slice;
       gr[G_W0] = w0;
       gr[G_NL] = w1 - w0 + 1;
       // workgroups whose slice starts inside this group begin with it
@@ -204,6 +212,8 @@ __global__ __launch_bounds__(PLAN_NT) void dsa_plan_kernel(IdxParams p) {
     p.hdr[2] = slice;
   }
 }
+
+#endif  // DSA_IDX_PART == 0
 
 // =============================================================================
 // Block-wide selection primitives (shared by the indexer and the merge).
@@ -817,6 +827,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
   const int g4 = lane >> 4;
   const int n16 = lane & 15;
 
+  // this workgroup's slice [a0, a1) of the key space, in pages
   const int n_groups = p.hdr[0];
   const int total = p.hdr[1];
   const int slice = p.hdr[2];
@@ -842,11 +853,11 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
     const int nl = uniform(gr[G_NL]);
     const int list_base = uniform(gr[G_LIST]);
     const int w0 = uniform(gr[G_W0]);
-    const int wreal = max(64, (range + 63) & ~63);
+    const int wreal = max(1, (range + PAGE - 1) / PAGE);  // pages
     if ((int)blockIdx.x >= w0 + nl) continue;  // only the group's cost weight lies in this slice
-    // this workgroup's keys of the group: [seg_lo, seg_hi), multiples of 16
-    const int seg_lo = max(a0, off) - off;
-    const int seg_hi = min(min(a1, off + wreal) - off, range);
+    // this workgroup's keys of the group: [seg_lo, seg_hi), seg_lo a multiple of 64
+    const int seg_lo = (max(a0, off) - off) * PAGE;
+    const int seg_hi = min((min(a1, off + wreal) - off) * PAGE, range);
     const int32_t* bt = p.block_table + (int64_t)max(seq, 0) * p.max_blocks;
 
     int vis[MQ];
@@ -1096,6 +1107,18 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
 #pragma unroll
           for (int q = 0; q < MQ; ++q) kk[q][qd] = kq[q];
         }
+        if (p.scores) {
+          // score dump (a debugging call): the fused scores exactly as the
+          // selection sees them (their order keys mapped back to fp32) for the
+          // visible positions of present pages; nothing is selected
+#pragma unroll
+          for (int q = 0; q < MQ; ++q)
+#pragma unroll
+            for (int qd = 0; qd < NQD; ++qd)
+              if (q < nq && kk[q][qd] != 0u)
+                p.scores[(int64_t)(t0 + q) * p.scores_ld + group_p0(r * GPW + 4 * qd) + lane] = key_float(kk[q][qd]);
+          continue;
+        }
         // append the keys above each query's bound: a wave's groups are
         // consecutive positions and waves follow each other, so a wave's
         // offset is the count of the waves before it (one barrier per round).
@@ -1156,6 +1179,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
         rpar ^= 1;
       }
     }
+
+    if (p.scores) continue;  // score dump: no selection, no lists
 
     // ---- final selection and output
     // split group: this workgroup's list is list il of each query; run jr
@@ -1258,6 +1283,36 @@ static hipError_t launch_indexer_mq(const IdxParams& p, int grid, hipStream_t st
   return p.MQ == 1 ? launch_indexer_t<DT, D, HT, 1, 8>(p, grid, st) : launch_indexer_t<DT, D, HT, 2, 8>(p, grid, st);
 }
 
+template <int DT, int D>
+static hipError_t launch_indexer_heads(const IdxParams& p, int grid, hipStream_t st) {
+  return p.H_idx <= 16 ? launch_indexer_mq<DT, D, 1>(p, grid, st) : launch_indexer_mq<DT, D, 4>(p, grid, st);
+}
+
+// one launcher per index format, each defined in its own part
+hipError_t launch_indexer_fp8(const IdxParams& p, int grid, hipStream_t st);
+hipError_t launch_indexer_mxfp8(const IdxParams& p, int grid, hipStream_t st);
+hipError_t launch_indexer_bf16_128(const IdxParams& p, int grid, hipStream_t st);
+hipError_t launch_indexer_bf16_64(const IdxParams& p, int grid, hipStream_t st);
+
+#if DSA_IDX_PART == 1
+hipError_t launch_indexer_fp8(const IdxParams& p, int grid, hipStream_t st) {
+  return launch_indexer_heads<1, 128>(p, grid, st);
+}
+#elif DSA_IDX_PART == 2
+hipError_t launch_indexer_mxfp8(const IdxParams& p, int grid, hipStream_t st) {
+  return launch_indexer_heads<2, 128>(p, grid, st);
+}
+#elif DSA_IDX_PART == 3
+hipError_t launch_indexer_bf16_128(const IdxParams& p, int grid, hipStream_t st) {
+  return launch_indexer_heads<0, 128>(p, grid, st);
+}
+#elif DSA_IDX_PART == 4
+hipError_t launch_indexer_bf16_64(const IdxParams& p, int grid, hipStream_t st) {
+  return launch_indexer_heads<0, 64>(p, grid, st);
+}
+#endif
+
+#if DSA_IDX_PART == 0
 hipError_t launch_indexer(const IdxParams& p, int idx_dtype, int D, int grid, hipStream_t st) {
   const size_t plan_smem = p.T <= PLAN_LDS_T ? PLAN_LDS_BYTES : 0;
   hipError_t e = hipFuncSetAttribute((const void*)dsa_plan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1267,16 +1322,10 @@ hipError_t launch_indexer(const IdxParams& p, int idx_dtype, int D, int grid, hi
   hipLaunchKernelGGL(dsa_plan_kernel, dim3(1), dim3(plan_nt), plan_smem, st, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const bool small_heads = p.H_idx <= 16;
-  if (idx_dtype == 1)
-    e = small_heads ? launch_indexer_mq<1, 128, 1>(p, grid, st) : launch_indexer_mq<1, 128, 4>(p, grid, st);
-  else if (idx_dtype == 2)
-    e = small_heads ? launch_indexer_mq<2, 128, 1>(p, grid, st) : launch_indexer_mq<2, 128, 4>(p, grid, st);
-  else if (D == 64)
-    e = small_heads ? launch_indexer_mq<0, 64, 1>(p, grid, st) : launch_indexer_mq<0, 64, 4>(p, grid, st);
-  else
-    e = small_heads ? launch_indexer_mq<0, 128, 1>(p, grid, st) : launch_indexer_mq<0, 128, 4>(p, grid, st);
-  return e;
+  if (idx_dtype == 1) return launch_indexer_fp8(p, grid, st);
+  if (idx_dtype == 2) return launch_indexer_mxfp8(p, grid, st);
+  return D == 64 ? launch_indexer_bf16_64(p, grid, st) : launch_indexer_bf16_128(p, grid, st);
 }
+#endif
 
 }  // namespace dsa

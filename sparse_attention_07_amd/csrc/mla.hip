@@ -25,8 +25,9 @@
 //    read (ds_read_b64_tr_b16) and P^T with plain 16-byte reads;
 //  * the O rescale is skipped for a wave when no head's running max moved;
 //  * with several splits, each split stores its normalised partial output
-//    O/l as fp16 (|O/l| is bounded by the largest value entry) plus (m, l) in
-//    fp32, and a small kernel merges them with log-sum-exp weights;
+//    O/l as bf16 (the latent cache's own range: |O/l| is bounded by the
+//    largest value entry) plus (m, l) in fp32, and a small kernel merges them
+//    with log-sum-exp weights;
 //  * optional residual + RMSNorm epilogue over the token's H x 512 values: with
 //    one split the workgroup holds the whole token and finishes it; with
 //    several, the combine adds the residual and stores per-head sums of
@@ -424,12 +425,12 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
       }
     } else {
       const int64_t rowi = ((int64_t)t * p.S + s) * H + h;
-      _Float16* prow = p.part_o + rowi * VDIM;
+      uint16_t* prow = p.part_o + rowi * VDIM;
 #pragma unroll
       for (int vt = 0; vt < VT; ++vt) {
-        _Float16 h4[4];
+        __bf16 h4[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) h4[i] = (_Float16)(o[vt][nt][i] * inv);
+        for (int i = 0; i < 4; ++i) h4[i] = (__bf16)(o[vt][nt][i] * inv);
         *reinterpret_cast<uint2*>(prow + (wave * VT + vt) * 16 + 4 * g4) = __builtin_bit_cast(uint2, h4);
       }
     }
@@ -472,10 +473,12 @@ __global__ __launch_bounds__(256) void dsa_mla_combine_kernel(MlaParams p) {
     for (int s = 0; s < SM; ++s) {
       const float wgt = (s < p.S && ms[s] != -INFINITY) ? exp2f(ms[s] - M) * ls[s] : 0.f;
       L += wgt;
-      _Float16 h8[8];
-      __builtin_memcpy(h8, &raw[s], 16);
+      const uint32_t rw[4] = {raw[s].x, raw[s].y, raw[s].z, raw[s].w};  // 8 bf16
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += wgt * (float)h8[i];
+      for (int j = 0; j < 4; ++j) {
+        acc[2 * j] += wgt * __uint_as_float(rw[j] << 16);
+        acc[2 * j + 1] += wgt * __uint_as_float(rw[j] & 0xffff0000u);
+      }
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;

@@ -27,8 +27,8 @@ VDIM = 512
 MAX_K = 2048
 
 # Every symbol the header declares (checked by the tests against include/dsa.h).
-EXPORTS = ("dsa_workspace_bytes", "dsa_indexer_topk", "dsa_sparse_mla_attn", "dsa_layer", "dsa_quantize_index_q",
-           "dsa_status_str", "dsa_abi_version")
+EXPORTS = ("dsa_workspace_bytes", "dsa_indexer_topk", "dsa_indexer_scores", "dsa_sparse_mla_attn", "dsa_layer",
+           "dsa_quantize_index_q", "dsa_status_str", "dsa_abi_version")
 
 
 class DSAError(RuntimeError):
@@ -69,6 +69,9 @@ def _load() -> ctypes.CDLL:
     lib.dsa_indexer_topk.restype = ctypes.c_int
     lib.dsa_indexer_topk.argtypes = [P(IndexerArgs), ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_size_t, ctypes.c_void_p]
+    lib.dsa_indexer_scores.restype = ctypes.c_int
+    lib.dsa_indexer_scores.argtypes = [P(IndexerArgs), ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                       ctypes.c_size_t, ctypes.c_void_p]
     lib.dsa_sparse_mla_attn.restype = ctypes.c_int
     lib.dsa_sparse_mla_attn.argtypes = [P(MlaArgs), ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
@@ -162,6 +165,20 @@ def indexer_topk(q_idx, w, k_idx_pool, block_table, seq_lens, K: int, *, q_idx_s
         workspace = _workspace(need, q_idx.device)
     _check(LIB.dsa_indexer_topk(ctypes.byref(a), K, _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
     return out
+
+
+def indexer_scores(q_idx, w, k_idx_pool, block_table, seq_lens, *, q_idx_scale=None, q_seq=None, q_visible=None,
+                   max_q_per_seq: int = 1, fill: float = float("nan")) -> torch.Tensor:
+    """Debugging aid: the indexer's fused fp32 scores [T, 64 * max_blocks] as
+    the Top-K compares them (positions not visible or on absent pages keep
+    `fill`)."""
+    a = indexer_args(q_idx, w, k_idx_pool, block_table, seq_lens, q_idx_scale=q_idx_scale, q_seq=q_seq,
+                     q_visible=q_visible, max_q_per_seq=max_q_per_seq)
+    ld = PAGE * a.max_blocks
+    scores = torch.full((a.T, ld), fill, dtype=torch.float32, device=q_idx.device)
+    workspace = _workspace(workspace_bytes(a, None, 1), q_idx.device)
+    _check(LIB.dsa_indexer_scores(ctypes.byref(a), _ptr(scores), ld, _ptr(workspace), workspace.numel(), _stream()))
+    return scores
 
 
 def sparse_mla_attn(q, kv_pool, indices, scale: float, *, out: Optional[torch.Tensor] = None,

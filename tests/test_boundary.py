@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     m = re.search(r"#define DSA_ABI_VERSION (\d+)", open(HEADER).read())
-    assert int(m.group(1)) == 5
+    assert int(m.group(1)) == 6
     assert dsa.LIB.dsa_abi_version() == int(m.group(1))
     assert dsa.status_str(0) == "ok"
     for s in range(1, 9):
@@ -135,6 +135,19 @@ def test_indexer_null_struct_output_and_workspace():
     assert call_idx(good_idx(), ws=_base + 16, ws_bytes=need) == E_WS  # workspace must be 256-B aligned
 
 
+def test_indexer_scores_argument_errors():
+    def call(a, scores=_base, ld=640, ws=None, ws_bytes=0):
+        return dsa.LIB.dsa_indexer_scores(None if a is None else ctypes.byref(a), scores, ld, ws, ws_bytes, None)
+    assert call(None) == E_NULL
+    assert call(good_idx(), scores=None) == E_NULL
+    assert call(good_idx(), scores=_base + 2) == E_ALIGN
+    assert call(good_idx(), ld=639) == E_SHAPE  # a row must hold 64 * max_blocks positions
+    assert call(good_idx(H_idx=0)) == E_SHAPE
+    assert call(good_idx()) == E_WS
+    need = dsa.workspace_bytes(good_idx(), None, 1)
+    assert call(good_idx(), ws=_base, ws_bytes=need - 1) == E_WS
+
+
 def call_mla(m, K=2048, idx=_base, out=_base, ws=None, ws_bytes=0):
     return dsa.LIB.dsa_sparse_mla_attn(None if m is None else ctypes.byref(m), idx, K, 0.04, out, ws, ws_bytes, None)
 
@@ -197,6 +210,27 @@ def test_workspace_bytes_invalid_and_scaling():
     # a single short-context decode needs no candidate lists (one chunk per query)
     small = dsa.workspace_bytes(good_idx(T=1, B=1, max_blocks=64), None, 256)
     assert 0 < small < 4096
+
+
+def test_keyspace_bound():
+    # The indexer lays every query group's key range end to end in one space
+    # counted in 64-key pages (32-bit): T * (max_blocks + 72) <= 2^30.
+    # The last 4096-query chunk of a 1,048,576-token prefill (16,384 pages),
+    # with paired queries and with one query per group at 600K tokens, fits.
+    one_m = good_idx(T=4096, B=1, max_blocks=16384, num_blocks=16384, max_q_per_seq=4096, q_seq=_base,
+                     q_visible=_base)
+    assert dsa.workspace_bytes(one_m, None, 2048) > 0
+    six = good_idx(T=4096, B=1, max_blocks=9375, num_blocks=9375, max_q_per_seq=1, q_seq=_base, q_visible=_base)
+    assert dsa.workspace_bytes(six, None, 2048) > 0
+    # at the bound, and one page past it
+    edge = (1 << 30) // 4096 - 72
+    assert dsa.workspace_bytes(good_idx(T=4096, B=1, max_blocks=edge, num_blocks=edge, q_seq=_base), None, 2048) > 0
+    past = good_idx(T=4096, B=1, max_blocks=edge + 1, num_blocks=edge + 1, q_seq=_base)
+    assert dsa.workspace_bytes(past, None, 2048) == 0
+    assert call_idx(past) == E_SHAPE
+    # 65,536 queries of a 1M-token sequence: about 1.08e9 pages, rejected
+    big = good_idx(T=65536, B=1, max_blocks=16384, num_blocks=16384, q_seq=_base)
+    assert call_idx(big) == E_SHAPE
 
 
 def call_quant(q=_base, rows=64, D=128, dt=None, codes=_base, scales=_base):

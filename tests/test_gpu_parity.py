@@ -121,29 +121,54 @@ def test_deterministic_bitwise():
     assert torch.equal(o1.view(torch.int16), layer.out.view(torch.int16))
 
 
-# --------------------------------------------------------------------------- full-size workloads, sampled
+# --------------------------------------------------------------------------- full-size workloads
+# Every query of the decode workloads is checked; each prefill chunk is
+# checked on 64 queries: both edges of the chunk, the queries around the
+# Top-K size (t + 1 <= 2048 keeps every visible position), and a seeded sample.
 def test_full_decode_b32_32k():
-    run_case(synth.PRESETS["decode_b32_32k"], queries=[0, 17, 31])
+    run_case(synth.PRESETS["decode_b32_32k"])
 
 
 def test_full_decode_b64_128k_fp8():
-    run_case(synth.PRESETS["decode_b64_128k_fp8"], queries=[0, 40, 63])
+    run_case(synth.PRESETS["decode_b64_128k_fp8"])
 
 
 def test_full_decode_b64_128k_mxfp8():
-    run_case(synth.PRESETS["decode_b64_128k_mxfp8"], queries=[0, 21, 63])
+    run_case(synth.PRESETS["decode_b64_128k_mxfp8"])
 
 
 def test_full_decode_b64_128k_fp8_latent():
-    run_case(synth.PRESETS["decode_b64_128k_fp8kv"], queries=[0, 17, 40, 63])
+    run_case(synth.PRESETS["decode_b64_128k_fp8kv"])
 
 
-def test_full_prefill_16k_last_chunk():
-    run_case(synth.PRESETS["prefill_16k"], prefill_chunk=3, queries=[0, 1, 2047, 4095])
+def prefill_queries(chunk, n=4096, k=2048, count=64, seed=0):
+    """Local query indices of one chunk: its edges, the keep-everything
+    boundary (global t + 1 = K) when it falls inside, and a seeded sample."""
+    fixed = {0, 1, 2, 63, 64, n // 2 - 1, n // 2, n - 3, n - 2, n - 1}
+    b = k - 1 - chunk * n  # local index of global t = K - 1
+    for d in (-2, -1, 0, 1, 2):
+        if 0 <= b + d < n:
+            fixed.add(b + d)
+    rng = np.random.default_rng(seed + chunk)
+    rest = [int(x) for x in rng.permutation(n) if int(x) not in fixed]
+    return sorted(fixed) + sorted(rest[: count - len(fixed)])
+
+
+@pytest.mark.parametrize("chunk", [0, 1, 2, 3])
+def test_full_prefill_16k_chunk(chunk):
+    run_case(synth.PRESETS["prefill_16k"], prefill_chunk=chunk, queries=prefill_queries(chunk))
 
 
 def test_full_mixed_1m():
-    run_case(synth.PRESETS["mixed_1m"], queries=[0, 3, 7, 10])
+    run_case(synth.PRESETS["mixed_1m"])
+
+
+def test_million_token_prefill_last_chunk():
+    # the last 4096-query chunk of a 1,048,576-token prefill: its query groups
+    # lay about 3.4e10 keys end to end in the indexer's key space (counted in
+    # 64-key pages); 16 MLA heads keep the inputs small
+    sp = spec("prefill_1m_last_chunk", lens=[1 << 20], queries_per_seq=[4096], H=16, seed=53)
+    run_case(sp, queries=[0, 1, 2047, 2048, 4094, 4095])
 
 
 def test_all_scores_tied_picks_lowest_positions():
@@ -198,11 +223,12 @@ def test_absent_pages_are_skipped():
         assert ok, msg
 
 
-def test_mla_score_outrun_takes_exact_max_path():
-    # one head's logit on a row in the second tile of a split exceeds that
-    # split's first-tile maximum by far more than the exponent slack of the
-    # 128-head kernel, which then recomputes the split with exact maxima
-    sp = spec("outrun", lens=[4096], H=128, K=2048, seed=31)
+def test_mla_large_online_softmax_rescale():
+    # one head's logit on row 300 (the second 32-row tile of its split)
+    # exceeds every earlier logit of that head by far (about 3 x |q|^2 x scale):
+    # the running maximum jumps and the accumulated output and sum are rescaled
+    # by a factor that underflows to zero, after which that row dominates
+    sp = spec("rescale", lens=[4096], H=128, K=2048, seed=31)
     case = synth.build_case(sp, device=DEV)
     bt = case.block_table[0].cpu()
     pos = torch.arange(sp.K)
@@ -218,5 +244,36 @@ def test_mla_score_outrun_takes_exact_max_path():
     got = out[0].float().cpu().numpy()
     assert abs(ref[h0] - rows[j, :512]).max() < 1e-3  # the planted row dominates head h0
     ok, msg = check_outputs(got, ref)
-    say("  outrun case:", msg)
+    say("  large rescale case:", msg)
+    assert ok, msg
+
+
+@pytest.mark.parametrize("e", [17, -16])
+def test_split_partials_keep_the_latent_range(e):
+    # Latent rows scaled by 2^e and MLA queries by 2^-e (both exact in bf16):
+    # logits are unchanged, outputs scale by 2^e.  With several splits per
+    # query the partial outputs are stored in between; at 2^17 they exceed
+    # what fp16 holds and at 2^-16 they would be fp16 subnormals.  Compared
+    # after dividing both sides by 2^e (exact), with the usual tolerances.
+    sp = spec(f"latent_range_{e}", lens=[20000, 9000, 3], seed=59)
+    case = synth.build_case(sp, device=DEV)
+    case.kv_pool.mul_(2.0 ** e)
+    case.q.mul_(2.0 ** -e)
+    layer = dsa.layer_from_case(case)
+    layer()
+    torch.cuda.synchronize()
+    idx = layer.indices.cpu().numpy()
+    got, ref = [], []
+    for t in range(case.T):
+        d, phys = query_case(case, t)
+        S, _ = O.query_scores(d, 0)
+        ok, msg = check_index_row(idx[t], S, phys, sp.K)
+        assert ok, msg
+        pos_of = {int(s): p for p, s in enumerate(phys)}
+        gpos = np.array([pos_of[int(s)] for s in idx[t] if s >= 0], dtype=np.int64)
+        ref.append(O.mla_query(d, 0, gpos) * 2.0 ** -e)
+        got.append(layer.out[t].float().cpu().numpy() * 2.0 ** -e)
+    assert np.isfinite(np.stack(got)).all()
+    ok, msg = check_outputs(np.stack(got), np.stack(ref))
+    say(f"  latent rows x 2^{e}: {msg}")
     assert ok, msg
