@@ -74,6 +74,7 @@ extern "C" {
 #define DSA_VALUE_DIM 512
 #define DSA_MAX_K 2048
 #define DSA_MAX_INDEX_HEADS 64
+#define DSA_STATIC_SCRATCH_BYTES ((size_t)64 << 20) /* dsa_layer_static's scratch per GPU */
 
 typedef enum dsa_status {
   DSA_OK = 0,
@@ -84,7 +85,9 @@ typedef enum dsa_status {
   DSA_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned                    */
   DSA_ERR_WORKSPACE = 6,   /* ws_bytes < dsa_workspace_bytes(...) or ws NULL      */
   DSA_ERR_UNSUPPORTED = 7, /* a valid but unimplemented combination               */
-  DSA_ERR_HIP = 8          /* a HIP launch failed                                 */
+  DSA_ERR_HIP = 8,         /* a HIP launch failed                                 */
+  DSA_ERR_TOO_LARGE = 9    /* dsa_layer_static: the call needs more scratch than  */
+                           /* DSA_STATIC_SCRATCH_BYTES                            */
 } dsa_status;
 
 typedef enum dsa_kv_dtype {
@@ -234,6 +237,24 @@ dsa_status dsa_sparse_mla_attn(const dsa_mla_args* a, const int32_t* indices, in
  */
 dsa_status dsa_layer(const dsa_indexer_args* idx, const dsa_mla_args* mla, int K, float scale,
                      int32_t* indices_out, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dsa_layer for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same launch sequence and results, with the scratch taken from an array the
+ * library holds on each GPU (DSA_STATIC_SCRATCH_BYTES, allocated with the code
+ * object when the library is first used on that GPU and held until the
+ * process ends) instead of a caller workspace.  The call allocates nothing.
+ *   Returns DSA_ERR_TOO_LARGE, before anything is launched, when the call
+ *   needs more than that (dsa_workspace_bytes(idx, mla, K) bytes: the five
+ *   workloads of the pages' model need at most about 49 MiB on a 256-CU GPU).
+ *   Every call on one GPU shares that GPU's array, which keeps the last call's
+ *   contents (the call clears what must start at zero itself): calls that
+ *   overlap on one GPU (different streams, or threads without ordering) race
+ *   and must be serialised by the caller.  The device is the current one.
+ */
+dsa_status dsa_layer_static(const dsa_indexer_args* idx, const dsa_mla_args* mla, int K, float scale,
+                            int32_t* indices_out, void* out, void* stream);
 
 /*
  * Index-query quantization, the step before step 1 ("Inference Acceleration

@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/dsa.h"
 #include "dsa_device.h"
@@ -242,6 +243,60 @@ MlaParams make_mla_params(const dsa_mla_args* m, const int32_t* indices, int K, 
 
 dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
 
+// Argument checks and layout of one layer call: the workspace bytes it needs.
+dsa_status layer_check(const dsa_indexer_args* idx, const dsa_mla_args* mla, int K, const int32_t* indices_out,
+                       const void* out, size_t* need) {
+  dsa_status st = check_indexer(idx, K);
+  if (st != DSA_OK) return st;
+  st = check_mla(mla, K);
+  if (st != DSA_OK) return st;
+  if (idx->T != mla->T || idx->num_blocks != mla->num_blocks) return DSA_ERR_SHAPE;
+  if (!out) return DSA_ERR_NULL;
+  if (!aligned(out, 8) || !aligned(indices_out, 4)) return DSA_ERR_ALIGN;
+  const IdxPlan ip = plan_indexer(idx, K, 0, device_cus());
+  const size_t idx_end = align_up(align_up(ip.end, 256) + (size_t)idx->T * K * 4, 256);
+  *need = plan_mla(mla, K, idx_end).end;
+  return DSA_OK;
+}
+
+// The layer's launch sequence on a checked call, with a workspace of at least
+// layer_check's bytes.
+dsa_status layer_launch(const dsa_indexer_args* idx, const dsa_mla_args* mla, int K, float scale,
+                        int32_t* indices_out, void* out, unsigned char* w, hipStream_t s) {
+  const IdxPlan ip = plan_indexer(idx, K, 0, device_cus());
+  const size_t off_idx = align_up(ip.end, 256);
+  const size_t idx_end = align_up(off_idx + (size_t)idx->T * K * 4, 256);
+  const MlaPlan mp = plan_mla(mla, K, idx_end);
+  int32_t* indices = indices_out ? indices_out : (int32_t*)(w + off_idx);
+  IdxParams p = make_idx_params(idx, K, indices, w, ip);
+  dsa_status st = hip_status(launch_indexer(p, idx->idx_dtype, idx->D_idx, ip.nwg, s));
+  if (st != DSA_OK) return st;
+  MlaParams q = make_mla_params(mla, indices, K, scale, out, w, mp);
+  return hip_status(launch_mla(q, s));
+}
+
+// ---- The library's own scratch for dsa_layer_static: one array per GPU,
+// allocated with the code object (a host-side name only; kernels get its
+// device address, looked up once per device).
+__device__ __align__(256) unsigned char scratch[DSA_STATIC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+dsa_status scratch_of_current_device(unsigned char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return DSA_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return DSA_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = (unsigned char*)g_scratch_ptr[dev];
+  return DSA_OK;
+}
+
 }  // namespace
 }  // namespace dsa
 
@@ -262,6 +317,7 @@ const char* dsa_status_str(dsa_status s) {
     case DSA_ERR_WORKSPACE: return "workspace missing or too small";
     case DSA_ERR_UNSUPPORTED: return "unsupported combination";
     case DSA_ERR_HIP: return "HIP launch failed";
+    case DSA_ERR_TOO_LARGE: return "the call needs more scratch than the library's static array holds";
   }
   return "unknown status";
 }
@@ -321,26 +377,23 @@ dsa_status dsa_sparse_mla_attn(const dsa_mla_args* m, const int32_t* indices, in
 
 dsa_status dsa_layer(const dsa_indexer_args* idx, const dsa_mla_args* mla, int K, float scale, int32_t* indices_out,
                      void* out, void* ws, size_t ws_bytes, void* stream) {
-  dsa_status st = check_indexer(idx, K);
+  size_t need = 0;
+  dsa_status st = layer_check(idx, mla, K, indices_out, out, &need);
   if (st != DSA_OK) return st;
-  st = check_mla(mla, K);
+  if (!ws || ws_bytes < need || !aligned(ws, 256)) return DSA_ERR_WORKSPACE;
+  return layer_launch(idx, mla, K, scale, indices_out, out, (unsigned char*)ws, (hipStream_t)stream);
+}
+
+dsa_status dsa_layer_static(const dsa_indexer_args* idx, const dsa_mla_args* mla, int K, float scale,
+                            int32_t* indices_out, void* out, void* stream) {
+  size_t need = 0;
+  dsa_status st = layer_check(idx, mla, K, indices_out, out, &need);
   if (st != DSA_OK) return st;
-  if (idx->T != mla->T || idx->num_blocks != mla->num_blocks) return DSA_ERR_SHAPE;
-  if (!out) return DSA_ERR_NULL;
-  if (!aligned(out, 8) || !aligned(indices_out, 4)) return DSA_ERR_ALIGN;
-  const IdxPlan ip = plan_indexer(idx, K, 0, device_cus());
-  const size_t off_idx = align_up(ip.end, 256);
-  const size_t idx_end = align_up(off_idx + (size_t)idx->T * K * 4, 256);
-  const MlaPlan mp = plan_mla(mla, K, idx_end);
-  if (!ws || ws_bytes < mp.end || !aligned(ws, 256)) return DSA_ERR_WORKSPACE;
-  unsigned char* w = (unsigned char*)ws;
-  int32_t* indices = indices_out ? indices_out : (int32_t*)(w + off_idx);
-  hipStream_t s = (hipStream_t)stream;
-  IdxParams p = make_idx_params(idx, K, indices, w, ip);
-  st = hip_status(launch_indexer(p, idx->idx_dtype, idx->D_idx, ip.nwg, s));
+  if (need > DSA_STATIC_SCRATCH_BYTES) return DSA_ERR_TOO_LARGE;
+  unsigned char* w = nullptr;
+  st = scratch_of_current_device(&w);
   if (st != DSA_OK) return st;
-  MlaParams q = make_mla_params(mla, indices, K, scale, out, w, mp);
-  return hip_status(launch_mla(q, s));
+  return layer_launch(idx, mla, K, scale, indices_out, out, w, (hipStream_t)stream);
 }
 
 dsa_status dsa_quantize_index_q(const void* q, int64_t rows, int32_t D, int32_t idx_dtype, void* codes,

@@ -28,7 +28,8 @@ MAX_K = 2048
 
 # Every symbol the header declares (checked by the tests against include/dsa.h).
 EXPORTS = ("dsa_workspace_bytes", "dsa_indexer_topk", "dsa_indexer_scores", "dsa_sparse_mla_attn", "dsa_layer",
-           "dsa_quantize_index_q", "dsa_status_str", "dsa_abi_version")
+           "dsa_layer_static", "dsa_quantize_index_q", "dsa_status_str", "dsa_abi_version")
+STATIC_SCRATCH_BYTES = 64 << 20
 
 
 class DSAError(RuntimeError):
@@ -78,6 +79,9 @@ def _load() -> ctypes.CDLL:
     lib.dsa_layer.restype = ctypes.c_int
     lib.dsa_layer.argtypes = [P(IndexerArgs), P(MlaArgs), ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.dsa_layer_static.restype = ctypes.c_int
+    lib.dsa_layer_static.argtypes = [P(IndexerArgs), P(MlaArgs), ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_void_p]
     lib.dsa_quantize_index_q.restype = ctypes.c_int
     lib.dsa_quantize_index_q.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
@@ -245,6 +249,16 @@ class Layer:
                              _ptr(self.indices), _ptr(self.out), _ptr(self.workspace), self.workspace.numel(),
                              _stream()))
         return self.out
+
+    def call_static(self, out: Optional[torch.Tensor] = None, indices: Optional[torch.Tensor] = None):
+        """The same layer through dsa_layer_static (the library's own scratch,
+        no workspace); results go to `out` / `indices` (default: this layer's
+        own buffers)."""
+        out = self.out if out is None else out
+        indices = self.indices if indices is None else indices
+        _check(LIB.dsa_layer_static(ctypes.byref(self.idx), ctypes.byref(self.mla), self.K, self.scale,
+                                    _ptr(indices), _ptr(out), _stream()))
+        return out
 
 
 def layer_from_case(case, want_indices: bool = True, **epilogue) -> Layer:

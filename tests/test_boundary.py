@@ -14,7 +14,7 @@ HEADER = os.path.join(ROOT, "include", "dsa.h")
 
 dsa = pytest.importorskip("sparse_attention_07_amd.dsa", reason="libdsa.so not built")
 
-OK, E_NULL, E_DTYPE, E_SHAPE, E_K, E_ALIGN, E_WS, E_UNSUP, E_HIP = range(9)
+OK, E_NULL, E_DTYPE, E_SHAPE, E_K, E_ALIGN, E_WS, E_UNSUP, E_HIP, E_TOO_LARGE = range(10)
 
 
 def header_functions():
@@ -38,7 +38,7 @@ def test_abi_version_and_status_strings():
     assert int(m.group(1)) == 6
     assert dsa.LIB.dsa_abi_version() == int(m.group(1))
     assert dsa.status_str(0) == "ok"
-    for s in range(1, 9):
+    for s in range(1, 10):
         assert dsa.status_str(s) and dsa.status_str(s) != "unknown status"
     assert dsa.status_str(99) == "unknown status"
 
