@@ -1,17 +1,22 @@
 """Benchmark of the DSA layer (lightning indexer + Top-K + sparse MLA) on one GPU.
 
-A step is one dsa_layer call (planning, fused indexer/Top-K/merge, sparse MLA
-split + combine) over one batch of synthetic input resident in HBM.  The
-default workload is 64 decoding sequences with cached lengths uniform in
-[65536, 131072], an FP8 e4m3 index-K cache (per-token fp32 scale, 64 heads x
-128), Top-2048, and a bf16 576-wide latent cache read by 128-head sparse MLA.
+A step is one pass of the layer over one batch of synthetic input resident in
+HBM: one dsa_layer call (planning, fused indexer/Top-K/merge, sparse MLA split
++ combine) for decode, one per chunk for chunked prefill.  The default workload
+is 64 decoding sequences with cached lengths uniform in [65536, 131072], an FP8
+e4m3 index-K cache (per-token fp32 scale, 64 heads x 128), Top-2048, and a bf16
+576-wide latent cache read by 128-head sparse MLA.
 
-Prints one JSON line.  `value` is decode query tokens per second of the whole
-layer; `roofline` reports the indexer kernel's algorithmic HBM bytes per launch
-over its event-timed launch duration (or, where the indexer's algorithmic flops
-per byte exceed the MFMA ridge, as in chunked prefill, its FP8 / bf16 MFMA
-flops against the dense MFMA peak); `cpu_baseline` is the CPU oracle timed on a
-bounded sample of the same workload.
+Prints one JSON line.  `value` is query tokens per second of the whole layer;
+`roofline` reports the dominant kernel, the indexer (planning + indexer
+kernels), timed with HIP events on its launch stream inside a layer-shaped
+sequence (indexer, then attention, per step): its algorithmic HBM bytes per
+launch over that duration (or, where the indexer's algorithmic flops per byte
+exceed the MFMA ridge, as in chunked prefill, its FP8 / bf16 MFMA flops
+against the dense MFMA peak), plus `layer_frac_hbm`, the whole step's
+algorithmic bytes (indexer + Top-K + sparse MLA) over its time against 8 TB/s;
+`cpu_baseline` is the CPU oracle timed on a bounded sample of the same
+workload.
 """
 from __future__ import annotations
 
@@ -45,6 +50,8 @@ def parse():
     ap.add_argument("--quant-dtype", choices=("fp8", "mxfp8"), default=None,
                     help="--op quantize: the code format (default: the workload's index dtype)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy-bandwidth", action="store_true",
+                    help="skip the plain device copy whose rate is reported as context")
     ap.add_argument("--cpu-sample", type=int, default=48, help="queries the CPU oracle is timed on")
     ap.add_argument("--copies", type=int, default=2,
                     help="input copies the steps rotate through, so no step re-reads the previous step's "
@@ -186,7 +193,8 @@ def cpu_baseline(case, n_sample):
         keys += int(case.q_visible[t])
     return dict(value=len(qs) / secs, unit="tokens/s", cores=len(os.sched_getaffinity(0)), kind="oracle",
                 sample=f"{len(qs)} of {case.T} queries of {s.name} ({keys} visible keys in total), "
-                       f"numpy fp64, {secs:.1f} s")
+                       f"numpy fp64, {secs:.1f} s",
+                omp_num_threads=os.environ.get("OMP_NUM_THREADS"))
 
 
 def quant_cpu_baseline(src, kind, label):
@@ -261,6 +269,25 @@ def bench_quantize(args, spec, case):
     print(json.dumps(line), flush=True)
 
 
+def copy_bandwidth(dev, nbytes=2 << 30, reps=5):
+    """Context, not a denominator: a plain device-to-device copy's rate (GB/s,
+    read + write bytes over time)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(gbps, 1)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -271,16 +298,22 @@ def main():
     from sparse_attention_07_amd import dsa, synth
 
     spec = synth.PRESETS[args.workload]
-    prefill_chunk = None
-    if spec.prefill is not None:
-        prefill_chunk = spec.prefill[0] // spec.prefill[1] - 1  # the heaviest (last) chunk
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    case = synth.build_case(spec, device=dev, prefill_chunk=prefill_chunk)
+    # A step is one pass of the whole layer over one batch: one dsa_layer call
+    # for decode; for chunked prefill, one call per chunk (all chunks of the
+    # sequence, in order).
+    if spec.prefill is not None:
+        n_chunks = -(-spec.prefill[0] // spec.prefill[1])
+        step_cases = [[synth.build_case(spec, device=dev, prefill_chunk=c) for c in range(n_chunks)]]
+    else:
+        step_cases = [[synth.build_case(spec, device=dev)]]
+    case = step_cases[0][-1]
     ep_kw = {}
     if args.epilogue:
         g = torch.Generator(device=dev).manual_seed(spec.seed + 7)
-        res = torch.randn(case.T, spec.H, 512, generator=g, device=dev).to(torch.bfloat16)
+        T_max = max(c.T for c in step_cases[0])
+        res = torch.randn(T_max, spec.H, 512, generator=g, device=dev).to(torch.bfloat16)
         gam = (1.0 + 0.1 * torch.randn(spec.H * 512, generator=g, device=dev)).to(torch.bfloat16)
         ep_kw = dict(residual=res, norm_weight=gam, residual_out=torch.empty_like(res), eps=1e-6)
     if args.op == "quantize":
@@ -288,52 +321,103 @@ def main():
         if args.copy_calibration:
             copy_calibration(dev)
         return
-    layers = [dsa.layer_from_case(case, **ep_kw)]
-    extra_cases = []
-    for _ in range(max(0, args.copies - 1)):
-        c2 = synth.Case(**{f: getattr(case, f) for f in case.__dataclass_fields__})
-        c2.k_idx_pool = case.k_idx_pool.clone()
-        c2.kv_pool = case.kv_pool.clone()
-        extra_cases.append(c2)
-        layers.append(dsa.layer_from_case(c2, **ep_kw))
+    if spec.prefill is None:
+        # copies of the caches the steps rotate through
+        for _ in range(max(0, args.copies - 1)):
+            c2 = synth.Case(**{f: getattr(case, f) for f in case.__dataclass_fields__})
+            c2.k_idx_pool = case.k_idx_pool.clone()
+            c2.kv_pool = case.kv_pool.clone()
+            step_cases.append([c2])
+
+    def ep_for(c):
+        if not ep_kw:
+            return {}
+        return dict(residual=ep_kw["residual"][: c.T], norm_weight=ep_kw["norm_weight"],
+                    residual_out=ep_kw["residual_out"][: c.T], eps=ep_kw["eps"])
+
+    layers = [[dsa.layer_from_case(c, **ep_for(c)) for c in cs] for cs in step_cases]
     torch.cuda.synchronize()
 
+    def step(i):
+        for lay in layers[i % len(layers)]:
+            lay()
+
     for i in range(args.warmup):
-        layers[i % len(layers)]()
+        step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        layers[i % len(layers)]()
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = wall / args.steps * 1e3
-    value = case.T * args.steps / wall
+    tokens_per_step = sum(c.T for c in step_cases[0])
+    value = tokens_per_step * args.steps / wall
 
-    # the dominant kernel: indexer + Top-K alone, timed with events on the launch stream
+    # The same kernels in the same order, one C call per step part, with HIP
+    # events on the launch stream around each: the indexer (planning +
+    # indexer/Top-K/merge kernels) and the sparse MLA (split + combine) as they
+    # run inside the layer step.
     stream = torch.cuda.current_stream()
-    idx_out = torch.empty(case.T, spec.K, dtype=torch.int32, device=dev)
-    ws = torch.empty(dsa.workspace_bytes(layers[0].idx, None, spec.K), dtype=torch.uint8, device=dev)
-    cases = [case] + extra_cases
+    splits = []
+    for cs, lays in zip(step_cases, layers):
+        parts = []
+        for c, lay in zip(cs, lays):
+            idx_out = torch.empty(c.T, spec.K, dtype=torch.int32, device=dev)
+            ws = torch.empty(max(256, dsa.workspace_bytes(lay.idx, None, spec.K)), dtype=torch.uint8, device=dev)
+            out = torch.empty_like(lay.out)
+            parts.append((c, idx_out, ws, out))
+        splits.append(parts)
 
-    def run_indexer(c):
-        return dsa.indexer_topk(c.q_idx, c.w, c.k_idx_pool, c.block_table, c.seq_lens, spec.K,
-                                q_idx_scale=c.q_idx_scale, q_seq=c.q_seq, q_visible=c.q_visible,
-                                max_q_per_seq=c.max_q_per_seq, out=idx_out, workspace=ws)
+    def run_split(i, ev=None):
+        for j, (c, idx_out, ws, out) in enumerate(splits[i % len(splits)]):
+            if ev is not None:
+                ev[j][0].record(stream)
+            dsa.indexer_topk(c.q_idx, c.w, c.k_idx_pool, c.block_table, c.seq_lens, spec.K,
+                             q_idx_scale=c.q_idx_scale, q_seq=c.q_seq, q_visible=c.q_visible,
+                             max_q_per_seq=c.max_q_per_seq, out=idx_out, workspace=ws)
+            if ev is not None:
+                ev[j][1].record(stream)
+            dsa.sparse_mla_attn(c.q, c.kv_pool, idx_out, spec.scale, out=out, **ep_for(c))
+            if ev is not None:
+                ev[j][2].record(stream)
 
     for i in range(args.warmup):
-        run_indexer(cases[i % len(cases)])
-    n_idx = max(20, args.steps)
+        run_split(i)
+    n_split = max(20, args.steps)
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in step_cases[0]] for _ in range(n_split)]
+    for i in range(n_split):
+        run_split(i, evs[i])
+    torch.cuda.synchronize()
+    idx_ms = sum(e[0].elapsed_time(e[1]) for ev in evs for e in ev) / n_split
+    mla_ms = sum(e[1].elapsed_time(e[2]) for ev in evs for e in ev) / n_split
+
+    # the indexer alone, back to back (context: no attention kernels between)
+    def run_indexer(i):
+        for c, idx_out, ws, _ in splits[i % len(splits)]:
+            dsa.indexer_topk(c.q_idx, c.w, c.k_idx_pool, c.block_table, c.seq_lens, spec.K,
+                             q_idx_scale=c.q_idx_scale, q_seq=c.q_seq, q_visible=c.q_visible,
+                             max_q_per_seq=c.max_q_per_seq, out=idx_out, workspace=ws)
+
+    for i in range(args.warmup):
+        run_indexer(i)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for i in range(n_idx):
-        run_indexer(cases[i % len(cases)])
+    for i in range(n_split):
+        run_indexer(i)
     e1.record(stream)
     torch.cuda.synchronize()
-    idx_ms = e0.elapsed_time(e1) / n_idx
+    idx_b2b_ms = e0.elapsed_time(e1) / n_split
 
-    idx_bytes, layer_bytes = algorithmic_bytes(case, layers[0].indices, args.epilogue)
-    idx_flops, mla_flops = algorithmic_flops(case, layers[0].indices)
+    idx_bytes = layer_bytes = idx_flops = mla_flops = 0
+    for c, lay in zip(step_cases[0], layers[0]):
+        ib, lb = algorithmic_bytes(c, lay.indices, args.epilogue)
+        fi, fm = algorithmic_flops(c, lay.indices)
+        idx_bytes, layer_bytes, idx_flops, mla_flops = idx_bytes + ib, layer_bytes + lb, idx_flops + fi, mla_flops + fm
     achieved = idx_bytes / (idx_ms * 1e-3) / 1e9
+    layer_frac = layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS
+    kernel = ("dsa_indexer_topk: planning + dsa_indexer_kernel (Top-K and list merge), timed inside the layer "
+              "step" + (f" (all {len(step_cases[0])} chunk calls of a step)" if len(step_cases[0]) > 1 else ""))
     # the indexer's bound: MFMA when its flops per algorithmic byte exceed the
     # chip's ridge (prefill: each key serves thousands of queries), else HBM
     mfma_peak = MFMA_PEAK_TFLOPS[spec.idx_dtype]
@@ -342,17 +426,31 @@ def main():
         roofline = {
             "bound": "mfma", "achieved": round(tflops, 1), "peak": mfma_peak, "unit": "TFLOP/s",
             "frac": round(tflops / mfma_peak, 4), "traffic": stored_traffic(f"indexer_traffic_{spec.name}"),
-            "kernel": "dsa_indexer_topk: planning + dsa_indexer_kernel (Top-K and list merge)",
-            "launch_ms": round(idx_ms, 5), "algorithmic_flops": idx_flops, "algorithmic_bytes": idx_bytes,
-            "dtype": "fp8" if spec.idx_dtype != "bf16" else "bf16",
+            "kernel": kernel, "launch_ms": round(idx_ms, 5), "algorithmic_flops": idx_flops,
+            "algorithmic_bytes": idx_bytes, "dtype": "fp8" if spec.idx_dtype != "bf16" else "bf16",
+            "back_to_back_ms": round(idx_b2b_ms, 5),
         }
     else:
         roofline = {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": stored_traffic(f"indexer_traffic_{spec.name}"),
-            "kernel": "dsa_indexer_topk: planning + dsa_indexer_kernel (Top-K and list merge)",
-            "launch_ms": round(idx_ms, 5), "algorithmic_bytes": idx_bytes,
+            "kernel": kernel, "launch_ms": round(idx_ms, 5), "algorithmic_bytes": idx_bytes,
+            "back_to_back_ms": round(idx_b2b_ms, 5),
+            "back_to_back_frac": round(idx_bytes / (idx_b2b_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         }
+    # the metric's own scope (indexer + Top-K + sparse MLA): the whole step
+    roofline["layer_frac_hbm"] = round(layer_frac, 4)
+    cfg = {
+        "workload": spec.name, "queries": tokens_per_step, "sequences": case.B,
+        "context_tokens_total": int(case.seq_lens.sum()), "index": f"{spec.idx_dtype} {spec.H_idx}x{spec.D_idx}",
+        "top_k": spec.K, "mla_heads": spec.H, "latent_dim": 576, "latent_cache": spec.kv_dtype,
+        "page_tokens": 64, "calls_per_step": len(step_cases[0]),
+        "input_copies_rotated": len(step_cases), "parallelism": "single GPU",
+        "epilogue": "residual + RMSNorm" if args.epilogue else None,
+    }
+    if spec.prefill is None and case.B > 1:
+        lens = case.seq_lens.tolist()
+        cfg["longest_over_mean_context"] = round(max(lens) / (sum(lens) / len(lens)), 3)
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -367,23 +465,19 @@ def main():
         "dtype": ("bf16" if spec.idx_dtype == "bf16" else f"{spec.idx_dtype}+bf16")
                  + ("+fp8kv" if spec.kv_dtype == "fp8" else ""),
         "data": "synthetic",
-        "config": {
-            "workload": spec.name, "queries": case.T, "sequences": case.B,
-            "context_tokens_total": int(case.seq_lens.sum()), "index": f"{spec.idx_dtype} {spec.H_idx}x{spec.D_idx}",
-            "top_k": spec.K, "mla_heads": spec.H, "latent_dim": 576, "latent_cache": spec.kv_dtype,
-            "page_tokens": 64,
-            "input_copies_rotated": len(layers), "parallelism": "single GPU",
-            "epilogue": "residual + RMSNorm" if args.epilogue else None,
-        },
+        "config": cfg,
         "roofline": roofline,
         "layer": {
             "algorithmic_bytes": layer_bytes, "GBps": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
-            "frac_hbm": round(layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "frac_hbm": round(layer_frac, 4),
             "algorithmic_flops": idx_flops + mla_flops,
             "TFLOPs": round((idx_flops + mla_flops) / (ms * 1e-3) / 1e12, 1),
             "mla_flops_bf16": mla_flops,
+            "indexer_ms_in_step": round(idx_ms, 5), "mla_ms_in_step": round(mla_ms, 5),
         },
     }
+    if not args.no_copy_bandwidth:
+        line["context"] = {"device_copy_GBps": copy_bandwidth(dev)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_sample)
     print(json.dumps(line), flush=True)

@@ -97,10 +97,13 @@ int device_cus() {
 // same value must be used for sizing and for the call.
 IdxPlan plan_indexer(const dsa_indexer_args* a, int K, size_t base, int nwg) {
   IdxPlan pl;
-  // Adjacent queries of one sequence are scored together (sharing each key
-  // load) only when there are many of them (chunked prefill): for a handful
-  // of speculative queries the doubled per-key work costs more than the
-  // extra key reads save.
+  // Adjacent queries of one sequence are scored in pairs, sharing each key
+  // load, only when there are many of them (chunked prefill).  For a handful of
+  // speculative queries on long sequences the pairs cost more than the extra
+  // key reads save: measured on the mixed batch (four queries on a 1M-token
+  // sequence), pairs streamed the keys in 91 us instead of 128 us but the
+  // call took 251 us instead of 182, the selection and the list merges of two
+  // queries per workgroup outweighing the saved reads.
   pl.MQ = a->max_q_per_seq >= 8 ? 2 : 1;
   pl.nwg = nwg;
   const int64_t maxlen = (int64_t)a->max_blocks * DSA_PAGE_TOKENS;
