@@ -23,7 +23,10 @@
 //    PV: wave w owns value dims [512w/NW, 512(w+1)/NW) for all heads and
 //    accumulates O^T += C^T P^T, reading C^T with the gfx950 LDS transpose
 //    read (ds_read_b64_tr_b16) and P^T with plain 16-byte reads;
-//  * the O rescale is skipped for a wave when no head's running max moved;
+//  * each head's reference maximum moves only when a tile's maximum exceeds
+//    it by more than 2^8 (probabilities stay below 256, exact in the end:
+//    O and l carry the same offset), so the O rescale is skipped for a wave
+//    unless some head's maximum jumped;
 //  * with several splits, each split stores its normalised partial output
 //    O/l as bf16 (the latent cache's own range: |O/l| is bounded by the
 //    largest value entry) plus (m, l) in fp32, and a small kernel merges them
@@ -45,6 +48,7 @@
 namespace dsa {
 
 constexpr int TILE_ROWS = 32;
+constexpr float RESCALE_SLACK = 8.f;  // log2 of the largest unnormalised probability
 constexpr int MLA_SMAX = 8;  // most splits of a query's index list (K / 256 for K <= 2048)
 constexpr int ROW_UNITS = LATENT * 2 / 16;                         // 72 sixteen-byte units per row
 constexpr int ROW_STRIDE = ROW_UNITS + 2;                          // padded row stride (units)
@@ -170,27 +174,37 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
   lds_barrier();
 
   constexpr int NSTAGE = MlaSmem<NW, KV8>::NSTAGE;
+  // Load k of this wave covers ring units (first + k) * 64 + lane: the lane's
+  // row (bf16: slot of the permuted layout) and 16-byte column advance by 64
+  // units (less than one row) per load, so they are stepped, not divided.
+  const int first_u = (wave * LMIN + min(wave, LEXTRA)) * 64 + lane;
+  const int r_first = first_u / RUNITS;
+  const int c_first = first_u - r_first * RUNITS;
   auto issue_tile = [&](int ti) {
     unsigned char* st = sm.stage[ti % NSTAGE];
     const int nl = LMIN + (wave < LEXTRA ? 1 : 0);
     const int first = wave * LMIN + min(wave, LEXTRA);
+    int r = r_first, c = c_first;
     for (int k = 0; k < nl; ++k) {
-      const int u0 = (first + k) * 64;
-      const int u = u0 + lane;
-      int r = u / RUNITS;  // FP8: row; bf16: slot
-      int c = u - r * RUNITS;
-      if (r >= TILE_ROWS || c >= (KV8 ? KV8_ROW_UNITS : ROW_UNITS)) {  // padding slot: a harmless valid unit
-        r = min(r, TILE_ROWS - 1);
-        c = 0;
+      int rr = r, cc = c;
+      if (rr >= TILE_ROWS || cc >= (KV8 ? KV8_ROW_UNITS : ROW_UNITS)) {  // padding: a harmless valid unit
+        rr = min(rr, TILE_ROWS - 1);
+        cc = 0;
       }
-      if constexpr (!KV8) r = slot_row(r);
-      int slot = sidx[ti * TILE_ROWS + r];
+      if constexpr (!KV8) rr = slot_row(rr);
+      int slot = sidx[ti * TILE_ROWS + rr];
       slot = slot < 0 ? 0 : slot;
-      const uint16_t* g = KV8 ? p.kv + (int64_t)slot * (KV8_ROW_UNITS * 8) + 8 * c
-                              : p.kv + (int64_t)slot * LATENT + 8 * c;
+      const uint16_t* g = KV8 ? p.kv + (int64_t)slot * (KV8_ROW_UNITS * 8) + 8 * cc
+                              : p.kv + (int64_t)slot * LATENT + 8 * cc;
       const uint32_t lds_addr =
-          (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)(st + 16 * u0);
+          (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)(st + 16 * (first + k) * 64);
       dma16_to_lds(g, uniform(lds_addr));
+      r += 64 / RUNITS;
+      c += 64 % RUNITS;
+      if (c >= RUNITS) {
+        c -= RUNITS;
+        ++r;
+      }
     }
   };
 
@@ -240,13 +254,20 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
           tmax = fmaxf(tmax, x[4 * mt + i]);
         }
       tmax = max_lane_groups(tmax);
-      const float m_new = fmaxf(m_run, tmax);
-      const float a_ = (m_new > m_run) ? exp2f(m_run - m_new) : 1.f;
+      // The reference maximum moves only when the tile's exceeds it by more
+      // than RESCALE_SLACK (log2 units): the probabilities then stay below
+      // 2^RESCALE_SLACK, O and l carry the same offset (the normalisation and
+      // the split combine remove it), and the O rescale (128 products per
+      // lane) runs only on such jumps instead of on almost every tile.
+      const float m_new = (tmax > m_run + RESCALE_SLACK) ? tmax : m_run;
+      // the hardware exp2 (v_exp_f32): results below 2^-126 only feed sums
+      // dominated by terms >= 1
+      const float a_ = (m_new > m_run) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
       float lsum = 0.f;
       __bf16 pv[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float pr = (m_new == -INFINITY) ? 0.f : exp2f(x[j] - m_new);
+        const float pr = (m_new == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x[j] - m_new);
         lsum += pr;
         pv[j] = (__bf16)pr;
       }
@@ -257,22 +278,27 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
     }
   };
   // O^T += C^T P^T of tile ti for this wave's value slice, from the bf16 tile at st
+  // the rescale of O by the factors of tile ti (only when some head's
+  // reference maximum moved)
+  auto pv_rescale = [&](int ti) {
+    float al[NW];
+    bool any = false;
+#pragma unroll
+    for (int nt = 0; nt < NW; ++nt) {
+      al[nt] = sm.alpha[ti & 1][16 * nt + n16];
+      any |= (al[nt] != 1.f);
+    }
+    if (__builtin_amdgcn_ballot_w64(any)) {
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt)
+#pragma unroll
+        for (int nt = 0; nt < NW; ++nt) o[vt][nt] *= al[nt];
+    }
+  };
   auto pv = [&](int ti, const unsigned char* st) {
     // ---- PV: O^T[v, head] = alpha * O^T + C^T[v, row] P^T[row, head], v in this wave's slice
+    // (the rescale by alpha is pv_rescale, run before)
     {
-      float al[NW];
-      bool any = false;
-#pragma unroll
-      for (int nt = 0; nt < NW; ++nt) {
-        al[nt] = sm.alpha[ti & 1][16 * nt + n16];
-        any |= (al[nt] != 1.f);
-      }
-      if (__builtin_amdgcn_ballot_w64(any)) {
-#pragma unroll
-        for (int vt = 0; vt < VT; ++vt)
-#pragma unroll
-          for (int nt = 0; nt < NW; ++nt) o[vt][nt] *= al[nt];
-      }
       // transpose-read base: row 8*g4 + n16/4, column 16*(wave*VT) + 4*(n16%4); v tile vt adds 32 bytes
       const unsigned char* tb = st + stage_off(8 * g4 + (n16 >> 2), wave * VT * 16 + 4 * (n16 & 3));
       v8bf av[VT];
@@ -302,7 +328,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
       __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // tile ti, the only one in flight, has landed
       lds_barrier_keep_dma();  // and every wave has left iteration ti-1 (stage (ti+1)%3 is free)
       if (ti + 1 < ntiles) issue_tile(ti + 1);
-      if (ti > 0) pv(ti - 1, sm.stage[(ti - 1) % STAGES]);
+      if (ti > 0) {
+        pv_rescale(ti - 1);
+        pv(ti - 1, sm.stage[(ti - 1) % STAGES]);
+      }
       if (ti < ntiles) logits_softmax(ti, sm.stage[ti % STAGES]);
     }
   } else {
@@ -343,7 +372,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
       if (ti + 1 < ntiles) issue_tile(ti + 1);
       if (ti < ntiles) dequant(ti);
       lds_barrier_keep_dma();  // bf16 tile ti is complete
-      if (ti > 0) pv(ti - 1, sm.tile[(ti - 1) & 1]);
+      if (ti > 0) {
+        pv_rescale(ti - 1);
+        pv(ti - 1, sm.tile[(ti - 1) & 1]);
+      }
       if (ti < ntiles) logits_softmax(ti, sm.tile[ti & 1]);
     }
   }
