@@ -327,11 +327,13 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
     for (int ti = 0; ti <= ntiles; ++ti) {
       __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // tile ti, the only one in flight, has landed
       lds_barrier_keep_dma();  // and every wave has left iteration ti-1 (stage (ti+1)%3 is free)
-      if (ti + 1 < ntiles) issue_tile(ti + 1);
       if (ti > 0) {
         pv_rescale(ti - 1);
         pv(ti - 1, sm.stage[(ti - 1) % STAGES]);
       }
+      // the next tile's gather, issued after the PV (it lands during the
+      // logits and the next PV)
+      if (ti + 1 < ntiles) issue_tile(ti + 1);
       if (ti < ntiles) logits_softmax(ti, sm.stage[ti % STAGES]);
     }
   } else {
