@@ -92,7 +92,9 @@ __device__ __forceinline__ int plan_vis(const IdxParams& p, int t) {
 // fields the later passes read are kept in LDS (dynamic, PLAN_LDS_BYTES), so
 // no pass waits on a global round trip for what an earlier pass produced.
 constexpr int PLAN_LDS_T = 4096;
-constexpr size_t PLAN_LDS_BYTES = (size_t)5 * PLAN_LDS_T * sizeof(int);
+constexpr int PLAN_LOADS = PLAN_LDS_T / PLAN_NT;  // queries per thread when staged in LDS
+constexpr size_t PLAN_LDS_BYTES = (size_t)6 * PLAN_LDS_T * sizeof(int);
+static_assert(PLAN_LDS_T % PLAN_NT == 0, "staged queries per thread");
 
 __global__ __launch_bounds__(PLAN_NT) void dsa_plan_kernel(IdxParams p) {
   __shared__ int s_w[16];
@@ -104,16 +106,45 @@ __global__ __launch_bounds__(PLAN_NT) void dsa_plan_kernel(IdxParams p) {
   int* s_nq = plan_lds + 2 * PLAN_LDS_T;    // [groups] queries
   int* s_rng = plan_lds + 3 * PLAN_LDS_T;   // [groups] key range
   int* s_off = plan_lds + 4 * PLAN_LDS_T;   // [groups] offset in the key space
+  int* s_seq = plan_lds + 5 * PLAN_LDS_T;   // [T] sequence of each query (-1: none)
   const int tid = threadIdx.x;
   const int nt = blockDim.x;  // fewer waves per barrier for a short batch
+  // ---- pass 0 (queries staged in LDS): every query's sequence and horizon
+  // loaded at once (one round trip), then the sequences' lengths (a second)
+  if (in_lds) {
+    int qs[PLAN_LOADS], qv[PLAN_LOADS];
+#pragma unroll
+    for (int i = 0; i < PLAN_LOADS; ++i) {
+      const int t = tid + i * nt;
+      qs[i] = t < p.T ? (p.q_seq ? p.q_seq[t] : t) : -1;
+      qv[i] = (t < p.T && p.q_visible) ? p.q_visible[t] : 0;
+    }
+    int len[PLAN_LOADS];
+#pragma unroll
+    for (int i = 0; i < PLAN_LOADS; ++i) {
+      qs[i] = (qs[i] >= 0 && qs[i] < p.B) ? qs[i] : -1;
+      len[i] = qs[i] >= 0 ? p.seq_lens[qs[i]] : 0;
+    }
+    const int maxlen = p.max_blocks * PAGE;
+#pragma unroll
+    for (int i = 0; i < PLAN_LOADS; ++i) {
+      const int t = tid + i * nt;
+      if (t < p.T) {
+        const int L = min(max(len[i], 0), maxlen);
+        const int v = p.q_visible ? qv[i] : L;
+        s_seq[t] = qs[i];
+        s_vis[t] = qs[i] >= 0 ? min(max(v, 0), L) : 0;
+      }
+    }
+    __syncthreads();
+  }
   // ---- pass 1: group starts (runs of one sequence, cut every MQ queries)
   int carry_run = 0, carry_gid = 0;
   for (int base = 0; base < p.T; base += nt) {
     const int t = base + tid;
     const bool valid = t < p.T;
-    const int b = valid ? plan_seq(p, t) : -2;
-    const int bprev = (valid && t > 0) ? plan_seq(p, t - 1) : -3;
-    if (in_lds && valid) s_vis[t] = plan_vis(p, t);
+    const int b = valid ? (in_lds ? s_seq[t] : plan_seq(p, t)) : -2;
+    const int bprev = (valid && t > 0) ? (in_lds ? s_seq[t - 1] : plan_seq(p, t - 1)) : -3;
     const bool f = valid && (t == 0 || b != bprev);
     int run = block_scan_incl(f ? t : -1, s_w, true);
     run = max(run, carry_run);
