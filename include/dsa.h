@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 6
+#define DSA_ABI_VERSION 7
 #define DSA_PAGE_TOKENS 64
 #define DSA_LATENT_DIM 576
 #define DSA_VALUE_DIM 512
@@ -86,8 +86,9 @@ typedef enum dsa_status {
   DSA_ERR_WORKSPACE = 6,   /* ws_bytes < dsa_workspace_bytes(...) or ws NULL      */
   DSA_ERR_UNSUPPORTED = 7, /* a valid but unimplemented combination               */
   DSA_ERR_HIP = 8,         /* a HIP launch failed                                 */
-  DSA_ERR_TOO_LARGE = 9    /* dsa_layer_static: the call needs more scratch than  */
+  DSA_ERR_TOO_LARGE = 9,   /* dsa_layer_static: the call needs more scratch than  */
                            /* DSA_STATIC_SCRATCH_BYTES                            */
+  DSA_ERR_TABLE = 10       /* dsa_check_tables: a table entry is out of range     */
 } dsa_status;
 
 typedef enum dsa_kv_dtype {
@@ -281,6 +282,26 @@ dsa_status dsa_layer_static(const dsa_indexer_args* idx, const dsa_mla_args* mla
  */
 dsa_status dsa_quantize_index_q(const void* q, int64_t rows, int32_t D, int32_t idx_dtype, void* codes,
                                 void* scales, void* stream);
+
+/*
+ * Debugging aid for the device-side contents the indexer reads (they are the
+ * caller's responsibility; the kernels treat bad entries as absent pages or
+ * clamp them, see the conventions above).  Checks HOST copies of the tables of
+ * a dsa_indexer_args call, without touching the device:
+ *   seq_lens[b]        in [0, 64 * max_blocks]                  (table 0)
+ *   block_table[b][i]  in [0, num_blocks) for the pages that hold
+ *                      positions 0 .. seq_lens[b] - 1            (table 1)
+ *   q_seq[t]           in [0, B)                                (table 2)
+ *   q_visible[t]       in [0, seq_lens[q_seq[t]]]                (table 3)
+ * seq_lens [B] and block_table [B][max_blocks] are required; q_seq and
+ * q_visible are required exactly when the call's device pointers are set.
+ * Returns DSA_OK, or DSA_ERR_TABLE with *bad_table and *bad_index (flat index
+ * into that table) naming the first bad entry; argument errors as for
+ * dsa_indexer_topk (K is not checked).  bad_table / bad_index may be NULL.
+ */
+dsa_status dsa_check_tables(const dsa_indexer_args* a, const int32_t* seq_lens, const int32_t* block_table,
+                            const int32_t* q_seq, const int32_t* q_visible, int32_t* bad_table,
+                            int64_t* bad_index);
 
 /* Static string for a status code ("unknown status" for anything else). */
 const char* dsa_status_str(dsa_status s);

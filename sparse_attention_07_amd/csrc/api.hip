@@ -321,6 +321,7 @@ const char* dsa_status_str(dsa_status s) {
     case DSA_ERR_UNSUPPORTED: return "unsupported combination";
     case DSA_ERR_HIP: return "HIP launch failed";
     case DSA_ERR_TOO_LARGE: return "the call needs more scratch than the library's static array holds";
+    case DSA_ERR_TABLE: return "a table entry is out of range";
   }
   return "unknown status";
 }
@@ -397,6 +398,37 @@ dsa_status dsa_layer_static(const dsa_indexer_args* idx, const dsa_mla_args* mla
   st = scratch_of_current_device(&w);
   if (st != DSA_OK) return st;
   return layer_launch(idx, mla, K, scale, indices_out, out, w, (hipStream_t)stream);
+}
+
+dsa_status dsa_check_tables(const dsa_indexer_args* a, const int32_t* seq_lens, const int32_t* block_table,
+                            const int32_t* q_seq, const int32_t* q_visible, int32_t* bad_table,
+                            int64_t* bad_index) {
+  dsa_status st = check_indexer(a, 1);
+  if (st != DSA_OK) return st;
+  if (!seq_lens || !block_table) return DSA_ERR_NULL;
+  if ((a->q_seq != nullptr) != (q_seq != nullptr) || (a->q_visible != nullptr) != (q_visible != nullptr))
+    return DSA_ERR_NULL;
+  auto bad = [&](int table, int64_t index) {
+    if (bad_table) *bad_table = table;
+    if (bad_index) *bad_index = index;
+    return DSA_ERR_TABLE;
+  };
+  const int64_t maxlen = (int64_t)a->max_blocks * DSA_PAGE_TOKENS;
+  for (int64_t b = 0; b < a->B; ++b)
+    if (seq_lens[b] < 0 || seq_lens[b] > maxlen) return bad(0, b);
+  for (int64_t b = 0; b < a->B; ++b) {
+    const int64_t pages = ((int64_t)seq_lens[b] + DSA_PAGE_TOKENS - 1) / DSA_PAGE_TOKENS;
+    for (int64_t i = 0; i < pages; ++i) {
+      const int32_t pg = block_table[b * a->max_blocks + i];
+      if (pg < 0 || pg >= a->num_blocks) return bad(1, b * a->max_blocks + i);
+    }
+  }
+  for (int64_t t = 0; t < a->T; ++t) {
+    const int64_t b = q_seq ? q_seq[t] : t;
+    if (b < 0 || b >= a->B) return bad(2, t);
+    if (q_visible && (q_visible[t] < 0 || q_visible[t] > seq_lens[b])) return bad(3, t);
+  }
+  return DSA_OK;
 }
 
 dsa_status dsa_quantize_index_q(const void* q, int64_t rows, int32_t D, int32_t idx_dtype, void* codes,

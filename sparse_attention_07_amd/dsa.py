@@ -28,7 +28,8 @@ MAX_K = 2048
 
 # Every symbol the header declares (checked by the tests against include/dsa.h).
 EXPORTS = ("dsa_workspace_bytes", "dsa_indexer_topk", "dsa_indexer_scores", "dsa_sparse_mla_attn", "dsa_layer",
-           "dsa_layer_static", "dsa_quantize_index_q", "dsa_status_str", "dsa_abi_version")
+           "dsa_layer_static", "dsa_quantize_index_q", "dsa_check_tables", "dsa_status_str", "dsa_abi_version")
+TABLE_NAMES = ("seq_lens", "block_table", "q_seq", "q_visible")
 STATIC_SCRATCH_BYTES = 64 << 20
 
 
@@ -85,6 +86,9 @@ def _load() -> ctypes.CDLL:
     lib.dsa_quantize_index_q.restype = ctypes.c_int
     lib.dsa_quantize_index_q.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.dsa_check_tables.restype = ctypes.c_int
+    lib.dsa_check_tables.argtypes = [P(IndexerArgs), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p, P(ctypes.c_int32), P(ctypes.c_int64)]
     lib.dsa_status_str.restype = ctypes.c_char_p
     lib.dsa_status_str.argtypes = [ctypes.c_int]
     lib.dsa_abi_version.restype = ctypes.c_int
@@ -183,6 +187,23 @@ def indexer_scores(q_idx, w, k_idx_pool, block_table, seq_lens, *, q_idx_scale=N
     workspace = _workspace(workspace_bytes(a, None, 1), q_idx.device)
     _check(LIB.dsa_indexer_scores(ctypes.byref(a), _ptr(scores), ld, _ptr(workspace), workspace.numel(), _stream()))
     return scores
+
+
+def check_tables(q_idx, w, k_idx_pool, block_table, seq_lens, *, q_idx_scale=None, q_seq=None, q_visible=None,
+                 max_q_per_seq: int = 1):
+    """Debugging aid: checks host copies of the tables an indexer call reads
+    (the arguments are those of indexer_topk).  Returns None when every entry
+    is in range, else (table name, flat index) of the first bad entry."""
+    a = indexer_args(q_idx, w, k_idx_pool, block_table, seq_lens, q_idx_scale=q_idx_scale, q_seq=q_seq,
+                     q_visible=q_visible, max_q_per_seq=max_q_per_seq)
+    host = [None if x is None else x.detach().to("cpu", torch.int32).contiguous()
+            for x in (seq_lens, block_table, q_seq, q_visible)]
+    table, index = ctypes.c_int32(-1), ctypes.c_int64(-1)
+    code = LIB.dsa_check_tables(ctypes.byref(a), *[_ptr(x) for x in host], ctypes.byref(table), ctypes.byref(index))
+    if code == 10:
+        return TABLE_NAMES[table.value], int(index.value)
+    _check(code)
+    return None
 
 
 def sparse_mla_attn(q, kv_pool, indices, scale: float, *, out: Optional[torch.Tensor] = None,

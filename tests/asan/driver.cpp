@@ -158,7 +158,7 @@ int main() {
     CHECK(dsa_quantize_index_q(P(), 64, 96, DSA_IDX_FP8_E4M3FN, P(), P(), nullptr) == DSA_ERR_SHAPE);
     CHECK(dsa_quantize_index_q(P(), -1, 128, DSA_IDX_FP8_E4M3FN, P(), P(), nullptr) == DSA_ERR_SHAPE);
     CHECK(dsa::g_idx_calls + dsa::g_mla_calls + dsa::g_quant_calls == before);
-    for (int s = 0; s <= 9; ++s) CHECK(dsa_status_str((dsa_status)s) != nullptr);
+    for (int s = 0; s <= 10; ++s) CHECK(dsa_status_str((dsa_status)s) != nullptr);
     CHECK(dsa_abi_version() == DSA_ABI_VERSION);
   }
   // ---- the static-scratch layer rejects calls larger than its array before
@@ -167,6 +167,30 @@ int main() {
     dsa_indexer_args a = idx_args(8192, 1, 128, 128, DSA_IDX_FP8_E4M3FN, 8192, true);
     dsa_mla_args m = mla_args(8192, 128, 128);
     CHECK(dsa_layer_static(&a, &m, 2048, 0.04f, nullptr, P(), nullptr) == DSA_ERR_TOO_LARGE);
+  }
+  // ---- host-copy table checks: every entry of a small call, one planted error per table
+  {
+    dsa_indexer_args a = idx_args(4, 3, 5, 12, DSA_IDX_FP8_E4M3FN, 2, true);
+    std::vector<int32_t> lens = {300, 64, 1}, bt(3 * 5, 0), qs = {0, 0, 1, 2}, qv = {299, 300, 64, 1};
+    for (int i = 0; i < 15; ++i) bt[i] = i % 12;
+    int32_t tab = -1;
+    int64_t at = -1;
+    CHECK(dsa_check_tables(&a, lens.data(), bt.data(), qs.data(), qv.data(), &tab, &at) == DSA_OK);
+    bt[4] = 12;
+    CHECK(dsa_check_tables(&a, lens.data(), bt.data(), qs.data(), qv.data(), &tab, &at) == DSA_ERR_TABLE);
+    CHECK(tab == 1 && at == 4);
+    bt[4] = 0;
+    qv[1] = 301;
+    CHECK(dsa_check_tables(&a, lens.data(), bt.data(), qs.data(), qv.data(), &tab, &at) == DSA_ERR_TABLE);
+    CHECK(tab == 3 && at == 1);
+    qv[1] = 300;
+    qs[3] = 3;
+    CHECK(dsa_check_tables(&a, lens.data(), bt.data(), qs.data(), qv.data(), nullptr, nullptr) == DSA_ERR_TABLE);
+    qs[3] = 2;
+    lens[2] = 321;
+    CHECK(dsa_check_tables(&a, lens.data(), bt.data(), qs.data(), qv.data(), &tab, &at) == DSA_ERR_TABLE);
+    CHECK(tab == 0 && at == 2);
+    CHECK(dsa_check_tables(&a, lens.data(), bt.data(), nullptr, qv.data(), &tab, &at) == DSA_ERR_NULL);
   }
   if (failures) {
     std::fprintf(stderr, "%d checks failed\n", failures);

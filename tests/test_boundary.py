@@ -14,7 +14,7 @@ HEADER = os.path.join(ROOT, "include", "dsa.h")
 
 dsa = pytest.importorskip("sparse_attention_07_amd.dsa", reason="libdsa.so not built")
 
-OK, E_NULL, E_DTYPE, E_SHAPE, E_K, E_ALIGN, E_WS, E_UNSUP, E_HIP, E_TOO_LARGE = range(10)
+OK, E_NULL, E_DTYPE, E_SHAPE, E_K, E_ALIGN, E_WS, E_UNSUP, E_HIP, E_TOO_LARGE, E_TABLE = range(11)
 
 
 def header_functions():
@@ -35,10 +35,10 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     m = re.search(r"#define DSA_ABI_VERSION (\d+)", open(HEADER).read())
-    assert int(m.group(1)) == 6
+    assert int(m.group(1)) == 7
     assert dsa.LIB.dsa_abi_version() == int(m.group(1))
     assert dsa.status_str(0) == "ok"
-    for s in range(1, 10):
+    for s in range(1, 11):
         assert dsa.status_str(s) and dsa.status_str(s) != "unknown status"
     assert dsa.status_str(99) == "unknown status"
 
@@ -254,3 +254,38 @@ def test_quantize_mxfp8_scale_bytes_need_no_alignment():
     # the E8M0 bytes are written one per group: any address; rows=0 stops before a launch
     assert call_quant(dt=dsa.IDX_MXFP8_E4M3, scales=_base + 1, rows=0) == OK
     assert call_quant(dt=dsa.IDX_MXFP8_E4M3, scales=_base + 1, q=_base + 4) == E_ALIGN
+
+
+def test_check_tables_on_host_copies():
+    import torch
+    from sparse_attention_07_amd import synth
+    case = synth.build_case(synth.CaseSpec("tables", H_idx=16, D_idx=128, idx_dtype="fp8", K=64, H=16,
+                                           lens=[300, 64, 1], queries_per_seq=[2, 1, 1], seed=3))
+    kw = dict(q_idx_scale=case.q_idx_scale, q_seq=case.q_seq, q_visible=case.q_visible,
+              max_q_per_seq=case.max_q_per_seq)
+    args = (case.q_idx, case.w, case.k_idx_pool, case.block_table, case.seq_lens)
+    assert dsa.check_tables(*args, **kw) is None
+    nb, mb = case.num_blocks, case.block_table.shape[1]
+
+    def planted(name, index, value):
+        t = {"seq_lens": case.seq_lens, "block_table": case.block_table, "q_seq": case.q_seq,
+             "q_visible": case.q_visible}[name].clone()
+        t.view(-1)[index] = value
+        a = list(args)
+        k = dict(kw)
+        if name in ("seq_lens", "block_table"):
+            a[4 if name == "seq_lens" else 3] = t
+        else:
+            k[name] = t
+        return dsa.check_tables(*a, **k)
+    assert planted("block_table", 0 * mb + 4, nb) == ("block_table", 4)    # page 4 of sequence 0 (position 256+)
+    assert planted("block_table", 1 * mb + 0, -1) == ("block_table", mb)
+    assert planted("block_table", 1 * mb + 1, -1) is None                  # past sequence 1's only page
+    assert planted("seq_lens", 2, 64 * mb + 1) == ("seq_lens", 2)
+    assert planted("q_seq", 3, 3) == ("q_seq", 3)
+    assert planted("q_visible", 0, 301) == ("q_visible", 0)
+    assert planted("q_visible", 2, -1) == ("q_visible", 2)
+    # host copies missing where the call has device tables
+    a = dsa.indexer_args(*args, **kw)
+    st = dsa.LIB.dsa_check_tables(ctypes.byref(a), None, None, None, None, None, None)
+    assert st == E_NULL
