@@ -119,6 +119,21 @@ __device__ __forceinline__ void dma16_to_lds(const void* gaddr, uint32_t lds_bas
       : "memory");
 }
 
+// The same copy from a wave-uniform base address (SGPR pair) plus a 32-bit
+// per-lane byte offset: the address arithmetic of a whole wave-load stays
+// scalar.
+__device__ __forceinline__ void dma16_to_lds_saddr(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  uint32_t saved_m0;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved_m0)
+      : "v"(voff), "s"(sbase), "s"(lds_base)
+      : "memory");
+}
+
 // Device-coherent (agent-scope) loads and stores for data that one workgroup
 // hands to another inside a launch.  They bypass the per-XCD cache levels a
 // plain access may find stale, so no device-scope fence (a writeback and an

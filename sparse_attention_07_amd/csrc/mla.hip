@@ -11,10 +11,11 @@
 //  * grid = (split, query); a workgroup owns a contiguous slice of the query's
 //    index list and all H heads, so every gathered row leaves HBM once;
 //  * rows are gathered 32 at a time with direct-to-LDS 16-byte loads
-//    (global_load_lds_dwordx4) into a 3-stage ring; rows sit at a padded
-//    stride of 74 sixteen-byte units in a permuted slot order that makes the
-//    operand reads of both phases free of bank conflicts (see row_slot), and
-//    operand addresses stay base + immediate;
+//    (global_load_lds_dwordx4) into a 3-stage ring: a row's 512 value dims
+//    are one 64-lane load from a uniform (scalar) row address, its rope dims
+//    a fifth of a load; rows sit in a permuted slot order at padded strides
+//    that keep the operand reads of both phases free of bank conflicts (see
+//    row_slot), and operand addresses stay base + immediate;
 //  * H/16 waves.  Logits: wave w owns heads 16w..16w+15, keeps their q in
 //    registers as the MFMA B operand and computes S^T = C q^T (bf16 16x16x32;
 //    rows on M in an order that makes the probabilities come out as 8
@@ -50,12 +51,13 @@ namespace dsa {
 constexpr int TILE_ROWS = 32;
 constexpr float RESCALE_SLACK = 8.f;  // log2 of the largest unnormalised probability
 constexpr int MLA_SMAX = 8;  // most splits of a query's index list (K / 256 for K <= 2048)
-constexpr int ROW_UNITS = LATENT * 2 / 16;                         // 72 sixteen-byte units per row
-constexpr int ROW_STRIDE = ROW_UNITS + 2;                          // padded row stride (units)
-constexpr int TILE_LOADS = (TILE_ROWS * ROW_STRIDE + 63) / 64;     // 37 wave-loads of 64 units
-constexpr int PT_STRIDE = TILE_ROWS + 16;                          // P^T row (bf16): 6 sixteen-byte units
+constexpr int A_STRIDE = 66;                          // value region: units per row slot (64 + 2 padding)
+constexpr int B_UNIT0 = TILE_ROWS * A_STRIDE;         // rope region: first unit
+constexpr int B_STRIDE = 10;                          // rope region: units per row slot (8 + 2 padding)
+constexpr int ROPE_LOADS = (TILE_ROWS * B_STRIDE + 63) / 64;  // 5 wave-loads
+constexpr int PT_STRIDE = TILE_ROWS + 16;             // P^T row (bf16): 6 sixteen-byte units
 constexpr int STAGES = 3;
-constexpr int STAGE_BYTES = TILE_LOADS * 64 * 16;
+constexpr int STAGE_BYTES = (B_UNIT0 + ROPE_LOADS * 64) * 16;  // 38,912 B
 
 // FP8 latent rows: 512 code bytes, 4 fp32 scales, 64 bf16 rope dims
 constexpr int KV8_ROW_UNITS = 41;                                   // 656 B
@@ -64,24 +66,26 @@ constexpr int KV8_ROPE_OFF = 528;
 constexpr int KV8_TILE_LOADS = (TILE_ROWS * KV8_ROW_UNITS + 63) / 64;  // 21 wave-loads of 64 units
 constexpr int KV8_STAGE_BYTES = KV8_TILE_LOADS * 64 * 16;
 
-// byte offset, inside a stage, of bf16 element (row r, column col)
-// LDS layout of a tile (bank conflicts measured with the LDS counters on
-// gfx950): a wave's 16-byte reads that put 16 lanes on 16 rows, the 4 lane
-// groups one unit apart, are conflict-free when the rows lie 2 mod 4 units
-// apart (74 here) and take 2-4 cycles more otherwise.  The logits A operand
-// of M-tile mt reads tile rows 8*(n/4) + n%4 + 4*mt for lanes n = 0..15, so
-// tile row r is stored in slot p(r) = 4*(r/8) + r%4 + 16*((r/4)%2): each
-// M-tile reads 16 consecutive slots.  The PV transpose reads (rows 8*g + j
-// and 8*g + 4 + j) then also fall on consecutive slots.
+// LDS layout of a bf16 tile.  Tile row r is stored in row slot
+// p(r) = 4*(r/8) + r%4 + 16*((r/4)%2): the logits A operand of M-tile mt
+// reads tile rows 8*(n/4) + n%4 + 4*mt for lanes n = 0..15, i.e. 16
+// consecutive slots, and the PV transpose reads (rows 8*g + j and 8*g + 4 + j)
+// fall on consecutive slots too.  A slot's 512 value dims (64 sixteen-byte
+// units) sit in the value region at a stride of 66 units, its 64 rope dims in
+// the rope region at 10 units.  Bank conflicts (measured with the LDS
+// counters on gfx950): a wave's 16-byte reads that put 16 lanes on 16 slots,
+// the 4 lane groups one unit apart, are conflict-free when the slots lie
+// 2 mod 4 units apart and take 2-4 cycles more otherwise.  The split of the
+// two regions makes one row's value units one 64-lane direct-to-LDS load
+// from a uniform row address.
 __device__ __forceinline__ int row_slot(int r) { return 4 * (r >> 3) + (r & 3) + 16 * ((r >> 2) & 1); }
 __device__ __forceinline__ int slot_row(int p) { return 8 * ((p & 15) >> 2) + (p & 3) + 4 * (p >> 4); }
-__device__ __forceinline__ int row_unit(int r) { return ROW_STRIDE * row_slot(r); }
-
-// byte offset, inside a stage, of bf16 element (row r, column col)
-__device__ __forceinline__ int stage_off(int r, int col) { return 16 * (row_unit(r) + (col >> 3)) + 2 * (col & 7); }
+// unit, inside a stage, of value unit u (0..63) and of rope unit j (0..7) of tile row r
+__device__ __forceinline__ int val_unit(int r, int u) { return A_STRIDE * row_slot(r) + u; }
+__device__ __forceinline__ int rope_unit(int r, int j) { return B_UNIT0 + B_STRIDE * row_slot(r) + j; }
 
 template <int NW, bool KV8>
-struct MlaSmem {
+struct alignas(16) MlaSmem {
   static constexpr int NSTAGE = KV8 ? 2 : STAGES;
   unsigned char stage[NSTAGE][KV8 ? KV8_STAGE_BYTES : STAGE_BYTES];  // gather ring
   unsigned char tile[KV8 ? 2 : 1][KV8 ? STAGE_BYTES : 16];          // FP8 only: two dequantized bf16 tiles
@@ -90,7 +94,7 @@ struct MlaSmem {
   float mfin[16 * NW];
   float lfin[16 * NW];
   float red[NW];  // per-wave partial sums (residual + RMSNorm epilogue)
-  // followed by the slice's slots (int32)
+  // followed by the slice's slots (int32, 16-byte aligned)
 };
 
 // 16 e4m3fn codes times one scale -> 16 bf16 (round to nearest even)
@@ -114,10 +118,11 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
   constexpr int NT = NW * 64;
   constexpr int H = 16 * NW;
   constexpr int VT = 32 / NW;  // 16-wide value tiles per wave in PV
-  constexpr int LOADS = KV8 ? KV8_TILE_LOADS : TILE_LOADS;
-  constexpr int RUNITS = KV8 ? KV8_ROW_UNITS : ROW_STRIDE;  // units per row in the gather ring
-  constexpr int LMIN = LOADS / NW;                     // DMA loads of every wave per tile
-  constexpr int LEXTRA = LOADS - LMIN * NW;            // waves [0, LEXTRA) issue one more
+  constexpr int LOADS = KV8_TILE_LOADS;                // FP8 rows: wave-loads per tile
+  constexpr int RUNITS = KV8_ROW_UNITS;                // FP8 rows: units per row in the gather ring
+  constexpr int LMIN = LOADS / NW;                     // FP8 rows: DMA loads of every wave per tile
+  constexpr int LEXTRA = LOADS - LMIN * NW;            // FP8 rows: waves [0, LEXTRA) issue one more
+  constexpr int RPW = TILE_ROWS / NW;                  // bf16 rows: value rows each wave gathers per tile
   extern __shared__ __align__(16) unsigned char smem_raw[];
   MlaSmem<NW, KV8>& sm = *reinterpret_cast<MlaSmem<NW, KV8>*>(smem_raw);
   int32_t* sidx = reinterpret_cast<int32_t*>(smem_raw + sizeof(MlaSmem<NW, KV8>));
@@ -174,36 +179,58 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
   lds_barrier();
 
   constexpr int NSTAGE = MlaSmem<NW, KV8>::NSTAGE;
-  // Load k of this wave covers ring units (first + k) * 64 + lane: the lane's
-  // row (bf16: slot of the permuted layout) and 16-byte column advance by 64
-  // units (less than one row) per load, so they are stepped, not divided.
+  // FP8 rows: load k of this wave covers ring units (first + k) * 64 + lane;
+  // the lane's row and 16-byte column advance by 64 units (less than one row)
+  // per load, so they are stepped, not divided.
   const int first_u = (wave * LMIN + min(wave, LEXTRA)) * 64 + lane;
   const int r_first = first_u / RUNITS;
   const int c_first = first_u - r_first * RUNITS;
   auto issue_tile = [&](int ti) {
     unsigned char* st = sm.stage[ti % NSTAGE];
-    const int nl = LMIN + (wave < LEXTRA ? 1 : 0);
-    const int first = wave * LMIN + min(wave, LEXTRA);
-    int r = r_first, c = c_first;
-    for (int k = 0; k < nl; ++k) {
-      int rr = r, cc = c;
-      if (rr >= TILE_ROWS || cc >= (KV8 ? KV8_ROW_UNITS : ROW_UNITS)) {  // padding: a harmless valid unit
-        rr = min(rr, TILE_ROWS - 1);
-        cc = 0;
+    const uint32_t st_lds = uniform((uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)st);
+    if constexpr (!KV8) {
+      // value units: one wave-load per row (lane i: unit i), from a uniform
+      // row address, so the address arithmetic is scalar
+#pragma unroll
+      for (int i0 = 0; i0 < RPW; i0 += 4) {
+        // this wave's next 4 rows (4 consecutive row slots): slots in one read
+        const v4i sl = *reinterpret_cast<const v4i*>(&sidx[ti * TILE_ROWS + RPW * wave + i0]);
+        const uint32_t lds0 = uniform(st_lds + 16 * A_STRIDE * row_slot(RPW * wave + i0));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          int slot = __builtin_amdgcn_readfirstlane(sl[i]);
+          slot = slot < 0 ? 0 : slot;
+          dma16_to_lds_saddr(p.kv + (int64_t)slot * LATENT, 16 * lane, lds0 + 16 * A_STRIDE * i);
+        }
       }
-      if constexpr (!KV8) rr = slot_row(rr);
-      int slot = sidx[ti * TILE_ROWS + rr];
-      slot = slot < 0 ? 0 : slot;
-      const uint16_t* g = KV8 ? p.kv + (int64_t)slot * (KV8_ROW_UNITS * 8) + 8 * cc
-                              : p.kv + (int64_t)slot * LATENT + 8 * cc;
-      const uint32_t lds_addr =
-          (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)(st + 16 * (first + k) * 64);
-      dma16_to_lds(g, uniform(lds_addr));
-      r += 64 / RUNITS;
-      c += 64 % RUNITS;
-      if (c >= RUNITS) {
-        c -= RUNITS;
-        ++r;
+      // rope units: wave-load j covers rope-region units 64j + lane (the two
+      // padding units of a slot get a harmless valid unit)
+      for (int j = wave; j < ROPE_LOADS; j += NW) {
+        const uint32_t u = 64 * j + lane;
+        const uint32_t ps = u / B_STRIDE, c = u - ps * B_STRIDE;
+        int slot = sidx[ti * TILE_ROWS + slot_row(ps)];
+        slot = slot < 0 ? 0 : slot;
+        dma16_to_lds(p.kv + (int64_t)slot * LATENT + 512 + 8 * (c < 8 ? c : 0), uniform(st_lds + 16 * (B_UNIT0 + 64 * j)));
+      }
+    } else {
+      const int nl = LMIN + (wave < LEXTRA ? 1 : 0);
+      const int first = wave * LMIN + min(wave, LEXTRA);
+      int r = r_first, c = c_first;
+      for (int k = 0; k < nl; ++k) {
+        int rr = r, cc = c;
+        if (rr >= TILE_ROWS || cc >= KV8_ROW_UNITS) {  // padding: a harmless valid unit
+          rr = min(rr, TILE_ROWS - 1);
+          cc = 0;
+        }
+        int slot = sidx[ti * TILE_ROWS + rr];
+        slot = slot < 0 ? 0 : slot;
+        dma16_to_lds(p.kv + (int64_t)slot * (KV8_ROW_UNITS * 8) + 8 * cc, st_lds + 16 * (first + k) * 64);
+        r += 64 / RUNITS;
+        c += 64 % RUNITS;
+        if (c >= RUNITS) {
+          c -= RUNITS;
+          ++r;
+        }
       }
     }
   };
@@ -229,12 +256,15 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
     const uint32_t vmask = (uint32_t)ballot(lane < 32 && sidx[ti * TILE_ROWS + (lane & 31)] >= 0);
     v4f acc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
     // M-tile row n16 holds tile row 8*(n16/4) + 4*mt + n16%4; k-step ks adds 64 bytes
-    const unsigned char* la0 = st + 16 * (row_unit(8 * (n16 >> 2) + (n16 & 3)) + g4);  // slot n16
-    const unsigned char* la1 = la0 + 16 * 16 * ROW_STRIDE;                              // slot 16 + n16
+    // (value region for k-steps 0..15, rope region for 16 and 17)
+    const unsigned char* la0 = st + 16 * (A_STRIDE * n16 + g4);  // slot n16
+    const unsigned char* lb0 = st + 16 * (B_UNIT0 + B_STRIDE * n16 + g4);
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) {
-      const v4i a0 = *reinterpret_cast<const v4i*>(la0 + 64 * ks);
-      const v4i a1 = *reinterpret_cast<const v4i*>(la1 + 64 * ks);
+      const unsigned char* a0p = ks < 16 ? la0 + 64 * ks : lb0 + 64 * (ks - 16);
+      const unsigned char* a1p = a0p + 16 * 16 * (ks < 16 ? A_STRIDE : B_STRIDE);  // slot 16 + n16
+      const v4i a0 = *reinterpret_cast<const v4i*>(a0p);
+      const v4i a1 = *reinterpret_cast<const v4i*>(a1p);
       acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a0), __builtin_bit_cast(v8bf, qb[ks]),
                                                        acc[0], 0, 0, 0);
       acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a1), __builtin_bit_cast(v8bf, qb[ks]),
@@ -300,13 +330,13 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
     // (the rescale by alpha is pv_rescale, run before)
     {
       // transpose-read base: row 8*g4 + n16/4, column 16*(wave*VT) + 4*(n16%4); v tile vt adds 32 bytes
-      const unsigned char* tb = st + stage_off(8 * g4 + (n16 >> 2), wave * VT * 16 + 4 * (n16 & 3));
+      const unsigned char* tb = st + 16 * val_unit(8 * g4 + (n16 >> 2), wave * VT * 2) + 8 * (n16 & 3);
       v8bf av[VT];
 #pragma unroll
       for (int vt = 0; vt < VT; ++vt) {
         const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(tb + 32 * vt));
         const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4s*)(tb + 16 * 16 * ROW_STRIDE + 32 * vt));  // row + 4: slot + 16
+            (__attribute__((address_space(3))) v4s*)(tb + 16 * 16 * A_STRIDE + 32 * vt));  // row + 4: slot + 16
         av[vt] = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
 #pragma unroll
@@ -329,12 +359,12 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
       lds_barrier_keep_dma();  // and every wave has left iteration ti-1 (stage (ti+1)%3 is free)
       if (ti > 0) {
         pv_rescale(ti - 1);
-        pv(ti - 1, sm.stage[(ti - 1) % STAGES]);
+        pv(ti - 1, sm.stage[uniform((ti - 1) % STAGES)]);
       }
       // the next tile's gather, issued after the PV (it lands during the
       // logits and the next PV)
       if (ti + 1 < ntiles) issue_tile(ti + 1);
-      if (ti < ntiles) logits_softmax(ti, sm.stage[ti % STAGES]);
+      if (ti < ntiles) logits_softmax(ti, sm.stage[uniform(ti % STAGES)]);
     }
   } else {
     // FP8 rows, pipelined like the bf16 loop with one more barrier: once tile
@@ -357,14 +387,14 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
         const float sc = *reinterpret_cast<const float*>(rowp + KV8_SCALE_OFF + 4 * (k >> 3));
         v4i lo, hi;
         dequant16(c16, sc, lo, hi);
-        unsigned char* d = dst + 16 * (row_unit(r) + 2 * k);
+        unsigned char* d = dst + 16 * val_unit(r, 2 * k);
         *reinterpret_cast<v4i*>(d) = lo;
         *reinterpret_cast<v4i*>(d + 16) = hi;
       }
 #pragma unroll 1
       for (int i = tid_o; i < TILE_ROWS * 8; i += NT) {  // rope: 8 units per row, copied
         const int r = i >> 3, j = i & 7;
-        *reinterpret_cast<v4i*>(dst + 16 * (row_unit(r) + 64 + j)) =
+        *reinterpret_cast<v4i*>(dst + 16 * rope_unit(r, j)) =
             *reinterpret_cast<const v4i*>(src + 16 * KV8_ROW_UNITS * r + KV8_ROPE_OFF + 16 * j);
       }
     };
