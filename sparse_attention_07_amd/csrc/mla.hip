@@ -46,6 +46,7 @@
 #include "dsa_device.h"
 #include "dsa_params.h"
 
+
 namespace dsa {
 
 constexpr int TILE_ROWS = 32;
@@ -57,6 +58,7 @@ constexpr int B_STRIDE = 10;                          // rope region: units per 
 constexpr int ROPE_LOADS = (TILE_ROWS * B_STRIDE + 63) / 64;  // 5 wave-loads
 constexpr int PT_STRIDE = TILE_ROWS + 16;             // P^T row (bf16): 6 sixteen-byte units
 constexpr int STAGES = 3;
+constexpr int LDS_AHEAD = 2;  // logits: k-steps of A operands read ahead (3 needs more registers than a wave has)
 constexpr int STAGE_BYTES = (B_UNIT0 + ROPE_LOADS * 64) * 16;  // 38,912 B
 
 // FP8 latent rows: 512 code bytes, 4 fp32 scales, 64 bf16 rope dims
@@ -96,6 +98,15 @@ struct alignas(16) MlaSmem {
   float red[NW];  // per-wave partial sums (residual + RMSNorm epilogue)
   // followed by the slice's slots (int32, 16-byte aligned)
 };
+
+// The lane index computed afresh (two VALU operations, no input), for
+// per-lane addresses used once per tile: nothing derived from the lane then
+// stays live across the tile loop.
+__device__ __forceinline__ int lane_fresh() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
 
 // 16 e4m3fn codes times one scale -> 16 bf16 (round to nearest even)
 __device__ __forceinline__ void dequant16(const v4i c, float sc, v4i& lo, v4i& hi) {
@@ -206,7 +217,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
       // rope units: wave-load j covers rope-region units 64j + lane (the two
       // padding units of a slot get a harmless valid unit)
       for (int j = wave; j < ROPE_LOADS; j += NW) {
-        const uint32_t u = 64 * j + lane;
+        const uint32_t u = 64 * j + lane_fresh();
         const uint32_t ps = u / B_STRIDE, c = u - ps * B_STRIDE;
         int slot = sidx[ti * TILE_ROWS + slot_row(ps)];
         slot = slot < 0 ? 0 : slot;
@@ -259,16 +270,31 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
     // (value region for k-steps 0..15, rope region for 16 and 17)
     const unsigned char* la0 = st + 16 * (A_STRIDE * n16 + g4);  // slot n16
     const unsigned char* lb0 = st + 16 * (B_UNIT0 + B_STRIDE * n16 + g4);
-#pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
+    // A operands read LDS_AHEAD k-steps ahead of their MFMAs, so the LDS
+    // latency is hidden behind the MFMAs of the steps in between
+    v4i ar[LDS_AHEAD + 1][2];
+    auto read_a = [&](int ks, v4i* a) {
       const unsigned char* a0p = ks < 16 ? la0 + 64 * ks : lb0 + 64 * (ks - 16);
       const unsigned char* a1p = a0p + 16 * 16 * (ks < 16 ? A_STRIDE : B_STRIDE);  // slot 16 + n16
-      const v4i a0 = *reinterpret_cast<const v4i*>(a0p);
-      const v4i a1 = *reinterpret_cast<const v4i*>(a1p);
-      acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a0), __builtin_bit_cast(v8bf, qb[ks]),
+      a[0] = *reinterpret_cast<const v4i*>(a0p);
+      a[1] = *reinterpret_cast<const v4i*>(a1p);
+    };
+#pragma unroll
+    for (int ks = 0; ks < LDS_AHEAD; ++ks) read_a(ks, ar[ks]);
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) {
+      if (ks + LDS_AHEAD < 18) read_a(ks + LDS_AHEAD, ar[(ks + LDS_AHEAD) % (LDS_AHEAD + 1)]);
+      const v4i* a = ar[ks % (LDS_AHEAD + 1)];
+      acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[0]), __builtin_bit_cast(v8bf, qb[ks]),
                                                        acc[0], 0, 0, 0);
-      acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a1), __builtin_bit_cast(v8bf, qb[ks]),
+      acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[1]), __builtin_bit_cast(v8bf, qb[ks]),
                                                        acc[1], 0, 0, 0);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) {
+      if (ks == 0) __builtin_amdgcn_sched_group_barrier(0x100, 2 * LDS_AHEAD, 0);
+      if (ks + LDS_AHEAD < 18) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
     // ---- online softmax: this lane holds head hq, rows 8*g4 + 4*mt + i
     {
@@ -304,7 +330,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
       l_run = l_run * a_ + lsum;
       m_run = m_new;
       *reinterpret_cast<v4i*>(&sm.pt[ti & 1][hq][8 * g4]) = __builtin_bit_cast(v4i, pv);
-      if (g4 == 0) sm.alpha[ti & 1][hq] = a_;
+      if (g4 == 0) sm.alpha[ti & 1][wave * 16 + (lane_fresh() & 15)] = a_;
     }
   };
   // O^T += C^T P^T of tile ti for this wave's value slice, from the bf16 tile at st
@@ -339,12 +365,22 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
             (__attribute__((address_space(3))) v4s*)(tb + 16 * 16 * A_STRIDE + 32 * vt));  // row + 4: slot + 16
         av[vt] = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
+      // P^T of head tile nt+1 is read while the MFMAs of tile nt issue
+      v4i pbr[2];
+      pbr[0] = *reinterpret_cast<const v4i*>(&sm.pt[ti & 1][n16][8 * g4]);
 #pragma unroll
       for (int nt = 0; nt < NW; ++nt) {
-        const v4i pb = *reinterpret_cast<const v4i*>(&sm.pt[ti & 1][16 * nt + n16][8 * g4]);
+        if (nt + 1 < NW) pbr[(nt + 1) & 1] = *reinterpret_cast<const v4i*>(&sm.pt[ti & 1][16 * (nt + 1) + n16][8 * g4]);
+        const v4i pb = pbr[nt & 1];
 #pragma unroll
         for (int vt = 0; vt < VT; ++vt)
           o[vt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[vt], __builtin_bit_cast(v8bf, pb), o[vt][nt], 0, 0, 0);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NW; ++nt) {
+        if (nt == 0) __builtin_amdgcn_sched_group_barrier(0x100, 2 * VT + 1, 0);
+        if (nt + 1 < NW) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, VT, 0);
       }
     }
   };
