@@ -196,34 +196,35 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
   const int first_u = (wave * LMIN + min(wave, LEXTRA)) * 64 + lane;
   const int r_first = first_u / RUNITS;
   const int c_first = first_u - r_first * RUNITS;
+  // bf16 rows: the DMA loads of tile ti into gather stage stage_i
+  auto issue_tile_bf16 = [&](int stage_i, int ti) {
+    const uint32_t st_lds = uniform((uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)sm.stage[stage_i]);
+    // value units: one wave-load per row (lane i: unit i), from a uniform row
+    // address, so the address arithmetic is scalar
+#pragma unroll
+    for (int i0 = 0; i0 < RPW; i0 += 4) {
+      // this wave's next 4 rows (4 consecutive row slots): slots in one read
+      const v4i sl = *reinterpret_cast<const v4i*>(&sidx[ti * TILE_ROWS + RPW * wave + i0]);
+      const uint32_t lds0 = uniform(st_lds + 16 * A_STRIDE * row_slot(RPW * wave + i0));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int slot = max(__builtin_amdgcn_readfirstlane(sl[i]), 0);  // absent rows: a harmless valid row
+        dma16_to_lds_saddr(p.kv + (int64_t)slot * LATENT, 16 * lane, lds0 + 16 * A_STRIDE * i);
+      }
+    }
+    // rope units: wave-load j covers rope-region units 64j + lane (the two
+    // padding units of a slot get a harmless valid unit)
+    for (int j = wave; j < ROPE_LOADS; j += NW) {
+      const uint32_t u = 64 * j + lane_fresh();
+      const uint32_t ps = u / B_STRIDE, c = u - ps * B_STRIDE;
+      const int slot = max(sidx[ti * TILE_ROWS + slot_row(ps)], 0);
+      dma16_to_lds(p.kv + (int64_t)slot * LATENT + 512 + 8 * (c < 8 ? c : 0), uniform(st_lds + 16 * (B_UNIT0 + 64 * j)));
+    }
+  };
   auto issue_tile = [&](int ti) {
     unsigned char* st = sm.stage[ti % NSTAGE];
     const uint32_t st_lds = uniform((uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)st);
-    if constexpr (!KV8) {
-      // value units: one wave-load per row (lane i: unit i), from a uniform
-      // row address, so the address arithmetic is scalar
-#pragma unroll
-      for (int i0 = 0; i0 < RPW; i0 += 4) {
-        // this wave's next 4 rows (4 consecutive row slots): slots in one read
-        const v4i sl = *reinterpret_cast<const v4i*>(&sidx[ti * TILE_ROWS + RPW * wave + i0]);
-        const uint32_t lds0 = uniform(st_lds + 16 * A_STRIDE * row_slot(RPW * wave + i0));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          int slot = __builtin_amdgcn_readfirstlane(sl[i]);
-          slot = slot < 0 ? 0 : slot;
-          dma16_to_lds_saddr(p.kv + (int64_t)slot * LATENT, 16 * lane, lds0 + 16 * A_STRIDE * i);
-        }
-      }
-      // rope units: wave-load j covers rope-region units 64j + lane (the two
-      // padding units of a slot get a harmless valid unit)
-      for (int j = wave; j < ROPE_LOADS; j += NW) {
-        const uint32_t u = 64 * j + lane_fresh();
-        const uint32_t ps = u / B_STRIDE, c = u - ps * B_STRIDE;
-        int slot = sidx[ti * TILE_ROWS + slot_row(ps)];
-        slot = slot < 0 ? 0 : slot;
-        dma16_to_lds(p.kv + (int64_t)slot * LATENT + 512 + 8 * (c < 8 ? c : 0), uniform(st_lds + 16 * (B_UNIT0 + 64 * j)));
-      }
-    } else {
+    if constexpr (KV8) {
       const int nl = LMIN + (wave < LEXTRA ? 1 : 0);
       const int first = wave * LMIN + min(wave, LEXTRA);
       int r = r_first, c = c_first;
@@ -246,7 +247,12 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
     }
   };
 
-  if (ntiles > 0) issue_tile(0);
+  if (ntiles > 0) {
+    if constexpr (!KV8)
+      issue_tile_bf16(0, 0);
+    else
+      issue_tile(0);
+  }
   // retire every plain global load here (tile 0 lands too), so no
   // compiler-inserted wait inside the tile loop can count (and drain) the row
   // DMA queue
@@ -268,8 +274,11 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
     v4f acc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
     // M-tile row n16 holds tile row 8*(n16/4) + 4*mt + n16%4; k-step ks adds 64 bytes
     // (value region for k-steps 0..15, rope region for 16 and 17)
-    const unsigned char* la0 = st + 16 * (A_STRIDE * n16 + g4);  // slot n16
-    const unsigned char* lb0 = st + 16 * (B_UNIT0 + B_STRIDE * n16 + g4);
+    // (per-lane offsets from a fresh lane index: nothing per lane stays live
+    // across the tile loop for them)
+    const int lf = lane_fresh();
+    const unsigned char* la0 = st + 16 * (A_STRIDE * (lf & 15) + (lf >> 4));  // slot n16
+    const unsigned char* lb0 = st + 16 * (B_UNIT0 + B_STRIDE * (lf & 15) + (lf >> 4));
     // A operands read LDS_AHEAD k-steps ahead of their MFMAs, so the LDS
     // latency is hidden behind the MFMAs of the steps in between
     v4i ar[LDS_AHEAD + 1][2];
@@ -297,7 +306,29 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
     // ---- online softmax: this lane holds head hq, rows 8*g4 + 4*mt + i
-    {
+    if (vmask == 0xffffffffu) {
+      // every row of the tile present (almost every tile): no masking, and
+      // the maximum (finite) is taken on the raw logits (the scale is positive)
+      float tm = fmaxf(fmaxf(fmaxf(acc[0][0], acc[0][1]), fmaxf(acc[0][2], acc[0][3])),
+                       fmaxf(fmaxf(acc[1][0], acc[1][1]), fmaxf(acc[1][2], acc[1][3])));
+      const float tmax = max_lane_groups(tm) * p.scale_log2;
+      const float m_new = (tmax > m_run + RESCALE_SLACK) ? tmax : m_run;
+      const float a_ = (m_new > m_run) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+      float lsum = 0.f;
+      __bf16 pv[8];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pr = __builtin_amdgcn_exp2f(fmaf(acc[mt][i], p.scale_log2, -m_new));
+          lsum += pr;
+          pv[4 * mt + i] = (__bf16)pr;
+        }
+      l_run = l_run * a_ + lsum;
+      m_run = m_new;
+      *reinterpret_cast<v4i*>(&sm.pt[ti & 1][hq][8 * g4]) = __builtin_bit_cast(v4i, pv);
+      if (g4 == 0) sm.alpha[ti & 1][wave * 16 + (lane_fresh() & 15)] = a_;
+    } else {
       float x[8];
       float tmax = -INFINITY;
 #pragma unroll
@@ -356,7 +387,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
     // (the rescale by alpha is pv_rescale, run before)
     {
       // transpose-read base: row 8*g4 + n16/4, column 16*(wave*VT) + 4*(n16%4); v tile vt adds 32 bytes
-      const unsigned char* tb = st + 16 * val_unit(8 * g4 + (n16 >> 2), wave * VT * 2) + 8 * (n16 & 3);
+      const int lf = lane_fresh();
+      const unsigned char* tb = st + 16 * val_unit(8 * (lf >> 4) + ((lf & 15) >> 2), wave * VT * 2) + 8 * (lf & 3);
       v8bf av[VT];
 #pragma unroll
       for (int vt = 0; vt < VT; ++vt) {
@@ -390,17 +422,21 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
     // tile ti-1 and the logits and softmax of tile ti (P^T and the rescale
     // factors are double-buffered).  The three gather stages hold tiles ti-1
     // (PV), ti (logits) and ti+1 (in flight), so gathers run one tile ahead.
+    int stg = 0;  // stage of tile ti
     for (int ti = 0; ti <= ntiles; ++ti) {
+      const int stg_prev = stg == 0 ? STAGES - 1 : stg - 1;
+      const int stg_next = stg == STAGES - 1 ? 0 : stg + 1;
       __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // tile ti, the only one in flight, has landed
       lds_barrier_keep_dma();  // and every wave has left iteration ti-1 (stage (ti+1)%3 is free)
       if (ti > 0) {
         pv_rescale(ti - 1);
-        pv(ti - 1, sm.stage[uniform((ti - 1) % STAGES)]);
+        pv(ti - 1, sm.stage[stg_prev]);
       }
       // the next tile's gather, issued after the PV (it lands during the
       // logits and the next PV)
-      if (ti + 1 < ntiles) issue_tile(ti + 1);
-      if (ti < ntiles) logits_softmax(ti, sm.stage[uniform(ti % STAGES)]);
+      if (ti + 1 < ntiles) issue_tile_bf16(stg_next, ti + 1);
+      if (ti < ntiles) logits_softmax(ti, sm.stage[stg]);
+      stg = stg_next;
     }
   } else {
     // FP8 rows, pipelined like the bf16 loop with one more barrier: once tile
