@@ -422,6 +422,11 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
     // tile ti-1 and the logits and softmax of tile ti (P^T and the rescale
     // factors are double-buffered).  The three gather stages hold tiles ti-1
     // (PV), ti (logits) and ti+1 (in flight), so gathers run one tile ahead.
+    // The two waves of a SIMD run the phases of an iteration in opposite
+    // orders (PV first, or logits first), so one's MFMAs overlap the other's
+    // softmax and gather issue; each order is its own loop (one loop with
+    // both orders inside spills).
+    if (wave < (NW + 1) / 2) {
     int stg = 0;  // stage of tile ti
     for (int ti = 0; ti <= ntiles; ++ti) {
       const int stg_prev = stg == 0 ? STAGES - 1 : stg - 1;
@@ -437,6 +442,22 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
       if (ti + 1 < ntiles) issue_tile_bf16(stg_next, ti + 1);
       if (ti < ntiles) logits_softmax(ti, sm.stage[stg]);
       stg = stg_next;
+    }
+    } else {
+    int stg = 0;  // stage of tile ti
+    for (int ti = 0; ti <= ntiles; ++ti) {
+      const int stg_prev = stg == 0 ? STAGES - 1 : stg - 1;
+      const int stg_next = stg == STAGES - 1 ? 0 : stg + 1;
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // tile ti, the only one in flight, has landed
+      lds_barrier_keep_dma();  // and every wave has left iteration ti-1 (stage (ti+1)%3 is free)
+      if (ti + 1 < ntiles) issue_tile_bf16(stg_next, ti + 1);
+      if (ti < ntiles) logits_softmax(ti, sm.stage[stg]);
+      if (ti > 0) {
+        pv_rescale(ti - 1);
+        pv(ti - 1, sm.stage[stg_prev]);
+      }
+      stg = stg_next;
+    }
     }
   } else {
     // FP8 rows, pipelined like the bf16 loop with one more barrier: once tile
