@@ -51,6 +51,7 @@ namespace dsa {
 
 constexpr int TILE_ROWS = 32;
 constexpr float RESCALE_SLACK = 8.f;  // log2 of the largest unnormalised probability
+constexpr float RESCALE_BOUND = 256.f;  // 2^RESCALE_SLACK
 constexpr int MLA_SMAX = 8;  // most splits of a query's index list (K / 256 for K <= 2048)
 constexpr int A_STRIDE = 66;                          // value region: units per row slot (64 + 2 padding)
 constexpr int B_UNIT0 = TILE_ROWS * A_STRIDE;         // rope region: first unit
@@ -307,25 +308,43 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
     }
     // ---- online softmax: this lane holds head hq, rows 8*g4 + 4*mt + i
     if (vmask == 0xffffffffu) {
-      // every row of the tile present (almost every tile): no masking, and
-      // the maximum (finite) is taken on the raw logits (the scale is positive)
-      float tm = fmaxf(fmaxf(fmaxf(acc[0][0], acc[0][1]), fmaxf(acc[0][2], acc[0][3])),
-                       fmaxf(fmaxf(acc[1][0], acc[1][1]), fmaxf(acc[1][2], acc[1][3])));
-      const float tmax = max_lane_groups(tm) * p.scale_log2;
-      const float m_new = (tmax > m_run + RESCALE_SLACK) ? tmax : m_run;
-      const float a_ = (m_new > m_run) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-      float lsum = 0.f;
-      __bf16 pv[8];
+      // every row of the tile present (almost every tile): no masking.  The
+      // probabilities are first taken against the running reference maximum
+      // (scale folded into the FMA that feeds the exponent); only if one of
+      // the wave's exceeds 2^RESCALE_SLACK (or the reference is still -inf)
+      // is the tile's maximum computed and the reference moved, so the
+      // maximum and its cross-lane reduction leave the common path.
+      float pr[8];
+      bool big = false;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pr = __builtin_amdgcn_exp2f(fmaf(acc[mt][i], p.scale_log2, -m_new));
-          lsum += pr;
-          pv[4 * mt + i] = (__bf16)pr;
+          pr[4 * mt + i] = __builtin_amdgcn_exp2f(fmaf(acc[mt][i], p.scale_log2, -m_run));
+          big |= !(pr[4 * mt + i] <= RESCALE_BOUND);
         }
+      float a_ = 1.f;
+      if (__builtin_amdgcn_ballot_w64(big)) {
+        // the maximum (finite) is taken on the raw logits (the scale is positive)
+        float tm = fmaxf(fmaxf(fmaxf(acc[0][0], acc[0][1]), fmaxf(acc[0][2], acc[0][3])),
+                         fmaxf(fmaxf(acc[1][0], acc[1][1]), fmaxf(acc[1][2], acc[1][3])));
+        const float tmax = max_lane_groups(tm) * p.scale_log2;
+        const float m_new = (tmax > m_run + RESCALE_SLACK) ? tmax : m_run;
+        a_ = (m_new > m_run) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pr[4 * mt + i] = __builtin_amdgcn_exp2f(fmaf(acc[mt][i], p.scale_log2, -m_new));
+        m_run = m_new;
+      }
+      float lsum = 0.f;
+      __bf16 pv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        lsum += pr[j];
+        pv[j] = (__bf16)pr[j];
+      }
       l_run = l_run * a_ + lsum;
-      m_run = m_new;
       *reinterpret_cast<v4i*>(&sm.pt[ti & 1][hq][8 * g4]) = __builtin_bit_cast(v4i, pv);
       if (g4 == 0) sm.alpha[ti & 1][wave * 16 + (lane_fresh() & 15)] = a_;
     } else {
