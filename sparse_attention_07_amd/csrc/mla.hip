@@ -24,10 +24,16 @@
 //    PV: wave w owns value dims [512w/NW, 512(w+1)/NW) for all heads and
 //    accumulates O^T += C^T P^T, reading C^T with the gfx950 LDS transpose
 //    read (ds_read_b64_tr_b16) and P^T with plain 16-byte reads;
+//  * the tile loop is software-pipelined with one barrier per tile (the PV
+//    of tile i-1 and the logits and softmax of tile i in one iteration); the
+//    two waves of a SIMD run those phases in opposite orders, and the logits'
+//    A operands are read two k-steps ahead of their MFMAs;
 //  * each head's reference maximum moves only when a tile's maximum exceeds
 //    it by more than 2^8 (probabilities stay below 256, exact in the end:
 //    O and l carry the same offset), so the O rescale is skipped for a wave
-//    unless some head's maximum jumped;
+//    unless some head's maximum jumped; on tiles whose rows are all present
+//    the probabilities are taken against the reference first and the tile
+//    maximum is computed only when one of them passes the bound;
 //  * with several splits, each split stores its normalised partial output
 //    O/l as bf16 (the latent cache's own range: |O/l| is bounded by the
 //    largest value entry) plus (m, l) in fp32, and a small kernel merges them
@@ -37,12 +43,13 @@
 //    several, the combine adds the residual and stores per-head sums of
 //    squares, and a small kernel applies the norm;
 //  * FP8 latent rows (656 B: e4m3fn nope, one fp32 scale per 128 dims, bf16
-//    rope) are gathered the same way into their own 3-stage ring (41 units per
-//    row instead of 72), then all waves dequantize the tile once into the bf16
-//    tile layout above (code * scale rounded to bf16), so the MFMA phases are
-//    the bf16 ones.  That saves 43 % of the gathered bytes and of the cache's
-//    footprint, but adds LDS traffic and a barrier per tile to a kernel whose
-//    logits phase is bound by LDS reads, so it runs slightly slower than bf16.
+//    rope) are gathered into a 2-stage ring of their own (41 sixteen-byte
+//    units per row, each lane stepping through the ring), then all waves
+//    dequantize the tile once into the bf16 tile layout above (code * scale
+//    rounded to bf16), so the MFMA phases are the bf16 ones.  That saves 43 %
+//    of the gathered bytes and of the cache's footprint, but the dequantization
+//    and its second barrier per tile sit on every tile's critical path, so it
+//    runs slower than bf16 rows.
 #include "dsa_device.h"
 #include "dsa_params.h"
 
