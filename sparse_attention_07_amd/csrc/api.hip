@@ -19,7 +19,7 @@ hipError_t launch_quantize_q(const void* q, int64_t rows, int D, int idx_dtype, 
 namespace {
 
 constexpr int MLA_TARGET_WGS = 256;
-constexpr int MLA_MIN_ROWS = 256;
+constexpr int MLA_MIN_ROWS = 32;
 constexpr int MLA_MAX_SPLITS = 8;
 constexpr int64_t KEYSPACE_MAX_PAGES = (int64_t)1 << 30;
 
