@@ -229,7 +229,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
       dma16_to_lds(p.kv + (int64_t)slot * LATENT + 512 + 8 * (c < 8 ? c : 0), uniform(st_lds + 16 * (B_UNIT0 + 64 * j)));
     }
   };
-  auto issue_tile = [&](int ti) {
+  auto issue_tile_fp8 = [&](int ti) {  // FP8 rows: the DMA loads of tile ti
     unsigned char* st = sm.stage[ti % NSTAGE];
     const uint32_t st_lds = uniform((uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)st);
     if constexpr (KV8) {
@@ -259,7 +259,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
     if constexpr (!KV8)
       issue_tile_bf16(0, 0);
     else
-      issue_tile(0);
+      issue_tile_fp8(0);
   }
   // retire every plain global load here (tile 0 lands too), so no
   // compiler-inserted wait inside the tile loop can count (and drain) the row
@@ -520,7 +520,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
     for (int ti = 0; ti <= ntiles; ++ti) {
       __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // tile ti, the only one in flight, has landed
       lds_barrier_keep_dma();  // every wave has left iteration ti-1: bf16 tile ti&1 and stage (ti+1)%2 are free
-      if (ti + 1 < ntiles) issue_tile(ti + 1);
+      if (ti + 1 < ntiles) issue_tile_fp8(ti + 1);
       if (ti < ntiles) dequant(ti);
       lds_barrier_keep_dma();  // bf16 tile ti is complete
       if (ti > 0) {
