@@ -186,6 +186,24 @@ def test_mla_null_and_workspace():
     assert dsa.workspace_bytes(None, good_mla(T=1000, **ep), 2048) == dsa.workspace_bytes(None, good_mla(T=1000), 2048)
 
 
+@pytest.mark.parametrize("T,H,K,splits", [
+    (64, 128, 2048, 4),   # the 128K decode batch: 256 workgroups
+    (32, 128, 2048, 8),   # 32 queries: 8 splits of 256 rows
+    (11, 128, 2048, 8),   # at most 8 splits (the combine's width)
+    (1, 16, 256, 8),      # a short list splits down to one 32-row tile per workgroup
+    (1, 16, 100, 2),      # 100 rows: 3 splits asked for, 64-row (two-tile) splits give 2
+    (1, 16, 40, 1),       # under two tiles: one split
+    (4096, 128, 2048, 1), # a prefill chunk: one workgroup per query, no partials
+])
+def test_mla_split_count_sizes_the_partials(T, H, K, splits):
+    # with S > 1 splits the workspace holds bf16 partials [T][S][H][512] and
+    # fp32 (m, l) pairs [T][S][H][2], each region 256-byte aligned
+    def align(n):
+        return (n + 255) // 256 * 256
+    want = 0 if splits == 1 else align(T * splits * H * 512 * 2) + align(T * splits * H * 2 * 4)
+    assert dsa.workspace_bytes(None, good_mla(T=T, H=H), K) == want
+
+
 def test_layer_argument_errors():
     def call(a, m, out=_base, ws=None, ws_bytes=0, idx_out=None):
         return dsa.LIB.dsa_layer(ctypes.byref(a), ctypes.byref(m), 2048, 0.04, idx_out, out, ws, ws_bytes, None)
