@@ -55,6 +55,7 @@
 
 
 namespace dsa {
+typedef int v2i __attribute__((ext_vector_type(2)));  // 8-byte streaming stores
 
 constexpr int TILE_ROWS = 32;
 constexpr float RESCALE_SLACK = 8.f;  // log2 of the largest unnormalised probability
@@ -66,6 +67,7 @@ constexpr int B_STRIDE = 10;                          // rope region: units per 
 constexpr int ROPE_LOADS = (TILE_ROWS * B_STRIDE + 63) / 64;  // 5 wave-loads
 constexpr int PT_STRIDE = TILE_ROWS + 16;             // P^T row (bf16): 6 sixteen-byte units
 constexpr int STAGES = 3;
+constexpr int OB_STRIDE = VDIM * 2 + 16;                // O row (bf16) staged in LDS for the store
 constexpr int LDS_AHEAD = 2;  // logits: k-steps of A operands read ahead (3 needs more registers than a wave has)
 constexpr int STAGE_BYTES = (B_UNIT0 + ROPE_LOADS * 64) * 16;  // 38,912 B
 
@@ -175,17 +177,20 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
   const int ntiles = (nrows + TILE_ROWS - 1) / TILE_ROWS;
 
   // ---- the slice's pool slots (invalid -> -1), and q of this wave's 16 heads
-  // as the logits B operand (k = latent dim).  The first NT slots are loaded
-  // before q, so the first tile's gather can start while q is in flight.
-  auto slot_of = [&](int i) {
-    int v = -1;
-    if (i < nrows) {
-      v = p.indices[(int64_t)t * p.K + r_begin + i];
-      if (v < 0 || (int64_t)v >= p.num_slots) v = -1;
-    }
-    return v;
-  };
-  const int v0 = slot_of(tid);
+  // as the logits B operand (k = latent dim).  Every slot load is issued
+  // before q, unconditionally (a slice holds at most KMAX rows; indices past
+  // the slice are clamped and their values masked afterwards), so no branch
+  // and no wait for q sits in front of the first tile's gather: it starts
+  // while q is still in flight.
+  constexpr int SPT = KMAX / NT;  // slot loads per thread
+  const int32_t* irow = p.indices + (int64_t)t * p.K;
+  const int ncap = ntiles * TILE_ROWS;  // slot entries; entry ncap takes the writes past them
+  int sv[SPT];
+#pragma unroll
+  for (int k = 0; k < SPT; ++k) sv[k] = irow[min(r_begin + min(tid + k * NT, max(nrows - 1, 0)), p.K - 1)];
+  // every wave's slot loads enter the memory pipeline before any q load (the
+  // q loads of the other waves would otherwise queue in front of them)
+  asm volatile("s_barrier" ::: "memory");
   const int hq = wave * 16 + n16;
   v4i qb[18];
   {
@@ -193,8 +198,12 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) qb[ks] = *reinterpret_cast<const v4i*>(qrow + 32 * ks + 8 * g4);
   }
-  if (tid < ntiles * TILE_ROWS) sidx[tid] = v0;
-  for (int i = tid + NT; i < ntiles * TILE_ROWS; i += NT) sidx[i] = slot_of(i);
+#pragma unroll
+  for (int k = 0; k < SPT; ++k) {
+    const int i = tid + k * NT;
+    const int v = sv[k];
+    sidx[i < ncap ? i : ncap] = (i < nrows && v >= 0 && (int64_t)v < p.num_slots) ? v : -1;
+  }
   lds_barrier();
 
   constexpr int NSTAGE = MlaSmem<NW, KV8>::NSTAGE;
@@ -592,31 +601,35 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
     }
     return;
   }
+  // O / l as bf16 rows [head][512] in LDS, over the gather ring and P^T (every
+  // wave is past its last read of them: the barrier above), then written out
+  // one 1 KB row per wave instruction (16 bytes per lane, whole lines), where
+  // the accumulator layout would give each store 32-byte pieces of 16 rows.
+  // The stores stream (nontemporal): the rows are read once, by the combine
+  // or the caller, and do not stay in the L2 as dirty lines that the next
+  // kernels (the next layer step's indexer) would have to write back.
+  using SmT = MlaSmem<NW, KV8>;
+  static_assert(__builtin_offsetof(SmT, mfin) >= (size_t)H * OB_STRIDE, "O rows fit below mfin");
 #pragma unroll
   for (int nt = 0; nt < NW; ++nt) {
     const int h = 16 * nt + n16;
     const float l_tot = sm.lfin[h];
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (p.S == 1) {
-      uint16_t* orow = p.out + ((int64_t)t * H + h) * VDIM;
 #pragma unroll
-      for (int vt = 0; vt < VT; ++vt) {
-        __bf16 b4[4];
+    for (int vt = 0; vt < VT; ++vt) {
+      __bf16 b4[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) b4[i] = (__bf16)(o[vt][nt][i] * inv);
-        *reinterpret_cast<uint2*>(orow + (wave * VT + vt) * 16 + 4 * g4) = __builtin_bit_cast(uint2, b4);
-      }
-    } else {
-      const int64_t rowi = ((int64_t)t * p.S + s) * H + h;
-      uint16_t* prow = p.part_o + rowi * VDIM;
-#pragma unroll
-      for (int vt = 0; vt < VT; ++vt) {
-        __bf16 h4[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) h4[i] = (__bf16)(o[vt][nt][i] * inv);
-        *reinterpret_cast<uint2*>(prow + (wave * VT + vt) * 16 + 4 * g4) = __builtin_bit_cast(uint2, h4);
-      }
+      for (int i = 0; i < 4; ++i) b4[i] = (__bf16)(o[vt][nt][i] * inv);
+      *reinterpret_cast<uint2*>(smem_raw + h * OB_STRIDE + 2 * ((wave * VT + vt) * 16 + 4 * g4)) =
+          __builtin_bit_cast(uint2, b4);
     }
+  }
+  lds_barrier();
+  {
+    uint16_t* dst = p.S == 1 ? p.out + (int64_t)t * H * VDIM : p.part_o + ((int64_t)t * p.S + s) * H * VDIM;
+    for (int h = wave; h < H; h += NW)
+      __builtin_nontemporal_store(*reinterpret_cast<const v4i*>(smem_raw + h * OB_STRIDE + 16 * lane),
+                                  reinterpret_cast<v4i*>(dst + (int64_t)h * VDIM + 8 * lane));
   }
   if (p.S > 1 && tid < H) {
     const int64_t rowi = ((int64_t)t * p.S + s) * H + tid;
@@ -636,7 +649,8 @@ __global__ __launch_bounds__(256) void dsa_mla_combine_kernel(MlaParams p) {
   const int t = (int)(th / p.H), h = (int)(th % p.H);
   const int v = (threadIdx.x & 63) * 8;
   // every split's (m, l) and partial row in one round of loads (splits past S
-  // repeat the last one and get weight 0), then the weights
+  // repeat the last one and get weight 0), then the weights.  Partial rows are
+  // read once and the output rows written once: both stream (nontemporal).
   float ms[SM], ls[SM];
   uint4 raw[SM];
 #pragma unroll
@@ -644,7 +658,7 @@ __global__ __launch_bounds__(256) void dsa_mla_combine_kernel(MlaParams p) {
     const int64_t rowi = ((int64_t)t * p.S + min(s, p.S - 1)) * p.H + h;
     ms[s] = p.part_ml[rowi * 2];
     ls[s] = p.part_ml[rowi * 2 + 1];
-    raw[s] = *reinterpret_cast<const uint4*>(p.part_o + rowi * VDIM + v);
+    raw[s] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p.part_o + rowi * VDIM + v)));
   }
   float M = -INFINITY;
 #pragma unroll
@@ -671,8 +685,8 @@ __global__ __launch_bounds__(256) void dsa_mla_combine_kernel(MlaParams p) {
     for (int i = 0; i < 8; ++i) b8[i] = (__bf16)(acc[i] * inv);
     uint2* o2 = reinterpret_cast<uint2*>(p.out + th * VDIM + v);  // the output is 8-byte aligned
     const uint4 u = __builtin_bit_cast(uint4, b8);
-    o2[0] = make_uint2(u.x, u.y);
-    o2[1] = make_uint2(u.z, u.w);
+    __builtin_nontemporal_store(v2i{(int)u.x, (int)u.y}, reinterpret_cast<v2i*>(o2));
+    __builtin_nontemporal_store(v2i{(int)u.z, (int)u.w}, reinterpret_cast<v2i*>(o2 + 1));
     return;
   }
   // residual epilogue: store y = attn + residual (bf16) and this head's sum of
@@ -722,7 +736,7 @@ __global__ __launch_bounds__(256) void dsa_mla_norm_kernel(MlaParams p) {
 template <int NW, bool KV8>
 static size_t mla_smem_t(int rows_per_split) {
   const int tiles = (rows_per_split + TILE_ROWS - 1) / TILE_ROWS;
-  return sizeof(MlaSmem<NW, KV8>) + (size_t)tiles * TILE_ROWS * 4;
+  return sizeof(MlaSmem<NW, KV8>) + (size_t)(tiles * TILE_ROWS + 4) * 4;  // + the spare entry
 }
 
 
