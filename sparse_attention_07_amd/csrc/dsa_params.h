@@ -60,7 +60,7 @@ struct MlaParams {
   int32_t rows_per_split;   // multiple of 32
   float scale_log2;         // softmax scale * log2(e)
   uint16_t* out;            // [T][H][512] bf16
-  uint16_t* part_o;         // [T][S][H][512] bf16, normalised O/l of each split (S > 1)
+  uint16_t* part_o;         // [T][S][H][512] bf16, unnormalised O of each split (S > 1)
   float* part_ml;           // [T][S][H][2]   fp32 (S > 1)
   // residual + RMSNorm epilogue (residual == nullptr: none)
   const uint16_t* residual; // [T][H][512] bf16

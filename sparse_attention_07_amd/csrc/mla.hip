@@ -34,10 +34,11 @@
 //    unless some head's maximum jumped; on tiles whose rows are all present
 //    the probabilities are taken against the reference first and the tile
 //    maximum is computed only when one of them passes the bound;
-//  * with several splits, each split stores its normalised partial output
-//    O/l as bf16 (the latent cache's own range: |O/l| is bounded by the
-//    largest value entry) plus (m, l) in fp32, and a small kernel merges them
-//    with log-sum-exp weights;
+//  * with several splits, each split stores its partial output O, not yet
+//    divided by l, as bf16 (probabilities below 2^8 over at most 2048 rows:
+//    |O| stays within 2^19 times the largest value entry, far inside bf16's
+//    range), plus (m, l) in fp32, and a small kernel merges them with
+//    log-sum-exp weights and divides once;
 //  * optional residual + RMSNorm epilogue over the token's H x 512 values: with
 //    one split the workgroup holds the whole token and finishes it; with
 //    several, the combine adds the residual and stores per-head sums of
@@ -610,11 +611,13 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
   // kernels (the next layer step's indexer) would have to write back.
   using SmT = MlaSmem<NW, KV8>;
   static_assert(__builtin_offsetof(SmT, mfin) >= (size_t)H * OB_STRIDE, "O rows fit below mfin");
+  // (a split's partial is O itself, unnormalised: the combine weighs it by
+  // exp2(m - M) and divides by the weighted sum of the l)
 #pragma unroll
   for (int nt = 0; nt < NW; ++nt) {
     const int h = 16 * nt + n16;
     const float l_tot = sm.lfin[h];
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float inv = p.S > 1 ? 1.f : (l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.f);
 #pragma unroll
     for (int vt = 0; vt < VT; ++vt) {
       __bf16 b4[4];
@@ -638,8 +641,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
   }
 }
 
-// Merge S partial results per (query, head), with O_s = l_s * (O/l)_s:
-// out = sum_s e^(m_s-M) l_s (O/l)_s / sum_s e^(m_s-M) l_s.
+// Merge S partial results per (query, head), each split's unnormalised O_s
+// with its (m_s, l_s): out = sum_s e^(m_s-M) O_s / sum_s e^(m_s-M) l_s.
 // A workgroup covers 4 (query, head) rows (one wave each, 8 values per lane);
 // H is a multiple of 4.  SM >= S: the splits loaded per row (4 when S <= 4,
 // so no load repeats a split).
@@ -668,8 +671,8 @@ __global__ __launch_bounds__(256) void dsa_mla_combine_kernel(MlaParams p) {
   if (M != -INFINITY) {
 #pragma unroll
     for (int s = 0; s < SM; ++s) {
-      const float wgt = (s < p.S && ms[s] != -INFINITY) ? exp2f(ms[s] - M) * ls[s] : 0.f;
-      L += wgt;
+      const float wgt = (s < p.S && ms[s] != -INFINITY) ? exp2f(ms[s] - M) : 0.f;
+      L += wgt * ls[s];
       const uint32_t rw[4] = {raw[s].x, raw[s].y, raw[s].z, raw[s].w};  // 8 bf16
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
