@@ -16,7 +16,9 @@ exceed the MFMA ridge, as in chunked prefill, its FP8 / bf16 MFMA flops
 against the dense MFMA peak), plus `layer_frac_hbm`, the whole step's
 algorithmic bytes (indexer + Top-K + sparse MLA) over its time against 8 TB/s;
 `cpu_baseline` is the CPU oracle timed on a bounded sample of the same
-workload.
+workload.  Before the W warm-up steps, untimed steps run for at least
+--settle-ms of wall time (`settle_steps` in the line), so the K timed steps
+start from the GPU's steady state under the layer's load, not from idle.
 """
 from __future__ import annotations
 
@@ -40,6 +42,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="untimed steps for at least this long before the warm-up steps, so the timed steps "
+                         "start from the GPU's steady state under this load rather than from idle")
     ap.add_argument("--workload", default="decode_b64_128k_fp8")
     ap.add_argument("--op", choices=("layer", "quantize"), default="layer",
                     help="layer: the DSA layer step (default); quantize: the index-query quantization that "
@@ -229,6 +234,8 @@ def bench_quantize(args, spec, case):
     ins = [src.clone() for _ in range(ncopy)]
     outs = [dsa.quantize_index_q(x, dt) for x in ins]
     stream = torch.cuda.current_stream()
+    n_settle = settle(lambda i: dsa.quantize_index_q(ins[i % ncopy], dt, codes=outs[i % ncopy][0],
+                                                     scales=outs[i % ncopy][1]), args.settle_ms)
     for i in range(args.warmup):
         dsa.quantize_index_q(ins[i % ncopy], dt, codes=outs[i % ncopy][0], scales=outs[i % ncopy][1])
     torch.cuda.synchronize()
@@ -249,6 +256,7 @@ def bench_quantize(args, spec, case):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": n_settle,
         "ms_per_step": round(wall / args.steps * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -267,6 +275,23 @@ def bench_quantize(args, spec, case):
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = quant_cpu_baseline(src, kind, spec.name)
     print(json.dumps(line), flush=True)
+
+
+def settle(run, ms):
+    """Run ``run(i)`` untimed, four calls per synchronisation, for at least
+    ``ms`` milliseconds of wall time; returns the number of calls.  From idle,
+    the first few milliseconds of steps run slower (the 128K decode step: 0.270
+    ms per step over 20 steps after 5 warm-up steps, 0.254 ms after 100), so
+    the timed steps start from the steady state a serving loop runs in."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(4):
+            run(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
 
 
 def copy_bandwidth(dev, nbytes=2 << 30, reps=5):
@@ -342,6 +367,7 @@ def main():
         for lay in layers[i % len(layers)]:
             lay()
 
+    n_settle = settle(step, args.settle_ms)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -458,6 +484,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": n_settle,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",

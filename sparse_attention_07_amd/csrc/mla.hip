@@ -189,9 +189,6 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_mla_split_kernel(MlaParams p) 
   int sv[SPT];
 #pragma unroll
   for (int k = 0; k < SPT; ++k) sv[k] = irow[min(r_begin + min(tid + k * NT, max(nrows - 1, 0)), p.K - 1)];
-  // every wave's slot loads enter the memory pipeline before any q load (the
-  // q loads of the other waves would otherwise queue in front of them)
-  asm volatile("s_barrier" ::: "memory");
   const int hq = wave * 16 + n16;
   v4i qb[18];
   {
