@@ -390,13 +390,16 @@ def main():
         parts = []
         for c, lay in zip(cs, lays):
             idx_out = torch.empty(c.T, spec.K, dtype=torch.int32, device=dev)
-            ws = torch.empty(max(256, dsa.workspace_bytes(lay.idx, None, spec.K)), dtype=torch.uint8, device=dev)
+            ws = dsa.workspace_init(torch.empty(max(256, dsa.workspace_bytes(lay.idx, None, spec.K)),
+                                                dtype=torch.uint8, device=dev))
+            mws = dsa.workspace_init(torch.empty(max(256, dsa.workspace_bytes(None, lay.mla, spec.K)),
+                                                 dtype=torch.uint8, device=dev))
             out = torch.empty_like(lay.out)
-            parts.append((c, idx_out, ws, out))
+            parts.append((c, idx_out, ws, mws, out))
         splits.append(parts)
 
     def run_split(i, ev=None):
-        for j, (c, idx_out, ws, out) in enumerate(splits[i % len(splits)]):
+        for j, (c, idx_out, ws, mws, out) in enumerate(splits[i % len(splits)]):
             if ev is not None:
                 ev[j][0].record(stream)
             dsa.indexer_topk(c.q_idx, c.w, c.k_idx_pool, c.block_table, c.seq_lens, spec.K,
@@ -404,7 +407,7 @@ def main():
                              max_q_per_seq=c.max_q_per_seq, out=idx_out, workspace=ws)
             if ev is not None:
                 ev[j][1].record(stream)
-            dsa.sparse_mla_attn(c.q, c.kv_pool, idx_out, spec.scale, out=out, **ep_for(c))
+            dsa.sparse_mla_attn(c.q, c.kv_pool, idx_out, spec.scale, out=out, workspace=mws, **ep_for(c))
             if ev is not None:
                 ev[j][2].record(stream)
 
@@ -420,7 +423,7 @@ def main():
 
     # the indexer alone, back to back (context: no attention kernels between)
     def run_indexer(i):
-        for c, idx_out, ws, _ in splits[i % len(splits)]:
+        for c, idx_out, ws, _, _ in splits[i % len(splits)]:
             dsa.indexer_topk(c.q_idx, c.w, c.k_idx_pool, c.block_table, c.seq_lens, spec.K,
                              q_idx_scale=c.q_idx_scale, q_seq=c.q_seq, q_visible=c.q_visible,
                              max_q_per_seq=c.max_q_per_seq, out=idx_out, workspace=ws)

@@ -21,7 +21,11 @@
  *     call only.
  *   - Every buffer is owned by the caller.  The library never allocates device
  *     memory; scratch comes from the caller's workspace (`ws`, `ws_bytes`),
- *     sized by dsa_workspace_bytes().  The workspace needs no initialisation.
+ *     sized by dsa_workspace_bytes().  A workspace's first
+ *     DSA_WS_RESERVED_BYTES hold the Top-K merges' arrival counters: they must
+ *     be zero before the workspace's first use (dsa_workspace_init, or any
+ *     zero fill), and every call leaves them zero again.  The rest needs no
+ *     initialisation.
  *   - Calls enqueue work on `stream` (a hipStream_t; NULL = the null stream),
  *     never synchronise, and keep no mutable global state.  Two calls that share
  *     a workspace must be ordered on one stream.
@@ -68,13 +72,14 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 7
+#define DSA_ABI_VERSION 8
 #define DSA_PAGE_TOKENS 64
 #define DSA_LATENT_DIM 576
 #define DSA_VALUE_DIM 512
 #define DSA_MAX_K 2048
 #define DSA_MAX_INDEX_HEADS 64
 #define DSA_STATIC_SCRATCH_BYTES ((size_t)64 << 20) /* dsa_layer_static's scratch per GPU */
+#define DSA_WS_RESERVED_BYTES ((size_t)32768)       /* counter region at the start of a workspace */
 
 typedef enum dsa_status {
   DSA_OK = 0,
@@ -193,8 +198,17 @@ typedef struct dsa_mla_args {
 
 /* Bytes of workspace the call needs.  Pass NULL for the struct a call does not
  * use (dsa_indexer_topk: mla = NULL; dsa_sparse_mla_attn: idx = NULL).  Returns
- * 0 when the arguments are invalid (the call itself reports why). */
+ * 0 when the arguments are invalid (the call itself reports why), and for an
+ * attention call that needs no workspace.  Every non-zero size includes the
+ * counter region, DSA_WS_RESERVED_BYTES. */
 size_t dsa_workspace_bytes(const dsa_indexer_args* idx, const dsa_mla_args* mla, int K);
+
+/* Prepares a new workspace: enqueues on `stream` a kernel that zeroes its first
+ * min(ws_bytes, DSA_WS_RESERVED_BYTES) bytes, the counter region.  Needed once
+ * per workspace, before its first call (calls leave the region zero).
+ * ws: device, 256-byte aligned (DSA_ERR_ALIGN); NULL only with ws_bytes == 0
+ * (DSA_ERR_NULL), which enqueues nothing. */
+dsa_status dsa_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Steps 1+2.  Writes indices_out[T][K] (int32 device): for each query the
@@ -250,9 +264,10 @@ dsa_status dsa_layer(const dsa_indexer_args* idx, const dsa_mla_args* mla, int K
  *   needs more than that (dsa_workspace_bytes(idx, mla, K) bytes: the five
  *   workloads of the pages' model need at most about 49 MiB on a 256-CU GPU).
  *   Every call on one GPU shares that GPU's array, which keeps the last call's
- *   contents (the call clears what must start at zero itself): calls that
- *   overlap on one GPU (different streams, or threads without ordering) race
- *   and must be serialised by the caller.  The device is the current one.
+ *   contents (the first call on a GPU clears the array's counter region with a
+ *   kernel on its stream; every call leaves it clear): calls that overlap on
+ *   one GPU (different streams, or threads without ordering) race and must be
+ *   serialised by the caller.  The device is the current one.
  */
 dsa_status dsa_layer_static(const dsa_indexer_args* idx, const dsa_mla_args* mla, int K, float scale,
                             int32_t* indices_out, void* out, void* stream);

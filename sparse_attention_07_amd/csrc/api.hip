@@ -15,6 +15,7 @@ hipError_t launch_indexer(const IdxParams& p, int idx_dtype, int D, int grid, hi
 hipError_t launch_mla(const MlaParams& p, hipStream_t st);
 hipError_t launch_quantize_q(const void* q, int64_t rows, int D, int idx_dtype, void* codes, void* scales,
                              hipStream_t st);
+hipError_t launch_clear_counters(void* ws, size_t bytes, hipStream_t st);
 
 namespace {
 
@@ -22,6 +23,16 @@ constexpr int MLA_TARGET_WGS = 256;
 constexpr int MLA_MIN_ROWS = 32;
 constexpr int MLA_MAX_SPLITS = 8;
 constexpr int64_t KEYSPACE_MAX_PAGES = (int64_t)1 << 30;
+// The workspace's counter region (its first DSA_WS_RESERVED_BYTES): the list
+// merges' arrival counters, which every call leaves clear, at fixed offsets so
+// that calls of any shape sharing a workspace agree on them.  Run counters:
+// one per candidate-list slot, at most 2 * MQ * nwg <= 4 * NWG_MAX; per-query
+// counters of calls with at most SMALL_T queries after them.
+constexpr int NWG_MAX = 1024;
+constexpr int SMALL_T = 64;  // calls with at most this many queries plan inside the indexer
+constexpr size_t RES_RUN = 0;
+constexpr size_t RES_MDONE = (size_t)4 * NWG_MAX * 4;
+static_assert(RES_MDONE + SMALL_T * 4 <= DSA_WS_RESERVED_BYTES, "counter region");
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -90,12 +101,12 @@ int device_cus() {
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
     n = 256;
-  return n;
+  return std::min(n, NWG_MAX);
 }
 
 // nwg: indexer workgroups (one per CU); the workspace depends on it, so the
 // same value must be used for sizing and for the call.
-IdxPlan plan_indexer(const dsa_indexer_args* a, int K, size_t base, int nwg) {
+IdxPlan plan_indexer(const dsa_indexer_args* a, int K, int nwg) {
   IdxPlan pl;
   // Adjacent queries of one sequence are scored in pairs, sharing each key
   // load, only when there are many of them (chunked prefill).  For a handful of
@@ -114,7 +125,7 @@ IdxPlan plan_indexer(const dsa_indexer_args* a, int K, size_t base, int nwg) {
   const int64_t max_total = T * (std::max<int64_t>(16, (maxlen + 15) & ~15) + SEG_COST);
   pl.need_merge = max_total - SEG_COST > MIN_SLICE;
   pl.lists = pl.need_merge ? (int64_t)2 * pl.MQ * nwg : 0;
-  size_t off = align_up(base, 256);
+  size_t off = DSA_WS_RESERVED_BYTES;
   pl.off_hdr = off;
   off = align_up(off + 64, 256);
   pl.off_groups = off;
@@ -131,8 +142,7 @@ IdxPlan plan_indexer(const dsa_indexer_args* a, int K, size_t base, int nwg) {
   off = align_up(off + (size_t)pl.lists * K * 4, 256);
   pl.off_lpos = off;
   off = align_up(off + (size_t)pl.lists * K * 4, 256);
-  pl.off_run = off;
-  off = align_up(off + (size_t)pl.lists * 4, 256);
+  pl.off_run = RES_RUN;  // in the counter region
   // a query's lists: at most one per workgroup, and its keys cover at most
   // maxlen / MIN_SLICE + 2 slices
   const int64_t nl_max = std::min<int64_t>(nwg, maxlen / MIN_SLICE + 2);
@@ -146,8 +156,12 @@ IdxPlan plan_indexer(const dsa_indexer_args* a, int K, size_t base, int nwg) {
     off = align_up(off + (size_t)pl.lists * K * 4, 256);
     pl.off_mpos = off;
     off = align_up(off + (size_t)pl.lists * K * 4, 256);
-    pl.off_mdone = off;
-    off = align_up(off + (size_t)T * 4, 256);
+    if (T <= SMALL_T) {
+      pl.off_mdone = RES_MDONE;  // in the counter region
+    } else {
+      pl.off_mdone = off;  // cleared by the planning kernel
+      off = align_up(off + (size_t)T * 4, 256);
+    }
   }
   pl.end = off;
   return pl;
@@ -178,6 +192,14 @@ MlaPlan plan_mla(const dsa_mla_args* m, int K, size_t base) {
   return pl;
 }
 
+// A standalone attention call: its partials sit past the counter region (the
+// workspace may be shared with indexer calls); with one split it needs none.
+MlaPlan mla_alone(const dsa_mla_args* m, int K) {
+  MlaPlan pl = plan_mla(m, K, DSA_WS_RESERVED_BYTES);
+  if (pl.S == 1) pl.end = 0;
+  return pl;
+}
+
 IdxParams make_idx_params(const dsa_indexer_args* a, int K, int32_t* indices, unsigned char* ws, const IdxPlan& pl) {
   IdxParams p{};
   p.q_idx = (const uint8_t*)a->q_idx;
@@ -200,6 +222,7 @@ IdxParams make_idx_params(const dsa_indexer_args* a, int K, int32_t* indices, un
   p.K = K;
   p.nwg = pl.nwg;
   p.MQ = pl.MQ;
+  p.inplan = a->T <= SMALL_T ? 1 : 0;
   p.indices = indices;
   p.hdr = (int32_t*)(ws + pl.off_hdr);
   p.groups = (int32_t*)(ws + pl.off_groups);
@@ -256,7 +279,7 @@ dsa_status layer_check(const dsa_indexer_args* idx, const dsa_mla_args* mla, int
   if (idx->T != mla->T || idx->num_blocks != mla->num_blocks) return DSA_ERR_SHAPE;
   if (!out) return DSA_ERR_NULL;
   if (!aligned(out, 8) || !aligned(indices_out, 4)) return DSA_ERR_ALIGN;
-  const IdxPlan ip = plan_indexer(idx, K, 0, device_cus());
+  const IdxPlan ip = plan_indexer(idx, K, device_cus());
   const size_t idx_end = align_up(align_up(ip.end, 256) + (size_t)idx->T * K * 4, 256);
   *need = plan_mla(mla, K, idx_end).end;
   return DSA_OK;
@@ -266,7 +289,7 @@ dsa_status layer_check(const dsa_indexer_args* idx, const dsa_mla_args* mla, int
 // layer_check's bytes.
 dsa_status layer_launch(const dsa_indexer_args* idx, const dsa_mla_args* mla, int K, float scale,
                         int32_t* indices_out, void* out, unsigned char* w, hipStream_t s) {
-  const IdxPlan ip = plan_indexer(idx, K, 0, device_cus());
+  const IdxPlan ip = plan_indexer(idx, K, device_cus());
   const size_t off_idx = align_up(ip.end, 256);
   const size_t idx_end = align_up(off_idx + (size_t)idx->T * K * 4, 256);
   const MlaPlan mp = plan_mla(mla, K, idx_end);
@@ -287,13 +310,17 @@ constexpr int MAX_DEVICES = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[MAX_DEVICES] = {};
 
-dsa_status scratch_of_current_device(unsigned char** out) {
+// The device address of the current GPU's array, looked up on the device's
+// first call, which also clears the array's counter region (a kernel on the
+// call's stream, ahead of the call's own kernels).
+dsa_status scratch_of_current_device(unsigned char** out, hipStream_t st) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return DSA_ERR_HIP;
   std::lock_guard<std::mutex> lk(g_scratch_mu);
   if (!g_scratch_ptr[dev]) {
     void* ptr = nullptr;
     if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return DSA_ERR_HIP;
+    if (launch_clear_counters(ptr, DSA_WS_RESERVED_BYTES, st) != hipSuccess) return DSA_ERR_HIP;
     g_scratch_ptr[dev] = ptr;
   }
   *out = (unsigned char*)g_scratch_ptr[dev];
@@ -330,14 +357,22 @@ size_t dsa_workspace_bytes(const dsa_indexer_args* idx, const dsa_mla_args* mla,
   size_t end = 0;
   if (idx) {
     if (check_indexer(idx, K) != DSA_OK) return 0;
-    end = plan_indexer(idx, K, 0, device_cus()).end;
+    end = plan_indexer(idx, K, device_cus()).end;
   }
   if (mla) {
     if (check_mla(mla, K) != DSA_OK) return 0;
-    if (idx) end = align_up(end + (size_t)idx->T * K * 4, 256);  // indices kept for the layer
+    if (!idx) return mla_alone(mla, K).end;
+    end = align_up(end + (size_t)idx->T * K * 4, 256);  // indices kept for the layer
     end = plan_mla(mla, K, end).end;
   }
   return end;
+}
+
+dsa_status dsa_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (ws_bytes == 0) return DSA_OK;
+  if (!ws) return DSA_ERR_NULL;
+  if (!aligned(ws, 256)) return DSA_ERR_ALIGN;
+  return hip_status(launch_clear_counters(ws, std::min(ws_bytes, (size_t)DSA_WS_RESERVED_BYTES), (hipStream_t)stream));
 }
 
 dsa_status dsa_indexer_topk(const dsa_indexer_args* a, int K, int32_t* indices_out, void* ws, size_t ws_bytes,
@@ -346,7 +381,7 @@ dsa_status dsa_indexer_topk(const dsa_indexer_args* a, int K, int32_t* indices_o
   if (st != DSA_OK) return st;
   if (!indices_out) return DSA_ERR_NULL;
   if (!aligned(indices_out, 4)) return DSA_ERR_ALIGN;
-  const IdxPlan pl = plan_indexer(a, K, 0, device_cus());
+  const IdxPlan pl = plan_indexer(a, K, device_cus());
   if (!ws || ws_bytes < pl.end || !aligned(ws, 256)) return DSA_ERR_WORKSPACE;
   IdxParams p = make_idx_params(a, K, indices_out, (unsigned char*)ws, pl);
   return hip_status(launch_indexer(p, a->idx_dtype, a->D_idx, pl.nwg, (hipStream_t)stream));
@@ -359,7 +394,7 @@ dsa_status dsa_indexer_scores(const dsa_indexer_args* a, float* scores, int64_t 
   if (!scores) return DSA_ERR_NULL;
   if (!aligned(scores, 4)) return DSA_ERR_ALIGN;
   if (ld < (int64_t)a->max_blocks * DSA_PAGE_TOKENS) return DSA_ERR_SHAPE;
-  const IdxPlan pl = plan_indexer(a, 1, 0, device_cus());
+  const IdxPlan pl = plan_indexer(a, 1, device_cus());
   if (!ws || ws_bytes < pl.end || !aligned(ws, 256)) return DSA_ERR_WORKSPACE;
   IdxParams p = make_idx_params(a, 1, nullptr, (unsigned char*)ws, pl);
   p.scores = scores;
@@ -373,7 +408,7 @@ dsa_status dsa_sparse_mla_attn(const dsa_mla_args* m, const int32_t* indices, in
   if (st != DSA_OK) return st;
   if (!indices || !out) return DSA_ERR_NULL;
   if (!aligned(indices, 4) || !aligned(out, 8)) return DSA_ERR_ALIGN;
-  const MlaPlan pl = plan_mla(m, K, 0);
+  const MlaPlan pl = mla_alone(m, K);
   if (pl.end > 0 && (!ws || ws_bytes < pl.end || !aligned(ws, 256))) return DSA_ERR_WORKSPACE;
   MlaParams p = make_mla_params(m, indices, K, scale, out, (unsigned char*)ws, pl);
   return hip_status(launch_mla(p, (hipStream_t)stream));
@@ -395,7 +430,7 @@ dsa_status dsa_layer_static(const dsa_indexer_args* idx, const dsa_mla_args* mla
   if (st != DSA_OK) return st;
   if (need > DSA_STATIC_SCRATCH_BYTES) return DSA_ERR_TOO_LARGE;
   unsigned char* w = nullptr;
-  st = scratch_of_current_device(&w);
+  st = scratch_of_current_device(&w, (hipStream_t)stream);
   if (st != DSA_OK) return st;
   return layer_launch(idx, mla, K, scale, indices_out, out, w, (hipStream_t)stream);
 }

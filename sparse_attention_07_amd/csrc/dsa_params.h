@@ -27,6 +27,7 @@ struct IdxParams {
   int32_t T, B, H_idx, K;
   int32_t nwg;  // indexer workgroups (each scans one equal slice of the key space)
   int32_t MQ;   // max queries per group
+  int32_t inplan;  // at most 64 queries: the indexer plans itself (no planning kernel, no hdr/groups/qgroup/wg_first)
   int32_t* indices;  // [T][K] output
   float* scores;      // score dump instead of selection (null: select): [T][scores_ld] fp32
   int64_t scores_ld;
@@ -39,14 +40,14 @@ struct IdxParams {
   uint32_t* list_mm;   //   [.][2] smallest and largest key of the list
   uint32_t* list_keys; //   [.][K] order keys, ascending position
   int32_t* list_pos;   //   [.][K] logical positions
-  int32_t* run_done;   //   [.] lists written of the run starting at each slot (cleared by the planning kernel)
+  int32_t* run_done;   //   [.] lists written of the run starting at each slot (clear at entry, cleared by the run's last arrival)
   // two-level merge of queries with many lists: intermediate lists (same
   // layout and slots as above) and a per-query count of finished runs
   int32_t* mlist_cnt;
   uint32_t* mlist_mm;
   uint32_t* mlist_keys;
   int32_t* mlist_pos;
-  int32_t* merge_done;  // [T], cleared by the planning kernel
+  int32_t* merge_done;  // [T], clear at entry, cleared by the query's last run
 };
 
 struct MlaParams {

@@ -55,6 +55,117 @@ namespace dsa {
 #define DSA_IDX_PART 0
 #endif
 
+// =============================================================================
+// Planning inside the indexer, for calls of at most PLAN_SMALL_T queries (every
+// decode batch): each workgroup derives the same plan as the planning kernel
+// below from the call's tables at its start, one query and then one group per
+// lane, so the call needs no planning launch and no round trips to read a plan
+// back.  This only works because the arrival counters of the list merges need
+// no clearing launch: each is cleared again by its run's last arrival, and a
+// workspace's counter region starts out clear (the C ABI's contract).
+// =============================================================================
+constexpr int PLAN_SMALL_T = 64;
+
+struct SmallPlan {
+  int grp[PLAN_SMALL_T * G_FIELDS];  // the planning kernel's group records
+  int qgroup[PLAN_SMALL_T];          // group of each query
+  int vis[PLAN_SMALL_T];             // visible keys of each query
+  int hdr[4];                        // groups, pages in the key space, pages per slice, this workgroup's first group
+};
+
+// One group record into registers: from the in-kernel plan (LDS reads) or
+// from the planning kernel's table (global loads), by an explicit branch so
+// that neither path becomes a generic (flat) access.
+__device__ __forceinline__ void read_group(const IdxParams& p, const SmallPlan& sp, int g, int (&r)[G_FIELDS]) {
+  if (p.inplan) {
+#pragma unroll
+    for (int f = 0; f < G_FIELDS; ++f) r[f] = sp.grp[g * G_FIELDS + f];
+  } else {
+#pragma unroll
+    for (int f = 0; f < G_FIELDS; ++f) r[f] = p.groups[(int64_t)g * G_FIELDS + f];
+  }
+#pragma unroll
+  for (int f = 0; f < G_FIELDS; ++f) r[f] = __builtin_amdgcn_readfirstlane(r[f]);
+}
+
+// Every wave computes the plan in registers; wave 0 stores it.  The caller
+// synchronises the workgroup before reading `sp`.
+__device__ __forceinline__ void plan_small(const IdxParams& p, SmallPlan& sp) {
+  const int lane = threadIdx.x & 63;
+  const int T = p.T;
+  const bool act = lane < T;
+  // query `lane`: its sequence (-1: none) and visible count, as in the planning kernel's first pass
+  int b = -1, qv = 0;
+  if (act) {
+    b = p.q_seq ? p.q_seq[lane] : lane;
+    qv = p.q_visible ? p.q_visible[lane] : 0;
+  }
+  b = (b >= 0 && b < p.B) ? b : -1;
+  const int len = b >= 0 ? p.seq_lens[b] : 0;
+  const int L = min(max(len, 0), p.max_blocks * PAGE);
+  const int vis = b >= 0 ? min(max(p.q_visible ? qv : L, 0), L) : 0;
+  // groups: runs of one sequence, cut every MQ queries
+  const int bprev = __shfl(b, max(lane - 1, 0));
+  const bool f = act && (lane == 0 || b != bprev);
+  const int run = wave_incl_max(f ? lane : -1);
+  const bool gs = act && ((lane - run) % p.MQ == 0);
+  const uint64_t gmask = ballot(gs);
+  const int n_groups = __builtin_popcountll(gmask);
+  const int qg = lanes_below(gmask) + (gs ? 1 : 0) - 1;
+  // lane g now stands for group g: its first query is the (g+1)-th set bit of
+  // gmask, the smallest t with g+1 starts in [0, t] (binary search on counts)
+  const bool isg = lane < n_groups;
+  int t0 = 0;
+#pragma unroll
+  for (int step = 32; step > 0; step >>= 1)
+    if (__builtin_popcountll(gmask & ((2ull << (t0 + step - 1)) - 1ull)) < lane + 1) t0 += step;
+  if (!isg) t0 = T;
+  const int tn = __shfl(t0, min(lane + 1, 63));
+  const int t1 = lane + 1 < n_groups ? tn : T;
+  int range = 0;
+  for (int k = 0; k < p.MQ; ++k) {
+    const int vk = __shfl(vis, min(t0 + k, 63));
+    if (isg && t0 + k < t1) range = max(range, vk);
+  }
+  const int seq = __shfl(b, min(t0, 63));
+  // key-space offsets (pages) and the slices, as in the planning kernel's second and third passes
+  const int wreal = max(1, (range + PAGE - 1) / PAGE);
+  const int wgt = isg ? wreal + SEG_COST_PG : 0;
+  const int incl = (int)wave_incl_scan((uint32_t)wgt);
+  const int off = incl - wgt;
+  const int total = __builtin_amdgcn_readlane(incl, 63);
+  const int slice = max(MIN_SLICE_PG, (total + p.nwg - 1) / p.nwg);
+  const int w0 = off / slice, w1 = (off + wreal - 1) / slice;
+  const int lists = (isg && w1 > w0) ? (t1 - t0) * (w1 - w0 + 1) : 0;
+  const int lincl = (int)wave_incl_scan((uint32_t)lists);
+  // this workgroup's slice starts inside the group whose weight covers it
+  const int a0 = (int)blockIdx.x * slice;
+  const int first = __builtin_popcountll(ballot(isg && off + wgt <= a0));
+  if (threadIdx.x < 64) {
+    if (isg) {
+      int* gr = sp.grp + lane * G_FIELDS;
+      gr[G_T0] = t0;
+      gr[G_NQ] = t1 - t0;
+      gr[G_SEQ] = seq;
+      gr[G_RANGE] = range;
+      gr[G_OFF] = off;
+      gr[G_NL] = w1 - w0 + 1;
+      gr[G_LIST] = lincl - lists;
+      gr[G_W0] = w0;
+    }
+    if (act) {
+      sp.qgroup[lane] = qg;
+      sp.vis[lane] = vis;
+    }
+    if (lane == 0) {
+      sp.hdr[0] = n_groups;
+      sp.hdr[1] = total;
+      sp.hdr[2] = slice;
+      sp.hdr[3] = first;
+    }
+  }
+}
+
 #if DSA_IDX_PART == 0
 // =============================================================================
 // Planning kernel: one workgroup (1024 threads; 256 for at most 256 queries,
@@ -242,6 +353,20 @@ __global__ __launch_bounds__(PLAN_NT) void dsa_plan_kernel(IdxParams p) {
     p.hdr[1] = total;
     p.hdr[2] = slice;
   }
+}
+
+// Clears the counter region at the start of a workspace (before its first use;
+// every call leaves it clear again).
+__global__ __launch_bounds__(256) void dsa_clear_kernel(uint32_t* w, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) w[i] = 0u;
+}
+
+hipError_t launch_clear_counters(void* ws, size_t bytes, hipStream_t st) {
+  const int n = (int)(bytes / 4);
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(dsa_clear_kernel, dim3((n + 255) / 256 < 64 ? (n + 255) / 256 : 64), dim3(256), 0, st,
+                     (uint32_t*)ws, n);
+  return hipGetLastError();
 }
 
 #endif  // DSA_IDX_PART == 0
@@ -715,9 +840,11 @@ __device__ __forceinline__ int merge_lists(const uint32_t* keys0, const int32_t*
 // One merge step for query t, run j, in the workgroup that wrote the run's
 // last list (every list of the run is complete and visible).  Block-wide;
 // ends with a barrier, after which the caller may reuse the LDS.
-__device__ __forceinline__ void merge_query(const IdxParams& p, int t, int j, MergeSmem& sm) {
+__device__ __forceinline__ void merge_query(const IdxParams& p, const SmallPlan& spl, int t, int j, MergeSmem& sm) {
   const int tid = threadIdx.x;
-  const int* gr = p.groups + (int64_t)p.qgroup[t] * G_FIELDS;
+  // the query's group record: the in-kernel plan's or the planning kernel's
+  int gr[G_FIELDS];
+  read_group(p, spl, __builtin_amdgcn_readfirstlane(p.inplan ? spl.qgroup[t] : p.qgroup[t]), gr);
   const int nl = gr[G_NL];  // lists of this query (one per overlapping indexer workgroup)
   const int nrun = nl > MRG_FAN ? (nl + MRG_FAN - 1) / MRG_FAN : 1;
   const int seq = gr[G_SEQ];
@@ -728,7 +855,7 @@ __device__ __forceinline__ void merge_query(const IdxParams& p, int t, int j, Me
   // into LDS (cand_key[KMAX ..] is unused then) with direct-to-LDS loads
   // that fly while the lists load: 16 bytes (4 pages) per lane, so the row
   // must be 16-byte aligned and a whole number of such pieces.
-  const int npg = (uniform(gr[G_RANGE]) + PAGE - 1) / PAGE;  // pages holding the group's keys
+  const int npg = (gr[G_RANGE] + PAGE - 1) / PAGE;  // pages holding the group's keys
   const bool stage = nrun == 1 && nl * K <= MRG_CHUNK && npg <= MRG_BT && (p.max_blocks & 3) == 0 &&
                      ((uintptr_t)bt & 15) == 0;
   int32_t* sbt = reinterpret_cast<int32_t*>(sm.cand_key + KMAX);
@@ -761,7 +888,12 @@ __device__ __forceinline__ void merge_query(const IdxParams& p, int t, int j, Me
     // the workgroup that finishes the last run merges the intermediate lists
     wait_vm();
     __syncthreads();
-    if (tid == 0) sm.sel[3] = atomicAdd(&p.merge_done[t], 1);
+    if (tid == 0) {
+      // the last run's arrival clears the counter for the next call
+      const int old = atomicAdd(p.merge_done + t, 1);
+      if (old == nrun - 1) st_dev(p.merge_done + t, 0);
+      sm.sel[3] = old;
+    }
     __syncthreads();
     const bool last = uniform(sm.sel[3]) == nrun - 1;
     lds_barrier();
@@ -827,6 +959,14 @@ struct IdxSmem {
   float wq[MQ][64];               // head weight x query scale of the group's queries
 };
 
+// Offset of the in-kernel plan in the indexer's LDS: past the streaming and
+// the merge layouts, which share the start.
+template <int NW, int MQ>
+struct SmallPlanOff {
+  static constexpr size_t value =
+      ((sizeof(IdxSmem<NW, MQ>) > sizeof(MergeSmem) ? sizeof(IdxSmem<NW, MQ>) : sizeof(MergeSmem)) + 15) / 16 * 16;
+};
+
 template <int DT, int D>
 struct Frag {
   // bf16: one 16-byte piece per 32-wide k step; fp8: two 16-byte pieces (k=128)
@@ -863,6 +1003,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Sm& sm = *reinterpret_cast<Sm*>(smem_raw);
   MergeSmem& msm = *reinterpret_cast<MergeSmem*>(smem_raw);  // same LDS, between segments
+  // the in-kernel plan sits past both (read until the last merge)
+  SmallPlan& spl = *reinterpret_cast<SmallPlan*>(smem_raw + SmallPlanOff<NW, MQ>::value);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -870,32 +1012,41 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
   const int g4 = lane >> 4;
   const int n16 = lane & 15;
 
+  // the plan: computed here for a small call, else the planning kernel's
+  // (the tables are picked where they are read, not held in registers)
+  if (p.inplan) {
+    plan_small(p, spl);
+    __syncthreads();
+  }
+
   // this workgroup's slice [a0, a1) of the key space, in pages
-  const int n_groups = p.hdr[0];
-  const int total = p.hdr[1];
-  const int slice = p.hdr[2];
+  const int* hdr = p.inplan ? spl.hdr : p.hdr;
+  const int n_groups = uniform(hdr[0]);
+  const int total = uniform(hdr[1]);
+  const int slice = uniform(hdr[2]);
   const int a0 = blockIdx.x * slice;
   const int a1 = min(a0 + slice, total);
   if (a0 >= a1) return;
 
-  // first group overlapping [a0, a1), found by the planning kernel
-  int g = uniform(p.wg_first[blockIdx.x]);
+  // first group overlapping [a0, a1)
+  int g = uniform(p.inplan ? spl.hdr[3] : p.wg_first[blockIdx.x]);
   // runs this workgroup completes, merged once its slice is streamed: at most
   // two split groups overlap a slice (the one across each end), each entry
   // (group << 8) | (run << 2) | query mask
   int pend0 = -1, pend1 = -1;
 
   for (; g < n_groups; ++g) {
-    const int* gr = p.groups + (int64_t)g * G_FIELDS;
-    const int off = uniform(gr[G_OFF]);
+    int gr[G_FIELDS];
+    read_group(p, spl, g, gr);
+    const int off = gr[G_OFF];
     if (off >= a1) break;
-    const int t0 = uniform(gr[G_T0]);
-    const int nq = uniform(gr[G_NQ]);
-    const int seq = uniform(gr[G_SEQ]);
-    const int range = uniform(gr[G_RANGE]);
-    const int nl = uniform(gr[G_NL]);
-    const int list_base = uniform(gr[G_LIST]);
-    const int w0 = uniform(gr[G_W0]);
+    const int t0 = gr[G_T0];
+    const int nq = gr[G_NQ];
+    const int seq = gr[G_SEQ];
+    const int range = gr[G_RANGE];
+    const int nl = gr[G_NL];
+    const int list_base = gr[G_LIST];
+    const int w0 = gr[G_W0];
     const int wreal = max(1, (range + PAGE - 1) / PAGE);  // pages
     if ((int)blockIdx.x >= w0 + nl) continue;  // only the group's cost weight lies in this slice
     // this workgroup's keys of the group: [seg_lo, seg_hi), seg_lo a multiple of 64
@@ -908,9 +1059,13 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
     for (int q = 0; q < MQ; ++q) {
       int v = 0;
       if (q < nq && seq >= 0) {
-        const int L = min(max(p.seq_lens[seq], 0), p.max_blocks * PAGE);
-        v = p.q_visible ? p.q_visible[t0 + q] : L;
-        v = min(max(v, 0), L);
+        if (p.inplan) {
+          v = spl.vis[t0 + q];
+        } else {
+          const int L = min(max(p.seq_lens[seq], 0), p.max_blocks * PAGE);
+          v = p.q_visible ? p.q_visible[t0 + q] : L;
+          v = min(max(v, 0), L);
+        }
       }
       vis[q] = uniform(v);
     }
@@ -1279,7 +1434,13 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
           // arrival: the list is complete before the run's counter moves
           wait_vm();
           __syncthreads();
-          if (tid == 0) sm.sel[3] = atomicAdd(&p.run_done[unit - il + jr], 1);
+          if (tid == 0) {
+            // the run's last arrival clears the counter for the next call
+            int* ctr = p.run_done + (unit - il + jr);
+            const int old = atomicAdd(ctr, 1);
+            if (old == rs - 1) st_dev(ctr, 0);
+            sm.sel[3] = old;
+          }
           __syncthreads();
           if (uniform(sm.sel[3]) == rs - 1) pend |= 1 << q;
         }
@@ -1300,10 +1461,13 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
   for (int k = 0; k < 2; ++k) {
     const int e = uniform(k == 0 ? pend0 : pend1);
     if (e < 0) break;
-    const int t0 = p.groups[(int64_t)(e >> 8) * G_FIELDS + G_T0];
+    int ge[G_FIELDS];
+    read_group(p, spl, e >> 8, ge);
+    const int t0 = ge[G_T0];
 #pragma unroll 1
     for (int q = 0; q < MQ; ++q)
-      if ((e >> q) & 1) merge_query(p, t0 + q, (e >> 2) & 63, msm);
+      if ((e >> q) & 1)
+        merge_query(p, spl, t0 + q, (e >> 2) & 63, msm);
   }
 }
 
@@ -1313,8 +1477,11 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
 template <int DT, int D, int HT, int MQ, int NW>
 static hipError_t launch_indexer_t(const IdxParams& p, int grid, hipStream_t st) {
   auto kfn = dsa_indexer_kernel<DT, D, HT, MQ, NW>;
-  // the merge reuses the workgroup's LDS when lists exist
-  const size_t smem = p.run_done ? std::max(sizeof(IdxSmem<NW, MQ>), sizeof(MergeSmem)) : sizeof(IdxSmem<NW, MQ>);
+  // the merge reuses the workgroup's LDS when lists exist; the in-kernel plan
+  // follows both
+  const size_t smem = p.inplan ? SmallPlanOff<NW, MQ>::value + sizeof(SmallPlan)
+                               : (p.run_done ? std::max(sizeof(IdxSmem<NW, MQ>), sizeof(MergeSmem))
+                                             : sizeof(IdxSmem<NW, MQ>));
   hipError_t e = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kfn, dim3(grid), dim3(NW * 64), smem, st, p);
@@ -1358,13 +1525,16 @@ hipError_t launch_indexer_bf16_64(const IdxParams& p, int grid, hipStream_t st) 
 #if DSA_IDX_PART == 0
 hipError_t launch_indexer(const IdxParams& p, int idx_dtype, int D, int grid, hipStream_t st) {
   const size_t plan_smem = p.T <= PLAN_LDS_T ? PLAN_LDS_BYTES : 0;
-  hipError_t e = hipFuncSetAttribute((const void*)dsa_plan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)PLAN_LDS_BYTES);
-  if (e != hipSuccess) return e;
-  const int plan_nt = p.T <= 64 ? 64 : (p.T <= 256 ? 256 : PLAN_NT);
-  hipLaunchKernelGGL(dsa_plan_kernel, dim3(1), dim3(plan_nt), plan_smem, st, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (!p.inplan) {  // a small call plans inside the indexer
+    e = hipFuncSetAttribute((const void*)dsa_plan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)PLAN_LDS_BYTES);
+    if (e != hipSuccess) return e;
+    const int plan_nt = p.T <= 64 ? 64 : (p.T <= 256 ? 256 : PLAN_NT);
+    hipLaunchKernelGGL(dsa_plan_kernel, dim3(1), dim3(plan_nt), plan_smem, st, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (idx_dtype == 1) return launch_indexer_fp8(p, grid, st);
   if (idx_dtype == 2) return launch_indexer_mxfp8(p, grid, st);
   return D == 64 ? launch_indexer_bf16_64(p, grid, st) : launch_indexer_bf16_128(p, grid, st);

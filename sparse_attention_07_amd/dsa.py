@@ -27,10 +27,11 @@ VDIM = 512
 MAX_K = 2048
 
 # Every symbol the header declares (checked by the tests against include/dsa.h).
-EXPORTS = ("dsa_workspace_bytes", "dsa_indexer_topk", "dsa_indexer_scores", "dsa_sparse_mla_attn", "dsa_layer",
+EXPORTS = ("dsa_workspace_bytes", "dsa_workspace_init", "dsa_indexer_topk", "dsa_indexer_scores", "dsa_sparse_mla_attn", "dsa_layer",
            "dsa_layer_static", "dsa_quantize_index_q", "dsa_check_tables", "dsa_status_str", "dsa_abi_version")
 TABLE_NAMES = ("seq_lens", "block_table", "q_seq", "q_visible")
 STATIC_SCRATCH_BYTES = 64 << 20
+WS_RESERVED_BYTES = 32768  # counter region at the start of a workspace (zero before first use)
 
 
 class DSAError(RuntimeError):
@@ -68,6 +69,8 @@ def _load() -> ctypes.CDLL:
     P = ctypes.POINTER
     lib.dsa_workspace_bytes.restype = ctypes.c_size_t
     lib.dsa_workspace_bytes.argtypes = [P(IndexerArgs), P(MlaArgs), ctypes.c_int]
+    lib.dsa_workspace_init.restype = ctypes.c_int
+    lib.dsa_workspace_init.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.dsa_indexer_topk.restype = ctypes.c_int
     lib.dsa_indexer_topk.argtypes = [P(IndexerArgs), ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_size_t, ctypes.c_void_p]
@@ -155,15 +158,24 @@ def workspace_bytes(idx: Optional[IndexerArgs], mla: Optional[MlaArgs], K: int) 
                                        None if mla is None else ctypes.byref(mla), K))
 
 
+def workspace_init(workspace: torch.Tensor) -> torch.Tensor:
+    """dsa_workspace_init on the current stream: clears the counter region a
+    new workspace must start with (once; calls leave it clear)."""
+    _check(LIB.dsa_workspace_init(_ptr(workspace), workspace.numel(), _stream()))
+    return workspace
+
+
 def _workspace(nbytes: int, device) -> torch.Tensor:
-    # 256-byte aligned by the caching allocator; no initialisation needed
-    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    # 256-byte aligned by the caching allocator; only the counter region needs
+    # initialising
+    return workspace_init(torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device))
 
 
 def indexer_topk(q_idx, w, k_idx_pool, block_table, seq_lens, K: int, *, q_idx_scale=None, q_seq=None,
                  q_visible=None, max_q_per_seq: int = 1, out: Optional[torch.Tensor] = None,
                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Indexer + Top-K: int32 [T, K] physical pool slots (ascending position), -1 padded."""
+    """Indexer + Top-K: int32 [T, K] physical pool slots (ascending position), -1 padded.
+    A `workspace` passed in must have been through workspace_init once."""
     a = indexer_args(q_idx, w, k_idx_pool, block_table, seq_lens, q_idx_scale=q_idx_scale, q_seq=q_seq,
                      q_visible=q_visible, max_q_per_seq=max_q_per_seq)
     if out is None:

@@ -15,6 +15,8 @@ namespace dsa {
 extern IdxParams g_idx;
 extern MlaParams g_mla;
 extern int g_idx_calls, g_mla_calls, g_quant_calls, g_idx_grid;
+extern void* g_clear_ptr;
+extern size_t g_clear_bytes;
 }
 
 static int failures = 0;
@@ -58,8 +60,16 @@ static void check_idx_layout(const unsigned char* ws, size_t bytes) {
   CHECK(inside(p.groups + (int64_t)p.T * dsa::G_FIELDS - 1, ws, bytes));
   CHECK(inside(p.qgroup + p.T - 1, ws, bytes));
   CHECK(inside(p.wg_first + p.nwg - 1, ws, bytes));
+  // a call of at most 64 queries plans inside the indexer
+  CHECK(p.inplan == (p.T <= 64 ? 1 : 0));
+  // the plan tables and the lists sit past the counter region
+  CHECK((const unsigned char*)p.hdr >= ws + DSA_WS_RESERVED_BYTES);
   if (p.run_done) {  // candidate lists (queries spanning several slices): 2 MQ nwg of K entries each
     const int64_t lists = (int64_t)2 * p.MQ * p.nwg;
+    // the arrival counters: at the start of the counter region, clear of everything else
+    CHECK((const unsigned char*)p.run_done == ws);
+    CHECK((const unsigned char*)(p.run_done + lists) <= ws + DSA_WS_RESERVED_BYTES);
+    CHECK((const unsigned char*)p.list_cnt >= ws + DSA_WS_RESERVED_BYTES);
     CHECK(inside(p.list_cnt + lists - 1, ws, bytes));
     CHECK(inside(p.list_mm + 2 * lists - 1, ws, bytes));
     CHECK(inside(p.list_keys + lists * p.K - 1, ws, bytes));
@@ -71,6 +81,13 @@ static void check_idx_layout(const unsigned char* ws, size_t bytes) {
       CHECK(inside(p.mlist_keys + lists * p.K - 1, ws, bytes));
       CHECK(inside(p.mlist_pos + lists * p.K - 1, ws, bytes));
       CHECK(inside(p.merge_done + p.T - 1, ws, bytes));
+      // per-query counters: in the counter region for a small call, else past it
+      if (p.T <= 64) {
+        CHECK((const unsigned char*)p.merge_done >= (const unsigned char*)(p.run_done + lists));
+        CHECK((const unsigned char*)(p.merge_done + p.T) <= ws + DSA_WS_RESERVED_BYTES);
+      } else {
+        CHECK((const unsigned char*)p.merge_done >= ws + DSA_WS_RESERVED_BYTES);
+      }
     }
   }
 }
@@ -110,6 +127,16 @@ int main() {
     }
     CHECK(dsa::g_mla.S * dsa::g_mla.rows_per_split >= c.K && dsa::g_mla.rows_per_split % 32 == 0);
     CHECK(dsa_layer(&a, &m, c.K, 0.04f, nullptr, P(), w, need_l - 256, nullptr) == DSA_ERR_WORKSPACE);
+    // a standalone attention call keeps its partials out of the counter region
+    const size_t need_m = dsa_workspace_bytes(nullptr, &m, c.K);
+    CHECK(dsa_sparse_mla_attn(&m, (const int32_t*)P(), c.K, 0.04f, P(), w, need_m, nullptr) == DSA_OK);
+    if (dsa::g_mla.part_o) {
+      CHECK(need_m > DSA_WS_RESERVED_BYTES);
+      CHECK((const unsigned char*)dsa::g_mla.part_o >= w + DSA_WS_RESERVED_BYTES);
+      CHECK(inside(dsa::g_mla.part_ml + (int64_t)c.T * dsa::g_mla.S * c.H * 2 - 1, w, need_m));
+    } else {
+      CHECK(need_m == 0);
+    }
     const size_t need_s = dsa_workspace_bytes(&a, nullptr, 1);
     CHECK(dsa_indexer_scores(&a, (float*)P(), (int64_t)64 * c.max_blocks, w, need_s, nullptr) == DSA_OK);
     CHECK(dsa_indexer_scores(&a, (float*)P(), (int64_t)64 * c.max_blocks - 1, w, need_s, nullptr) == DSA_ERR_SHAPE);
@@ -159,7 +186,17 @@ int main() {
     CHECK(dsa_quantize_index_q(P(), -1, 128, DSA_IDX_FP8_E4M3FN, P(), P(), nullptr) == DSA_ERR_SHAPE);
     CHECK(dsa::g_idx_calls + dsa::g_mla_calls + dsa::g_quant_calls == before);
     for (int s = 0; s <= 10; ++s) CHECK(dsa_status_str((dsa_status)s) != nullptr);
+    CHECK(dsa_workspace_init(nullptr, 1 << 20, nullptr) == DSA_ERR_NULL);
+    CHECK(dsa_workspace_init(P(16), 1 << 20, nullptr) == DSA_ERR_ALIGN);
     CHECK(dsa_abi_version() == DSA_ABI_VERSION);
+  }
+  // ---- dsa_workspace_init clears the counter region (or less, for a smaller workspace)
+  {
+    CHECK(dsa_workspace_init(nullptr, 0, nullptr) == DSA_OK);
+    CHECK(dsa_workspace_init(P(), 1 << 20, nullptr) == DSA_OK);
+    CHECK(dsa::g_clear_ptr == P() && dsa::g_clear_bytes == DSA_WS_RESERVED_BYTES);
+    CHECK(dsa_workspace_init(P(), 4096, nullptr) == DSA_OK);
+    CHECK(dsa::g_clear_bytes == 4096);
   }
   // ---- the static-scratch layer rejects calls larger than its array before
   // touching the device

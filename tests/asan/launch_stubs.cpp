@@ -26,4 +26,11 @@ hipError_t launch_quantize_q(const void*, int64_t, int, int, void*, void*, hipSt
   ++g_quant_calls;
   return hipSuccess;
 }
+void* g_clear_ptr = nullptr;
+size_t g_clear_bytes = 0;
+hipError_t launch_clear_counters(void* ws, size_t bytes, hipStream_t) {
+  g_clear_ptr = ws;
+  g_clear_bytes = bytes;
+  return hipSuccess;
+}
 }  // namespace dsa

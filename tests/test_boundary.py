@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     m = re.search(r"#define DSA_ABI_VERSION (\d+)", open(HEADER).read())
-    assert int(m.group(1)) == 7
+    assert int(m.group(1)) == 8
     assert dsa.LIB.dsa_abi_version() == int(m.group(1))
     assert dsa.status_str(0) == "ok"
     for s in range(1, 11):
@@ -197,10 +197,12 @@ def test_mla_null_and_workspace():
 ])
 def test_mla_split_count_sizes_the_partials(T, H, K, splits):
     # with S > 1 splits the workspace holds bf16 partials [T][S][H][512] and
-    # fp32 (m, l) pairs [T][S][H][2], each region 256-byte aligned
+    # fp32 (m, l) pairs [T][S][H][2], each region 256-byte aligned, past the
+    # counter region an indexer call sharing the workspace keeps at its start
     def align(n):
         return (n + 255) // 256 * 256
-    want = 0 if splits == 1 else align(T * splits * H * 512 * 2) + align(T * splits * H * 2 * 4)
+    want = 0 if splits == 1 else (dsa.WS_RESERVED_BYTES + align(T * splits * H * 512 * 2)
+                                  + align(T * splits * H * 2 * 4))
     assert dsa.workspace_bytes(None, good_mla(T=T, H=H), K) == want
 
 
@@ -225,9 +227,19 @@ def test_workspace_bytes_invalid_and_scaling():
     a = good_idx(T=64, B=64, max_blocks=2048, num_blocks=100000)
     n = dsa.workspace_bytes(a, good_mla(T=64, num_blocks=100000), 2048)
     assert 0 < n < (1 << 30)
-    # a single short-context decode needs no candidate lists (one chunk per query)
+    # a single short-context decode needs no candidate lists (one chunk per query):
+    # the counter region and a few plan records
     small = dsa.workspace_bytes(good_idx(T=1, B=1, max_blocks=64), None, 256)
-    assert 0 < small < 4096
+    assert dsa.WS_RESERVED_BYTES < small < dsa.WS_RESERVED_BYTES + 4096
+
+
+def test_workspace_counter_region_constant_and_init_errors():
+    m = re.search(r"#define DSA_WS_RESERVED_BYTES \(\(size_t\)(\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) == dsa.WS_RESERVED_BYTES
+    init = dsa.LIB.dsa_workspace_init
+    assert init(None, 0, None) == 0           # nothing to clear: nothing enqueued
+    assert init(None, 4096, None) == E_NULL
+    assert init(_base + 16, 4096, None) == E_ALIGN
 
 
 def test_keyspace_bound():
