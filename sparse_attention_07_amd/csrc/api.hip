@@ -137,7 +137,7 @@ IdxPlan plan_indexer(const dsa_indexer_args* a, int K, int nwg) {
   pl.off_lcnt = off;
   off = align_up(off + (size_t)pl.lists * 4, 256);
   pl.off_lmin = off;
-  off = align_up(off + (size_t)pl.lists * 8, 256);
+  off = align_up(off + (size_t)pl.lists * 4, 256);
   pl.off_lkeys = off;
   off = align_up(off + (size_t)pl.lists * K * 4, 256);
   pl.off_lpos = off;
@@ -151,7 +151,7 @@ IdxPlan plan_indexer(const dsa_indexer_args* a, int K, int nwg) {
     pl.off_mcnt = off;
     off = align_up(off + (size_t)pl.lists * 4, 256);
     pl.off_mmin = off;
-    off = align_up(off + (size_t)pl.lists * 8, 256);
+    off = align_up(off + (size_t)pl.lists * 4, 256);
     pl.off_mkeys = off;
     off = align_up(off + (size_t)pl.lists * K * 4, 256);
     pl.off_mpos = off;
@@ -229,13 +229,13 @@ IdxParams make_idx_params(const dsa_indexer_args* a, int K, int32_t* indices, un
   p.qgroup = (int32_t*)(ws + pl.off_qgroup);
   p.wg_first = (int32_t*)(ws + pl.off_wgfirst);
   p.list_cnt = (int32_t*)(ws + pl.off_lcnt);
-  p.list_mm = (uint32_t*)(ws + pl.off_lmin);
+  p.list_min = (uint32_t*)(ws + pl.off_lmin);
   p.list_keys = (uint32_t*)(ws + pl.off_lkeys);
   p.list_pos = (int32_t*)(ws + pl.off_lpos);
   p.run_done = pl.need_merge ? (int32_t*)(ws + pl.off_run) : nullptr;
   const bool two = pl.merge_runs > 1;
   p.mlist_cnt = two ? (int32_t*)(ws + pl.off_mcnt) : nullptr;
-  p.mlist_mm = two ? (uint32_t*)(ws + pl.off_mmin) : nullptr;
+  p.mlist_min = two ? (uint32_t*)(ws + pl.off_mmin) : nullptr;
   p.mlist_keys = two ? (uint32_t*)(ws + pl.off_mkeys) : nullptr;
   p.mlist_pos = two ? (int32_t*)(ws + pl.off_mpos) : nullptr;
   p.merge_done = two ? (int32_t*)(ws + pl.off_mdone) : nullptr;

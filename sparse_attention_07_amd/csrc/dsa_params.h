@@ -37,14 +37,14 @@ struct IdxParams {
   int32_t* qgroup;     // [T] group of each query
   int32_t* wg_first;   // [nwg] first group of each indexer workgroup
   int32_t* list_cnt;   // per (query, chunk) candidate list: entry count
-  uint32_t* list_mm;   //   [.][2] smallest and largest key of the list
+  uint32_t* list_min;  //   [.] smallest key of the list (read only when the list is full)
   uint32_t* list_keys; //   [.][K] order keys, ascending position
   int32_t* list_pos;   //   [.][K] logical positions
   int32_t* run_done;   //   [.] lists written of the run starting at each slot (clear at entry, cleared by the run's last arrival)
   // two-level merge of queries with many lists: intermediate lists (same
   // layout and slots as above) and a per-query count of finished runs
   int32_t* mlist_cnt;
-  uint32_t* mlist_mm;
+  uint32_t* mlist_min;
   uint32_t* mlist_keys;
   int32_t* mlist_pos;
   int32_t* merge_done;  // [T], clear at entry, cleared by the query's last run

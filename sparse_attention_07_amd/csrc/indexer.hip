@@ -647,32 +647,20 @@ __device__ __forceinline__ int block_append(uint32_t* keys, int32_t* pos, int ba
   return total;
 }
 
-// Smallest and largest key of keys[0..n) (block-wide; n >= 1).
+// Smallest key of keys[0..n) (block-wide; n >= 1).
 template <int NW>
-__device__ __forceinline__ void block_minmax(const uint32_t* keys, int n, uint32_t* red, uint32_t& mn_out, uint32_t& mx_out) {
+__device__ __forceinline__ uint32_t block_min(const uint32_t* keys, int n, uint32_t* red) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t mn = 0xffffffffu, mx = 0u;
-  for (int i = tid; i < n; i += NW * 64) {
-    mn = min(mn, keys[i]);
-    mx = max(mx, keys[i]);
-  }
+  uint32_t mn = 0xffffffffu;
+  for (int i = tid; i < n; i += NW * 64) mn = min(mn, keys[i]);
   mn = wave_min_u32(mn);
-  mx = wave_max_u32(mx);
-  if (lane == 0) {
-    red[wave] = mn;
-    red[NW + wave] = mx;
-  }
+  if (lane == 0) red[wave] = mn;
   lds_barrier();
   mn = 0xffffffffu;
-  mx = 0u;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    mn = min(mn, red[w]);
-    mx = max(mx, red[NW + w]);
-  }
+  for (int w = 0; w < NW; ++w) mn = min(mn, red[w]);
   lds_barrier();
-  mn_out = mn;
-  mx_out = mx;
+  return mn;
 }
 
 // =============================================================================
@@ -737,11 +725,13 @@ __device__ __forceinline__ uint32_t block_lb(uint32_t lb, MergeSmem& sm) {
 }
 
 // Top-K of the n <= MRG_NT lists at keys0/pos0 (list i at offset i K; counts
-// and [min, max] pairs at cnt0/mm0), keys below the largest minimum of a full
-// list (or below lb0) excluded: the kept entries, in position order, go to
-// sm.cand_key/cand_pos [0, cnt); returns cnt.  Ends with a barrier.
+// and minima at cnt0/min0, a minimum being read only for a full list), keys
+// below the largest minimum of a full list (or below lb0) excluded: the kept
+// entries, in position order, go to sm.cand_key/cand_pos [0, cnt); returns cnt
+// and sets kmin to the smallest kept key.  Ends with a barrier.
 __device__ __forceinline__ int merge_lists(const uint32_t* keys0, const int32_t* pos0, const int32_t* cnt0,
-                                           const uint32_t* mm0, int n, uint32_t lb0, int K, MergeSmem& sm) {
+                                           const uint32_t* min0, int n, uint32_t lb0, int K, MergeSmem& sm,
+                                           uint32_t& kmin) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // list counts and minima: loaded before the first chunk, reduced after it
   // has been issued, so the two latencies overlap
@@ -749,7 +739,7 @@ __device__ __forceinline__ int merge_lists(const uint32_t* keys0, const int32_t*
   uint32_t lm = 0u;
   if (tid < n) {
     lc = ld_dev(cnt0 + tid);
-    lm = ld_dev(mm0 + 2 * tid);
+    lm = ld_dev(min0 + tid);
   }
   const int total = n * K;
   const int nchunks = (total + MRG_CHUNK - 1) / MRG_CHUNK;
@@ -776,6 +766,7 @@ __device__ __forceinline__ int merge_lists(const uint32_t* keys0, const int32_t*
   const uint32_t lb = max(lb0, block_lb(tid < n && lc == K ? lm : 1u, sm));
   uint32_t thr = lb - 1u;  // keep keys > thr
   int cnt = 0;
+  uint32_t kbuf = 0xffffffffu;  // smallest key in the buffer (several chunks)
   for (int c = 0; c < nchunks; ++c) {
     if (c > 0) wch = load_chunk(c);
     const int cn = min(MRG_CHUNK, total - c * MRG_CHUNK);
@@ -790,7 +781,6 @@ __device__ __forceinline__ int merge_lists(const uint32_t* keys0, const int32_t*
     if (nchunks == 1) {
       // ---- single chunk: select straight from the registers
       const SelRule rule = select_rule<MRG_NW, MRG_RS>(rk, rp, K, sm.hist, sm.sel, sm.red);
-      uint32_t kmin;
       cnt = select_output<MRG_NW, MRG_RS>(rk, rp, rule, sm.red, kmin, [&](int o, uint32_t k, int32_t ps) {
         sm.cand_key[o] = k;
         sm.cand_pos[o] = ps;
@@ -813,8 +803,8 @@ __device__ __forceinline__ int merge_lists(const uint32_t* keys0, const int32_t*
     if (cnt + tot > MRG_CAP && cnt > K) {
       // cut the buffer to its Top-K (raising the bound), then drop the chunk's
       // entries that no longer pass
-      thr = max(thr, block_select<MRG_NW, MRG_CAP / MRG_NT>(sm.cand_key, sm.cand_pos, cnt, K, sm.hist, sm.sel,
-                                                             sm.red));
+      kbuf = block_select<MRG_NW, MRG_CAP / MRG_NT>(sm.cand_key, sm.cand_pos, cnt, K, sm.hist, sm.sel, sm.red);
+      thr = max(thr, kbuf);
       cnt = K;
       mask();
       tot = count_valid();
@@ -823,17 +813,19 @@ __device__ __forceinline__ int merge_lists(const uint32_t* keys0, const int32_t*
     // that does not fit (cnt <= K then, and cnt + K <= MRG_CAP)
     const SelRule rule = cnt + tot > MRG_CAP ? select_rule<MRG_NW, MRG_RS>(rk, rp, K, sm.hist, sm.sel, sm.red)
                                              : SelRule{0u, 0xffffffffu, 0u, 0u};
-    uint32_t kmin;
-    cnt += select_output<MRG_NW, MRG_RS>(rk, rp, rule, sm.red, kmin,
+    uint32_t kapp;
+    cnt += select_output<MRG_NW, MRG_RS>(rk, rp, rule, sm.red, kapp,
                                          [&](int o, uint32_t k, int32_t ps) {
                                            sm.cand_key[cnt + o] = k;
                                            sm.cand_pos[cnt + o] = ps;
                                          });
+    kbuf = min(kbuf, kapp);
   }
   if (nchunks > 1 && cnt > K) {
-    block_select<MRG_NW, MRG_CAP / MRG_NT>(sm.cand_key, sm.cand_pos, cnt, K, sm.hist, sm.sel, sm.red);
+    kbuf = block_select<MRG_NW, MRG_CAP / MRG_NT>(sm.cand_key, sm.cand_pos, cnt, K, sm.hist, sm.sel, sm.red);
     cnt = K;
   }
+  if (nchunks > 1) kmin = kbuf;
   return cnt;
 }
 
@@ -869,8 +861,9 @@ __device__ __forceinline__ void merge_query(const IdxParams& p, const SmallPlan&
   // this run's lists (the other runs may still be streaming)
   const int c0 = j * MRG_FAN;
   const int nj = nrun == 1 ? nl : min(MRG_FAN, nl - c0);
+  uint32_t kmin;
   int cnt = merge_lists(p.list_keys + (unit0 + c0) * K, p.list_pos + (unit0 + c0) * K, p.list_cnt + unit0 + c0,
-                        p.list_mm + 2 * (unit0 + c0), nj, 1u, K, sm);
+                        p.list_min + unit0 + c0, nj, 1u, K, sm, kmin);
   if (nrun > 1) {
     // ---- first level: the run's Top-K becomes intermediate list unit0 + j
     const int64_t u = unit0 + j;
@@ -878,12 +871,9 @@ __device__ __forceinline__ void merge_query(const IdxParams& p, const SmallPlan&
       st_dev(p.mlist_keys + u * K + i, i < cnt ? sm.cand_key[i] : 0u);
       if (i < cnt) st_dev(p.mlist_pos + u * K + i, sm.cand_pos[i]);
     }
-    uint32_t mn = 0u, mx = 0u;
-    if (cnt > 0) block_minmax<MRG_NW>(sm.cand_key, cnt, sm.red, mn, mx);
     if (tid == 0) {
       st_dev(p.mlist_cnt + u, cnt);
-      st_dev(p.mlist_mm + 2 * u, mn);
-      st_dev(p.mlist_mm + 2 * u + 1, mx);
+      st_dev(p.mlist_min + u, kmin);
     }
     // the workgroup that finishes the last run merges the intermediate lists
     wait_vm();
@@ -898,8 +888,8 @@ __device__ __forceinline__ void merge_query(const IdxParams& p, const SmallPlan&
     const bool last = uniform(sm.sel[3]) == nrun - 1;
     lds_barrier();
     if (!last) return;
-    cnt = merge_lists(p.mlist_keys + unit0 * K, p.mlist_pos + unit0 * K, p.mlist_cnt + unit0, p.mlist_mm + 2 * unit0,
-                      nrun, 1u, K, sm);
+    cnt = merge_lists(p.mlist_keys + unit0 * K, p.mlist_pos + unit0 * K, p.mlist_cnt + unit0, p.mlist_min + unit0,
+                      nrun, 1u, K, sm, kmin);
   }
   // ---- output: kept positions (in LDS, in order) to pool slots
   if (stage) {
@@ -1392,8 +1382,9 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
     for (int q = 0; q < MQ; ++q) {
       if (q < nq) {
         int c = cnt[q];
+        uint32_t kmin = 0u;  // smallest kept key, when a selection ran
         if (c > p.K) {
-          block_select<NW, R>(sm.cand_key[q], sm.cand_pos[q], c, p.K, sm.hist, sm.sel, sm.red);
+          kmin = block_select<NW, R>(sm.cand_key[q], sm.cand_pos[q], c, p.K, sm.hist, sm.sel, sm.red);
           c = p.K;
         } else {
           lds_barrier();  // other waves' appends are visible
@@ -1424,12 +1415,13 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
             st_dev(p.list_keys + unit * p.K + i, i < c ? sm.cand_key[q][i] : 0u);
             if (i < c) st_dev(p.list_pos + unit * p.K + i, sm.cand_pos[q][i]);
           }
-          uint32_t mn = 0u, mx = 0u;
-          if (c > 0) block_minmax<NW>(sm.cand_key[q], c, sm.red, mn, mx);
+          // a list's minimum is read only when it is full (it then bounds the
+          // query's K-th key from below): the selection's, or one pass when
+          // exactly K candidates needed no selection
+          if (c == p.K && cnt[q] == p.K) kmin = block_min<NW>(sm.cand_key[q], c, sm.red);
           if (tid == 0) {
             st_dev(p.list_cnt + unit, c);
-            st_dev(p.list_mm + 2 * unit, mn);
-            st_dev(p.list_mm + 2 * unit + 1, mx);
+            st_dev(p.list_min + unit, kmin);
           }
           // arrival: the list is complete before the run's counter moves
           wait_vm();

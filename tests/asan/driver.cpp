@@ -71,13 +71,13 @@ static void check_idx_layout(const unsigned char* ws, size_t bytes) {
     CHECK((const unsigned char*)(p.run_done + lists) <= ws + DSA_WS_RESERVED_BYTES);
     CHECK((const unsigned char*)p.list_cnt >= ws + DSA_WS_RESERVED_BYTES);
     CHECK(inside(p.list_cnt + lists - 1, ws, bytes));
-    CHECK(inside(p.list_mm + 2 * lists - 1, ws, bytes));
+    CHECK(inside(p.list_min + lists - 1, ws, bytes));
     CHECK(inside(p.list_keys + lists * p.K - 1, ws, bytes));
     CHECK(inside(p.list_pos + lists * p.K - 1, ws, bytes));
     CHECK(inside(p.run_done + lists - 1, ws, bytes));
     if (p.mlist_pos) {
       CHECK(inside(p.mlist_cnt + lists - 1, ws, bytes));
-      CHECK(inside(p.mlist_mm + 2 * lists - 1, ws, bytes));
+      CHECK(inside(p.mlist_min + lists - 1, ws, bytes));
       CHECK(inside(p.mlist_keys + lists * p.K - 1, ws, bytes));
       CHECK(inside(p.mlist_pos + lists * p.K - 1, ws, bytes));
       CHECK(inside(p.merge_done + p.T - 1, ws, bytes));
