@@ -1,8 +1,9 @@
 """Benchmark of the DSA layer (lightning indexer + Top-K + sparse MLA) on one GPU.
 
 A step is one pass of the layer over one batch of synthetic input resident in
-HBM: one dsa_layer call (planning, fused indexer/Top-K/merge, sparse MLA split
-+ combine) for decode, one per chunk for chunked prefill.  The default workload
+HBM: one dsa_layer call (fused indexer/Top-K/merge, which plans a call of up
+to 64 queries itself, else after a planning kernel; sparse MLA split +
+combine) for decode, one per chunk for chunked prefill.  The default workload
 is 64 decoding sequences with cached lengths uniform in [65536, 131072], an FP8
 e4m3 index-K cache (per-token fp32 scale, 64 heads x 128), Top-2048, and a bf16
 576-wide latent cache read by 128-head sparse MLA.
@@ -445,7 +446,8 @@ def main():
         idx_bytes, layer_bytes, idx_flops, mla_flops = idx_bytes + ib, layer_bytes + lb, idx_flops + fi, mla_flops + fm
     achieved = idx_bytes / (idx_ms * 1e-3) / 1e9
     layer_frac = layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS
-    kernel = ("dsa_indexer_topk: planning + dsa_indexer_kernel (Top-K and list merge), timed inside the layer "
+    planning = "in-kernel planning" if step_cases[0][0].T <= 64 else "planning kernel"
+    kernel = (f"dsa_indexer_topk: {planning} + dsa_indexer_kernel (Top-K and list merge), timed inside the layer "
               "step" + (f" (all {len(step_cases[0])} chunk calls of a step)" if len(step_cases[0]) > 1 else ""))
     # the indexer's bound: MFMA when its flops per algorithmic byte exceed the
     # chip's ridge (prefill: each key serves thousands of queries), else HBM
