@@ -72,6 +72,18 @@ def test_fp8_latent_decode_ragged_multisplit():
     run_case(spec("fp8kv_ragged", lens=[40000, 1000, 3, 9000, 2047], seed=43, kv_dtype="fp8"))
 
 
+@pytest.mark.parametrize("idx_dtype,D_idx,H_idx,kv_dtype", [
+    ("mxfp8", 128, 64, "fp8"),   # group-scaled index keys with FP8 latent rows
+    ("bf16", 128, 64, "fp8"),    # bf16 index keys with FP8 latent rows
+    ("bf16", 64, 64, "bf16"),    # 64-wide bf16 index keys, all 64 heads
+    ("fp8", 128, 32, "fp8"),     # two head tiles of the indexer
+])
+def test_format_combinations(idx_dtype, D_idx, H_idx, kv_dtype):
+    # every query of a ragged batch whose longest sequence spans several slices
+    run_case(spec(f"combo_{idx_dtype}{D_idx}_h{H_idx}_{kv_dtype}", idx_dtype=idx_dtype, D_idx=D_idx, H_idx=H_idx,
+                  kv_dtype=kv_dtype, lens=[21000, 1, 4100, 333], queries_per_seq=[2, 1, 1, 3], seed=81))
+
+
 @pytest.mark.parametrize("H", [16, 32, 64])
 def test_fp8_latent_fewer_heads(H):
     run_case(spec(f"fp8kv_h{H}", lens=[5000, 300], seed=44 + H, kv_dtype="fp8", H=H, K=1024))
