@@ -912,13 +912,16 @@ __device__ __forceinline__ void merge_query(const IdxParams& p, const SmallPlan&
 // Main indexer kernel.
 // =============================================================================
 // Candidate buffer entries per query (a multiple of the workgroup's threads:
-// the selections hold CAP / NT entries per thread).  Two queries per group:
-// 5120 measured 3 % faster per prefill call than 4096 (fewer in-stream cuts),
-// 4608 and 6144 in between, 8192 slower (every cut and final select then
-// holds 16 entries per thread).
+// the selections hold CAP / NT entries per thread, and a selection's passes
+// cost in proportion to that).  Two queries per group: 5120 measured 3 %
+// faster per prefill call than 4096 (fewer in-stream cuts), 4608 and 6144 in
+// between, 8192 slower.  One query per group: 5120 against 4096 / 6144 /
+// 8192 / 10240 gave decode_b32_32k 0.130 against 0.135 / 0.134 / 0.139 /
+// 0.140 ms per layer step, mixed_1m 0.200 against 0.200 / 0.201 / 0.202 /
+// 0.205, and the 128K batch within 0.5 us of the best.
 template <int MQ>
 struct CapOf {
-  static constexpr int value = MQ == 1 ? 8192 : 5120;
+  static constexpr int value = 5120;
 };
 // An in-stream cut keeps the Top-K plus at most this many more: the radix
 // select may stop at the pass that finds the bin of the K-th largest key once
