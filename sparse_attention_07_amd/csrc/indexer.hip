@@ -729,9 +729,12 @@ __device__ __forceinline__ uint32_t block_lb(uint32_t lb, MergeSmem& sm) {
 // below the largest minimum of a full list (or below lb0) excluded: the kept
 // entries, in position order, go to sm.cand_key/cand_pos [0, cnt); returns cnt
 // and sets kmin to the smallest kept key.  Ends with a barrier.
-__device__ __forceinline__ int merge_lists(const uint32_t* keys0, const int32_t* pos0, const int32_t* cnt0,
-                                           const uint32_t* min0, int n, uint32_t lb0, int K, MergeSmem& sm,
-                                           uint32_t& kmin) {
+template <int RS>
+__device__ __forceinline__ int merge_lists_rs(const uint32_t* keys0, const int32_t* pos0, const int32_t* cnt0,
+                                              const uint32_t* min0, int n, uint32_t lb0, int K, MergeSmem& sm,
+                                              uint32_t& kmin) {
+  static_assert(RS <= MRG_RS && RS % 4 == 0, "entries per lane");
+  constexpr int CH = RS * MRG_NT;  // entries per chunk
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // list counts and minima: loaded before the first chunk, reduced after it
   // has been issued, so the two latencies overlap
@@ -742,20 +745,21 @@ __device__ __forceinline__ int merge_lists(const uint32_t* keys0, const int32_t*
     lm = ld_dev(min0 + tid);
   }
   const int total = n * K;
-  const int nchunks = (total + MRG_CHUNK - 1) / MRG_CHUNK;
+  // fewer entries per lane than MRG_RS: the caller guarantees one chunk
+  const int nchunks = RS < MRG_RS ? 1 : (total + CH - 1) / CH;
 
   // Chunk layout: wave w holds entries [w * wch, (w + 1) * wch) of the chunk,
   // 64 per slot; every load comes from a clamped index and out-of-range slots
   // are dropped afterwards (loading them too keeps all loads in one straight
   // run: a branch per slot made the compiler wait between them, 3.7 -> 6.5 us).
-  uint32_t rk[MRG_RS];
-  int32_t rp[MRG_RS];
+  uint32_t rk[RS];
+  int32_t rp[RS];
   auto load_chunk = [&](int c) {
-    const int cb = c * MRG_CHUNK;
-    const int cn = min(MRG_CHUNK, total - cb);
+    const int cb = c * CH;
+    const int cn = min(CH, total - cb);
     const int wch = (((cn + MRG_NW - 1) / MRG_NW) + 63) & ~63;
 #pragma unroll
-    for (int s = 0; s < MRG_RS; ++s) {
+    for (int s = 0; s < RS; ++s) {
       const int e = cb + min(wave * wch + s * 64 + lane, cn - 1);
       rk[s] = ld_dev(keys0 + e);
       rp[s] = ld_dev(pos0 + e);
@@ -769,10 +773,10 @@ __device__ __forceinline__ int merge_lists(const uint32_t* keys0, const int32_t*
   uint32_t kbuf = 0xffffffffu;  // smallest key in the buffer (several chunks)
   for (int c = 0; c < nchunks; ++c) {
     if (c > 0) wch = load_chunk(c);
-    const int cn = min(MRG_CHUNK, total - c * MRG_CHUNK);
+    const int cn = min(CH, total - c * CH);
     auto mask = [&]() {
 #pragma unroll
-      for (int s = 0; s < MRG_RS; ++s) {
+      for (int s = 0; s < RS; ++s) {
         const int e = wave * wch + s * 64 + lane;
         if (s * 64 >= wch || e >= cn || rk[s] <= thr) rk[s] = 0u;
       }
@@ -780,8 +784,8 @@ __device__ __forceinline__ int merge_lists(const uint32_t* keys0, const int32_t*
     mask();
     if (nchunks == 1) {
       // ---- single chunk: select straight from the registers
-      const SelRule rule = select_rule<MRG_NW, MRG_RS>(rk, rp, K, sm.hist, sm.sel, sm.red);
-      cnt = select_output<MRG_NW, MRG_RS>(rk, rp, rule, sm.red, kmin, [&](int o, uint32_t k, int32_t ps) {
+      const SelRule rule = select_rule<MRG_NW, RS>(rk, rp, K, sm.hist, sm.sel, sm.red);
+      cnt = select_output<MRG_NW, RS>(rk, rp, rule, sm.red, kmin, [&](int o, uint32_t k, int32_t ps) {
         sm.cand_key[o] = k;
         sm.cand_pos[o] = ps;
       });
@@ -791,7 +795,7 @@ __device__ __forceinline__ int merge_lists(const uint32_t* keys0, const int32_t*
     auto count_valid = [&]() {
       uint32_t wc = 0;
 #pragma unroll
-      for (int s = 0; s < MRG_RS; ++s) wc += (uint32_t)__builtin_popcountll(ballot(rk[s] != 0u));
+      for (int s = 0; s < RS; ++s) wc += (uint32_t)__builtin_popcountll(ballot(rk[s] != 0u));
       if (lane == 0) sm.red[8 * wave + 7] = wc;
       lds_barrier();
       int m = 0;
@@ -811,10 +815,10 @@ __device__ __forceinline__ int merge_lists(const uint32_t* keys0, const int32_t*
     }
     // append in order: every valid entry, or only the chunk's own Top-K when
     // that does not fit (cnt <= K then, and cnt + K <= MRG_CAP)
-    const SelRule rule = cnt + tot > MRG_CAP ? select_rule<MRG_NW, MRG_RS>(rk, rp, K, sm.hist, sm.sel, sm.red)
+    const SelRule rule = cnt + tot > MRG_CAP ? select_rule<MRG_NW, RS>(rk, rp, K, sm.hist, sm.sel, sm.red)
                                              : SelRule{0u, 0xffffffffu, 0u, 0u};
     uint32_t kapp;
-    cnt += select_output<MRG_NW, MRG_RS>(rk, rp, rule, sm.red, kapp,
+    cnt += select_output<MRG_NW, RS>(rk, rp, rule, sm.red, kapp,
                                          [&](int o, uint32_t k, int32_t ps) {
                                            sm.cand_key[cnt + o] = k;
                                            sm.cand_pos[cnt + o] = ps;
@@ -827,6 +831,20 @@ __device__ __forceinline__ int merge_lists(const uint32_t* keys0, const int32_t*
   }
   if (nchunks > 1) kmin = kbuf;
   return cnt;
+}
+
+// Merge over the entries per lane the lists need: a chunk of 16, 24 or 28
+// entries per lane holds 4, 6 or 7 full lists of K = 2048 (a selection's
+// passes cost in proportion to the entries each lane holds); 32 per lane,
+// in one chunk or several, otherwise.
+__device__ __forceinline__ int merge_lists(const uint32_t* keys0, const int32_t* pos0, const int32_t* cnt0,
+                                           const uint32_t* min0, int n, uint32_t lb0, int K, MergeSmem& sm,
+                                           uint32_t& kmin) {
+  const int total = n * K;
+  if (total <= 16 * MRG_NT) return merge_lists_rs<16>(keys0, pos0, cnt0, min0, n, lb0, K, sm, kmin);
+  if (total <= 24 * MRG_NT) return merge_lists_rs<24>(keys0, pos0, cnt0, min0, n, lb0, K, sm, kmin);
+  if (total <= 28 * MRG_NT) return merge_lists_rs<28>(keys0, pos0, cnt0, min0, n, lb0, K, sm, kmin);
+  return merge_lists_rs<MRG_RS>(keys0, pos0, cnt0, min0, n, lb0, K, sm, kmin);
 }
 
 // One merge step for query t, run j, in the workgroup that wrote the run's
