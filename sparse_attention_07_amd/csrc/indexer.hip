@@ -1405,7 +1405,14 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
         int c = cnt[q];
         uint32_t kmin = 0u;  // smallest kept key, when a selection ran
         if (c > p.K) {
-          kmin = block_select<NW, R>(sm.cand_key[q], sm.cand_pos[q], c, p.K, sm.hist, sm.sel, sm.red);
+          // as few entries per thread as the buffer needs (a selection's
+          // passes cost in proportion to them)
+          if (c <= 6 * NT)
+            kmin = block_select<NW, 6>(sm.cand_key[q], sm.cand_pos[q], c, p.K, sm.hist, sm.sel, sm.red);
+          else if (c <= 8 * NT)
+            kmin = block_select<NW, 8>(sm.cand_key[q], sm.cand_pos[q], c, p.K, sm.hist, sm.sel, sm.red);
+          else
+            kmin = block_select<NW, R>(sm.cand_key[q], sm.cand_pos[q], c, p.K, sm.hist, sm.sel, sm.red);
           c = p.K;
         } else {
           lds_barrier();  // other waves' appends are visible
