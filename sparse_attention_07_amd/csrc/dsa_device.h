@@ -18,7 +18,13 @@ constexpr int PAGE = 64;
 constexpr int LATENT = 576;
 constexpr int VDIM = 512;
 constexpr int KMAX = 2048;
-constexpr int ROUND = 1024;  // keys scored per streaming round of the indexer
+// Keys scored per streaming round of the indexer (one candidate count and
+// barrier per round): 512 for one query per group, 1024 for two.  Measured
+// (same box): 512 against 1024 keys, mixed_1m 0.1920 against 0.1943 ms per
+// layer step and the 128K decode batch 0.2370 against 0.2375, but the
+// paired-query prefill indexer 4 % slower; 2048 slower everywhere.  512 is
+// the least the four-group prefetch ring allows.
+constexpr int round_keys(int mq) { return mq == 1 ? 512 : 1024; }
 constexpr int MIN_SLICE = 4096;       // smallest key slice an indexer workgroup is given
 constexpr int MERGE_FAN = 8;          // candidate lists one merge workgroup takes at once
 // Fixed cost of one indexer segment (a group's keys inside one workgroup's

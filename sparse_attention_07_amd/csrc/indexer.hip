@@ -28,7 +28,7 @@
 //    run on them; one permlane butterfly then sums the four head groups of
 //    four consecutive groups at once, leaving one key per lane (64 keys) for
 //    the key scale, the bound test and the candidate ballots;
-//  * selection streams: after each 1024-key round the keys above the current
+//  * selection streams: after each 512-key round (1024 for paired queries) the keys above the current
 //    bound (a lower bound of the K-th score) are appended, in position order,
 //    to an LDS candidate buffer (one barrier per round: a wave's offset is
 //    the count of the waves before it); only when a round would not fit is
@@ -957,7 +957,7 @@ struct IdxSmem {
   static constexpr int NT = NW * 64;
   static constexpr int R = CAP / NT;  // candidate entries per thread in a selection
   static_assert(CAP % NT == 0, "selection register slots");
-  static_assert(CAP >= KMAX + CUT_SLACK + ROUND, "after a cut the buffer holds one more round");
+  static_assert(CAP >= KMAX + CUT_SLACK + round_keys(MQ), "after a cut the buffer holds one more round");
   uint32_t cand_key[MQ][CAP];
   int32_t cand_pos[MQ][CAP];
   uint32_t hist[2 * NW * 256];
@@ -999,6 +999,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
   constexpr int NT = NW * 64;
   constexpr int CAP = Sm::CAP;
   constexpr int R = Sm::R;
+  constexpr int ROUND = round_keys(MQ);  // keys per round
   constexpr int GPW = ROUND / 16 / NW;  // 16-key groups per wave per round
   constexpr int ES = DT == 0 ? 2 : 1;   // bytes per element
   constexpr int ROWB = D * ES;          // bytes per key row
@@ -1317,6 +1318,17 @@ __global__ __launch_bounds__(NW * 64, 1) void dsa_indexer_kernel(IdxParams p) {
           finish_quad(part, qsc[qd & 1], qok[qd & 1], group_p0(r * GPW + 4 * qd), kq);
 #pragma unroll
           for (int q = 0; q < MQ; ++q) kk[q][qd] = kq[q];
+        }
+        if constexpr (NQD % 2 == 1) {
+          // an odd number of quads per round: the next round's first quad is
+          // in slot 1, so the slots trade places (the parity is the quad's
+          // place in the whole stream, not in the round)
+          const float ts = qsc[0];
+          qsc[0] = qsc[1];
+          qsc[1] = ts;
+          const bool tk = qok[0];
+          qok[0] = qok[1];
+          qok[1] = tk;
         }
         if (p.scores) {
           // score dump (a debugging call): the fused scores exactly as the

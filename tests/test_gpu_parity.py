@@ -1,7 +1,7 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle.
 
 Small cases are checked on every query; they span several key chunks, merge
-tree levels, 1024-key rounds and 32-row attention tiles, with ragged tails.
+tree levels, 512-key rounds and 32-row attention tiles, with ragged tails.
 The five named workloads run at full size in the launch configuration the
 benchmark times, with sampled queries checked one by one."""
 import dataclasses
